@@ -1,0 +1,175 @@
+"""Seeded synthetic inputs for paged MLA decode.
+
+This module only draws random numbers and lays them out (sequence lengths,
+page permutations, block tables, bf16 bit patterns of N(0, 1) values, sparse
+top-k index lists).  It holds none of the decode arithmetic; the tests and the
+benchmark feed the same arrays to the HIP library and to the CPU oracle.
+
+Recipe (NumPy PCG64, seed = workload number): draw the lengths, then the page
+permutation, then q, then the cache, then (sparse only) the indices.  Normal
+values are drawn as float32 and rounded to bf16, ties to even.  Pages are
+handed out consecutively from the permutation, sequence by sequence.  Rows that
+no sequence references (unassigned pages, slots past a sequence's length in its
+last page) and the block-table padding page may be filled with NaN ("poison")
+so that any read of them shows up in the outputs.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+PAGE = 64
+D_QK = 576
+D_V = 512
+BF16_NAN = 0x7FC0
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (nearest, ties to even); returns uint16 bit patterns."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def normal_bf16(rng: np.random.Generator, shape, chunk: int = 1 << 24) -> np.ndarray:
+    """N(0, 1) values drawn as float32 and rounded to bf16 bit patterns."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16)
+    for i in range(0, n, chunk):
+        m = min(chunk, n - i)
+        out[i:i + m] = f32_to_bf16_bits(rng.standard_normal(m, dtype=np.float32))
+    return out.reshape(shape)
+
+
+@dataclass
+class Workload:
+    """One decode call's inputs (host arrays)."""
+    name: str
+    q: np.ndarray              # uint16 [B, s_q, h_q, 576]
+    kv: np.ndarray             # uint16 [num_pages, 64, h_kv, 576]
+    block_table: np.ndarray    # int32 [B, max_blocks]
+    cache_seqlens: np.ndarray  # int32 [B]
+    causal: bool = False
+    indices: np.ndarray | None = None   # int32 [B, s_q, topk]
+    dv: int = D_V
+    softmax_scale: float | None = None
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def B(self):
+        return self.q.shape[0]
+
+    @property
+    def s_q(self):
+        return self.q.shape[1]
+
+    @property
+    def h_q(self):
+        return self.q.shape[2]
+
+    @property
+    def topk(self):
+        return None if self.indices is None else self.indices.shape[2]
+
+
+def build(name: str, seed: int, lengths: np.ndarray | None, *, B: int, s_q: int, h_q: int,
+          num_pages: int, causal: bool = False, max_blocks: int | None = None,
+          poison: bool = False, h_kv: int = 1, topk: int | None = None,
+          rng: np.random.Generator | None = None, pad_page: int | None = None,
+          dv: int = D_V) -> Workload:
+    """Assemble a workload.  ``lengths`` may be drawn by the caller from ``rng``
+    (the same generator is then used for the rest, keeping the draw order)."""
+    rng = np.random.default_rng(seed) if rng is None else rng
+    lengths = np.asarray(lengths, dtype=np.int64)
+    nblk = (lengths + PAGE - 1) // PAGE
+    mb = int(max(1, nblk.max())) if max_blocks is None else int(max_blocks)
+    need = int(nblk.sum())
+    padded = bool((nblk < mb).any())
+    spare = 1 if (pad_page is None and padded) else 0
+    pool = max(num_pages, need + spare)
+    perm = rng.permutation(pool)
+    bt = np.empty((B, mb), dtype=np.int32)
+    if pad_page is not None:
+        pad = int(pad_page)
+    else:
+        pad = int(perm[need]) if need < pool else 0
+    bt[:] = pad
+    off = 0
+    for b in range(B):
+        n = int(nblk[b])
+        bt[b, :n] = perm[off:off + n]
+        off += n
+    q = normal_bf16(rng, (B, s_q, h_q, D_QK))
+    kv = normal_bf16(rng, (pool, PAGE, h_kv, D_QK))
+    indices = None
+    if topk is not None:
+        indices = np.empty((B, s_q, topk), dtype=np.int32)
+        for b in range(B):
+            for s in range(s_q):
+                hi = int(lengths[b]) - s_q + s + 1
+                indices[b, s] = rng.choice(hi, size=topk, replace=False)
+    if poison:
+        referenced = np.zeros((pool, PAGE), dtype=bool)
+        for b in range(B):
+            L = int(lengths[b])
+            for j in range(int(nblk[b])):
+                n_valid = min(PAGE, L - j * PAGE)
+                referenced[bt[b, j], :n_valid] = True
+        kv[~referenced] = BF16_NAN
+    return Workload(name=name, q=q, kv=kv, block_table=bt,
+                    cache_seqlens=lengths.astype(np.int32), causal=causal,
+                    indices=indices, dv=dv,
+                    meta=dict(seed=seed, pool_pages=pool, pad_page=pad, poison=poison))
+
+
+# ---------------------------------------------------------------------------
+# The five named workloads (sizes of the headline decode scenarios)
+# ---------------------------------------------------------------------------
+def tiny(poison: bool = False) -> Workload:
+    """b=2, s_q=1, h_q=16, lengths {37, 130}; 4 of 8 physical pages, shuffled."""
+    rng = np.random.default_rng(1)
+    lengths = np.array([37, 130])
+    return build("tiny b2 h16 L{37,130}", 1, lengths, B=2, s_q=1, h_q=16, num_pages=8,
+                 poison=poison, rng=rng)
+
+
+def memory_bound(poison: bool = False) -> Workload:
+    """b=64, s_q=1, h_q=16, lengths uniform in [1, 4096], 6000-page pool."""
+    rng = np.random.default_rng(2)
+    lengths = rng.integers(1, 4097, size=64)
+    return build("memory-bound b64 h16 L~U[1,4096]", 2, lengths, B=64, s_q=1, h_q=16,
+                 num_pages=6000, max_blocks=64, poison=poison, rng=rng)
+
+
+def near_ridge(poison: bool = False) -> Workload:
+    """b=128, s_q=1, h_q=128, every length 4096, 8192-page pool."""
+    rng = np.random.default_rng(3)
+    lengths = np.full(128, 4096)
+    return build("near-ridge b128 h128 L4096", 3, lengths, B=128, s_q=1, h_q=128,
+                 num_pages=8192, max_blocks=64, poison=poison, rng=rng)
+
+
+def mtp_causal(poison: bool = False) -> Workload:
+    """b=32, s_q=2 causal, h_q=128, lengths log-uniform in [256, 16384], 8192-page pool."""
+    rng = np.random.default_rng(4)
+    lengths = np.floor(np.exp(rng.uniform(np.log(256), np.log(16384), size=32))).astype(np.int64)
+    return build("mtp-causal b32 sq2 h128 L~logU[256,16384]", 4, lengths, B=32, s_q=2,
+                 h_q=128, num_pages=8192, causal=True, max_blocks=256, poison=poison, rng=rng)
+
+
+def sparse_topk(poison: bool = False, B: int = 16) -> Workload:
+    """b=16, s_q=8, h_q=128, length 65536, top-k 2048 unique unsorted indices per query token."""
+    rng = np.random.default_rng(5)
+    lengths = np.full(B, 65536)
+    return build(f"sparse-topk b{B} sq8 h128 L65536 k2048", 5, lengths, B=B, s_q=8, h_q=128,
+                 num_pages=B * 1024, max_blocks=1024, topk=2048, poison=poison, rng=rng)
+
+
+NAMED = {
+    "tiny": tiny,
+    "memory_bound": memory_bound,
+    "near_ridge": near_ridge,
+    "mtp_causal": mtp_causal,
+    "sparse_topk": sparse_topk,
+}
