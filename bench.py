@@ -1,0 +1,225 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged MLA decode hot path on one MI355X.
+
+A step is one pass of the whole path over one batch: the split-KV plan
+(mla_get_metadata), the split decode kernel and the merge kernel
+(mla_decode_with_kvcache).  The default workload is the memory-bound decode:
+b=64, s_q=1, h_q=16, h_kv=1, d_qk=576, dv=512, lengths uniform in [1, 4096]
+(seeded), 64-token pages, shuffled block table over a 6000-page pool, bf16
+N(0, 1) data.
+
+Inputs are resident in HBM before timing starts.  Four copies of the cache
+(each 442 MB) are used in rotation, so the 256 MB Infinity Cache cannot serve
+a step from the previous one; the step reads its keys from HBM as a decode
+over a fresh layer would.  A GPU sleep queued ahead of the timed steps lets
+the host enqueue them all before the GPU reaches them, so the K steps run
+back to back and the HIP events measure GPU time, not Python launch time.
+
+Prints one JSON line (the last line of stdout).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+KV_ROW_BYTES = 576 * 2
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
+NCOPIES = 4
+
+
+def algorithmic_work(w):
+    """KV bytes (each key row once) and FLOPs (2 * (576 + 512) per query row and key)."""
+    L = w.cache_seqlens.astype(np.int64)
+    if w.indices is not None:
+        ok = (w.indices >= 0) & (w.indices < L[:, None, None])
+        keys = int(ok.sum())
+        return keys * KV_ROW_BYTES, keys * w.h_q * 2 * (576 + 512)
+    kv = int(L.sum()) * KV_ROW_BYTES
+    if w.causal:
+        qk = sum(w.h_q * max(int(l) - w.s_q + s + 1, 0) for l in L for s in range(w.s_q))
+    else:
+        qk = int(L.sum()) * w.s_q * w.h_q
+    return kv, qk * 2 * (576 + 512)
+
+
+def gpu_sleep_ms(torch, ms):
+    """Queue a GPU spin of about `ms` milliseconds on the current stream."""
+    if not hasattr(gpu_sleep_ms, "cycles_per_ms"):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.cuda._sleep(1_000_000)
+        e1.record()
+        torch.cuda.synchronize()
+        gpu_sleep_ms.cycles_per_ms = 1_000_000 / max(e0.elapsed_time(e1), 1e-3)
+    torch.cuda._sleep(int(gpu_sleep_ms.cycles_per_ms * ms))
+
+
+def _to_dev(torch, a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    return t.cuda() if dtype is None else t.cuda().view(dtype)
+
+
+def run_workload(torch, m, w, steps, warmup, ncopies=NCOPIES):
+    q0 = _to_dev(torch, w.q.view(np.int16), torch.bfloat16)
+    kv0 = _to_dev(torch, w.kv.view(np.int16), torch.bfloat16)
+    bt = _to_dev(torch, w.block_table.astype(np.int32))
+    sl = _to_dev(torch, w.cache_seqlens.astype(np.int32))
+    idx = _to_dev(torch, w.indices.astype(np.int32)) if w.indices is not None else None
+    qs = [q0] + [q0.clone() for _ in range(ncopies - 1)]
+    kvs = [kv0] + [kv0.clone() for _ in range(ncopies - 1)]
+    rows = w.s_q * w.h_q
+    plan, ns = m.get_mla_metadata(sl, rows, 1, s_q=w.s_q, topk=w.topk)
+    W = plan.numel() // 8 - 1
+    B = w.B
+    o = torch.empty((B, w.s_q, w.h_q, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, w.s_q, w.h_q), dtype=torch.float32, device="cuda")
+    ws_bytes = m.workspace_bytes(B, w.s_q, rows, 1, w.topk or 0, 512, W)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+
+    def step(k, ev=None):
+        c = k % ncopies
+        if ev is not None:
+            ev[0].record()
+        p, n = m.get_mla_metadata(sl, rows, 1, s_q=w.s_q, topk=w.topk)
+        if ev is not None:
+            ev[1].record()
+        m.mla_decode_with_kvcache(qs[c], kvs[c], bt, sl, 512, p, n, causal=w.causal, indices=idx,
+                                  out=(o, lse), workspace=ws, phases=1)
+        if ev is not None:
+            ev[2].record()
+        m.mla_decode_with_kvcache(qs[c], kvs[c], bt, sl, 512, p, n, causal=w.causal, indices=idx,
+                                  out=(o, lse), workspace=ws, phases=2)
+        if ev is not None:
+            ev[3].record()
+
+    for k in range(warmup):
+        step(k)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    gpu_sleep_ms(torch, 2.0 + 0.25 * steps)   # host enqueues all steps meanwhile
+    t0 = time.perf_counter()
+    start.record()
+    for k in range(steps):
+        step(k, evs[k])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    plan_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    dec_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    comb_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    return dict(ms_per_step=total_ms / steps, wall_s=wall, plan_ms=float(np.mean(plan_ms)),
+                decode_ms=float(np.mean(dec_ms)), decode_ms_med=float(np.median(dec_ms)),
+                combine_ms=float(np.mean(comb_ms)), num_workers=W,
+                o=o, lse=lse)
+
+
+def cpu_baseline(w, budget_s=10.0):
+    """The CPU oracle on the same workload, repeated until ~budget_s of CPU time."""
+    from oracle import mla_oracle as orc
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        infos = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max((i.get("num_threads") or 1) for i in infos) if infos else None
+    except Exception:
+        pass
+    kv_bytes, _ = algorithmic_work(w)
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        orc.decode(w.q, w.kv, w.block_table, w.cache_seqlens, 512, causal=w.causal,
+                   indices=w.indices)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 50:
+            break
+    return {"value": round(kv_bytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": threads or os.cpu_count(),
+            "kind": "oracle",
+            "sample": f"float64 NumPy oracle, whole workload ({w.B} sequences) decoded {reps}x in {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="memory_bound",
+                    choices=["tiny", "memory_bound", "near_ridge", "mtp_causal", "sparse_topk"])
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--secondary", action="store_true",
+                    help="also time the near-ridge, MTP-causal and sparse top-k workloads")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the decode shards over sequences with no exchange, "
+              "and this build runs on a single MI355X; use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import mla_paged_kv_get_amd as m
+    from mla_paged_kv_get_amd import workloads as wl
+
+    w = wl.NAMED[args.workload]()
+    kv_bytes, flops = algorithmic_work(w)
+    r = run_workload(torch, m, w, args.steps, args.warmup)
+    dec_s = r["decode_ms"] / 1e3
+    achieved = kv_bytes / dec_s / 1e9
+    step_s = r["ms_per_step"] / 1e3
+    line = {
+        "metric": "paged MLA decode: achieved KV HBM GB/s + bf16 TFLOPS (% of MI355X roofline)",
+        "value": round(kv_bytes / step_s / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "s_q": w.s_q, "h_q": w.h_q, "h_kv": 1,
+                   "d_qk": 576, "dv": 512, "page": 64, "causal": bool(w.causal),
+                   "topk": w.topk, "kv_bytes": kv_bytes, "flops": flops,
+                   "num_workers": r["num_workers"], "kv_copies_rotated": NCOPIES},
+        "tflops": round(flops / step_s / 1e12, 3),
+        "step_breakdown_ms": {"plan": round(r["plan_ms"], 5), "decode": round(r["decode_ms"], 5),
+                              "combine": round(r["combine_ms"], 5)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode split kernel", "launch_ms": round(r["decode_ms"], 5),
+                     "mfma_tflops": round(flops / dec_s / 1e12, 2),
+                     "mfma_frac": round(flops / dec_s / 1e12 / BF16_PEAK_TFLOPS, 4)},
+    }
+    if args.secondary:
+        sec = {}
+        for name in ("near_ridge", "mtp_causal", "sparse_topk"):
+            w2 = wl.NAMED[name]()
+            kb, fl = algorithmic_work(w2)
+            r2 = run_workload(torch, m, w2, max(10, args.steps // 2), 3)
+            d2 = r2["decode_ms"] / 1e3
+            sec[name] = {"workload": w2.name, "decode_ms": round(r2["decode_ms"], 5),
+                         "combine_ms": round(r2["combine_ms"], 5), "plan_ms": round(r2["plan_ms"], 5),
+                         "kv_GBps": round(kb / d2 / 1e9, 1), "hbm_frac": round(kb / d2 / 1e9 / HBM_PEAK_GBS, 4),
+                         "TFLOPS": round(fl / d2 / 1e12, 1), "mfma_frac": round(fl / d2 / 1e12 / BF16_PEAK_TFLOPS, 4),
+                         "step_ms": round(r2["ms_per_step"], 5)}
+            del r2
+            torch.cuda.empty_cache()
+        line["secondary"] = sec
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

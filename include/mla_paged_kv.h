@@ -1,0 +1,201 @@
+/*
+ * mla_paged_kv.h — C ABI of the MI355X (gfx950) paged MLA decode library.
+ *
+ * Multi-head latent attention decode over a paged, compressed-latent KV
+ * cache.  Every cached token is one latent row of 576 bf16 values shared by
+ * all query heads (512 latent values followed by 64 decoupled-RoPE values;
+ * "Novita AI, H100 및 H200에서 FlashMLA 평가", section "MLA란 무엇인가요?").
+ * K is the whole row, V is its first dv = 512 values.  Rows live in pages of
+ * 64 tokens reached through a per-sequence block table, and sequences have
+ * their own lengths ("What is FlashMLA", topnet.top, section "FlashMLA의 주요
+ * 특성" and the installation-and-use section, steps 2 and 3).
+ *
+ * The library follows the two-call shape of those steps: a metadata call that
+ * plans the split-KV work once per decode step (reusable by every layer while
+ * the lengths do not change), and a decode call per layer returning (o, lse).
+ *
+ * Conventions shared by every entry point
+ *  - Pointers marked "device" are device (HBM) addresses on the current HIP
+ *    device; the others are host addresses.  The caller owns every buffer.  The
+ *    library allocates no memory and keeps no pointer after a call returns,
+ *    except that enqueued kernels use the buffers until they finish on `stream`.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue
+ *    work; errors inside kernels surface at the caller's next synchronisation.
+ *  - Arguments are checked on the host before anything is enqueued; a failed
+ *    check returns a nonzero status and enqueues nothing.  No C++ exception
+ *    crosses this boundary.
+ *  - Tensors are dense and row-major (C order).
+ *
+ * Shapes (bf16 values are passed as raw 16-bit patterns):
+ *   q            [batch, s_q, h_q, d_qk]        bf16, device
+ *   kvcache      [num_pages, 64, h_kv, d_qk]    bf16, device
+ *   block_table  [batch, max_blocks]            int32, device; entry j of row b
+ *                is the physical page of logical tokens 64*j .. 64*j + 63
+ *   cache_seqlens[batch]                        int32, device; L_b >= 0
+ *   indices      [batch, s_q, topk]             int32, device (sparse mode only)
+ *   o            [batch, s_q, h_q, dv]          bf16, device (output)
+ *   lse          [batch, s_q, h_q]              fp32, device (output)
+ * Supported: d_qk = 576, dv = 512, page size 64, h_kv = 1.
+ */
+#ifndef MLA_PAGED_KV_H_
+#define MLA_PAGED_KV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define MLA_OK 0
+#define MLA_ERR_INVALID_ARGUMENT 1   /* null pointer, bad size, inconsistent shapes */
+#define MLA_ERR_UNSUPPORTED 2        /* a shape this build does not implement */
+#define MLA_ERR_WORKSPACE_TOO_SMALL 3
+#define MLA_ERR_HIP 4                /* a HIP runtime call or kernel launch failed */
+
+#define MLA_PAGE_SIZE 64
+#define MLA_D_QK 576
+#define MLA_D_V 512
+#define MLA_PLAN_WORDS 8             /* int32 words per plan row */
+
+/* Human-readable text of a status code (static storage, never NULL). */
+const char* mla_status_string(int status);
+
+/*
+ * mla_plan_dims — host only; sizes the metadata call's outputs.
+ *
+ * The work of one decode call is a list of items.  Dense mode (topk <= 0):
+ * one item per sequence, of length cache_seqlens[b], with num_q_rows =
+ * s_q * h_q / h_kv query rows sharing it (the pages' second argument of the
+ * metadata call).  Sparse mode (topk > 0): one item per query token
+ * (batch * s_q items) whose keys are the topk entries of indices[b, s, :],
+ * with num_q_rows / s_q rows each.
+ *
+ *   num_workers_request  0 = let the library choose (CU count and the decode
+ *                        variant picked for this row count); > 0 forces it
+ *   out_num_workers      workers W of the plan (host)
+ *   out_plan_words       int32 words of the plan buffer = 8 * (W + 1) (host)
+ *   out_num_items        items of the call; num_splits holds items + 1 words (host)
+ * Needs the current HIP device only when num_workers_request == 0.
+ */
+int mla_plan_dims(int batch, int s_q, int num_q_rows, int h_kv, int topk,
+                  int num_workers_request, int* out_num_workers,
+                  int* out_plan_words, int* out_num_items);
+
+/*
+ * mla_get_metadata — split-KV tile scheduler ("get_mla_metadata" of the
+ * pages, topnet.top installation-and-use section, step 2).
+ *
+ * Splits every item's 64-token blocks into contiguous runs spread over W
+ * workers so that each worker gets about the same number of blocks plus a
+ * fixed per-run overhead, and counts each item's runs (splits).  Integer only
+ * and deterministic.
+ *
+ *   cache_seqlens  [batch] int32, device (read in sparse mode as well: index
+ *                  entries outside [0, L_b) are padding)
+ *   plan           [8 * (W + 1)] int32, device (output).  Row 0 = {W, per-run
+ *                  overhead in blocks, blocks per worker P, items, version 1,
+ *                  64, total cost T, 0}; row 1 + w = {first item, its first
+ *                  block, last item, end block (exclusive) in the last item,
+ *                  split number of the run in the first item, 0, 0, 0}, or
+ *                  {-1, 0, -1, 0, 0, 0, 0, 0} for a worker with no blocks.
+ *   num_splits     [items + 1] int32, device (output): exclusive prefix sum
+ *                  of the per-item split counts.
+ * The plan stays valid for every decode call with the same lengths, batch,
+ * s_q, topk and W; items of length 0 get no split.
+ */
+int mla_get_metadata(const int32_t* cache_seqlens, int batch, int s_q,
+                     int num_q_rows, int h_kv, int topk, int num_workers,
+                     int32_t* plan, int32_t* num_splits, void* stream);
+
+/*
+ * mla_workspace_bytes — host only; bytes of the decode scratch buffer:
+ * (items + W) partial results of num_q_rows x (dv + 1) fp32 values each.
+ */
+size_t mla_workspace_bytes(int batch, int s_q, int num_q_rows, int h_kv, int topk,
+                           int dv, int num_workers);
+
+/*
+ * mla_decode_with_kvcache — the decode ("flash_mla_with_kvcache" of the pages,
+ * topnet.top installation-and-use section, step 3).
+ *
+ * For query token s of sequence b and head h, with key set J:
+ *   dense, causal = 0:  J = {0 .. L_b - 1}
+ *   dense, causal = 1:  J = {0 .. L_b - s_q + s}  (the s_q query tokens are the
+ *                       last s_q tokens of the cache)
+ *   sparse (indices):   J = {indices[b, s, t] : 0 <= indices[b, s, t] < L_b}
+ *   S_j   = softmax_scale * <q[b, s, h, :], K_j>   (K_j = cache row of key j)
+ *   o     = sum_j exp(S_j - m) V_j / sum_j exp(S_j - m), rounded to bf16
+ *   lse   = m + ln(sum_j exp(S_j - m)) with m = max_j S_j (natural log)
+ * An empty J gives o = 0 and lse = -inf.  Cache rows outside J (slots past L_b
+ * in a sequence's last page, pages not in the first ceil(L_b / 64) block-table
+ * entries) are never read.
+ *
+ *   num_pages       pages in kvcache (used to check the plan's bounds only on
+ *                   the validation call; not read by the kernels)
+ *   page_size       must be 64
+ *   max_blocks      columns of block_table
+ *   plan, num_splits, num_workers   from mla_get_metadata with the same
+ *                   lengths / batch / s_q / topk and num_q_rows = s_q*h_q/h_kv
+ *   causal          0 or 1 (must be 0 in sparse mode)
+ *   softmax_scale   > 0 (the pages' default for d_qk = 576 is 576^-0.5)
+ *   indices, topk   NULL and 0 for dense mode
+ *   workspace       device scratch of at least mla_workspace_bytes(...) bytes
+ */
+int mla_decode_with_kvcache(const void* q, const void* kvcache, int64_t num_pages,
+                            int page_size, const int32_t* block_table, int max_blocks,
+                            const int32_t* cache_seqlens, int batch, int s_q, int h_q,
+                            int h_kv, int d_qk, int dv, const int32_t* plan,
+                            const int32_t* num_splits, int num_workers, int causal,
+                            float softmax_scale, const int32_t* indices, int topk,
+                            void* o, float* lse, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
+ * mla_decode_with_kvcache_phase — the same decode in two separately launched
+ * phases, for callers that time or overlap them: phases = 1 runs the split
+ * kernel only (items covered by one worker get their final o / lse, the others
+ * get fp32 partials in `workspace`); phases = 2 runs the merge of the partials
+ * only (it must follow phase 1 on the same stream with the same arguments);
+ * phases = 3 runs both and is mla_decode_with_kvcache.  Any other value returns
+ * MLA_ERR_INVALID_ARGUMENT.  Same arguments, checks and ownership rules as
+ * mla_decode_with_kvcache.
+ */
+int mla_decode_with_kvcache_phase(const void* q, const void* kvcache, int64_t num_pages,
+                                  int page_size, const int32_t* block_table, int max_blocks,
+                                  const int32_t* cache_seqlens, int batch, int s_q, int h_q,
+                                  int h_kv, int d_qk, int dv, const int32_t* plan,
+                                  const int32_t* num_splits, int num_workers, int causal,
+                                  float softmax_scale, const int32_t* indices, int topk,
+                                  void* o, float* lse, void* workspace,
+                                  size_t workspace_bytes, int phases, void* stream);
+
+/*
+ * mla_debug_row_ids — indexing probe (test use).  Writes, through the same
+ * device address function the decode kernels use, the physical cache row
+ * (page * 64 + slot) of every key, or -1 where a key is not in the key set:
+ *   dense:  out [batch, max_blocks * 64] int64, device; entry (b, j) for
+ *           j < L_b, -1 for j >= L_b
+ *   sparse: out [batch, s_q, topk] int64, device; -1 for padding entries
+ */
+int mla_debug_row_ids(const int32_t* block_table, int max_blocks,
+                      const int32_t* cache_seqlens, int batch, int s_q,
+                      const int32_t* indices, int topk, int64_t* out, void* stream);
+
+/*
+ * mla_validate_inputs — opt-in device-side check of the index data the host
+ * cannot see: every block-table entry a key can reach lies in [0, num_pages),
+ * L_b <= max_blocks * 64 and L_b >= 0.  Writes the number of violations to
+ * *error_count (one int32, device; zeroed by this call) on `stream`.
+ */
+int mla_validate_inputs(const int32_t* block_table, int max_blocks,
+                        const int32_t* cache_seqlens, int batch, int s_q,
+                        const int32_t* indices, int topk, int64_t num_pages,
+                        int32_t* error_count, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_PAGED_KV_H_ */

@@ -1,0 +1,12 @@
+"""MI355X-native paged MLA decode: a C-ABI HIP library for gfx950 and its Python binding."""
+from .api import (  # noqa: F401
+    debug_row_ids,
+    get_mla_metadata,
+    mla_decode_with_kvcache,
+    plan_dims,
+    validate_inputs,
+    workspace_bytes,
+)
+
+__all__ = ["get_mla_metadata", "mla_decode_with_kvcache", "debug_row_ids", "validate_inputs",
+           "plan_dims", "workspace_bytes"]

@@ -1,0 +1,165 @@
+"""Python binding of the paged MLA decode library (argument marshalling only).
+
+The two calls follow "What is FlashMLA" (topnet.top), installation-and-use
+section, steps 2 and 3: a metadata call once per decode step, then a decode
+call per layer that returns ``(o, lse)``.  torch provides device memory and the
+current HIP stream; every step of the computation runs in the HIP library.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+
+D_QK = 576
+D_V = 512
+PAGE = 64
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _as_bits(t: torch.Tensor, name: str) -> torch.Tensor:
+    _need(t.dtype in (torch.bfloat16, torch.int16, torch.uint16), f"{name} must hold bf16 values")
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+    return t
+
+
+def _i32(t: torch.Tensor, name: str) -> torch.Tensor:
+    _need(t.dtype == torch.int32 and t.is_contiguous(), f"{name} must be a contiguous int32 tensor")
+    return t
+
+
+def plan_dims(batch: int, s_q: int, num_q_rows: int, h_kv: int, topk: int = 0,
+              num_workers: int = 0):
+    W, words, items = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _lib.check(_lib.lib().mla_plan_dims(batch, s_q, num_q_rows, h_kv, topk, num_workers,
+                                        ctypes.byref(W), ctypes.byref(words), ctypes.byref(items)),
+               "mla_plan_dims")
+    return W.value, words.value, items.value
+
+
+def workspace_bytes(batch, s_q, num_q_rows, h_kv, topk, dv, num_workers) -> int:
+    return int(_lib.lib().mla_workspace_bytes(batch, s_q, num_q_rows, h_kv, topk, dv, num_workers))
+
+
+def get_mla_metadata(cache_seqlens: torch.Tensor, num_q_rows: int, h_kv: int, *, s_q: int = 1,
+                     topk: int | None = None, num_workers: int | None = None):
+    """Split-KV plan: returns ``(tile_scheduler_metadata, num_splits)`` (int32, device).
+
+    ``num_q_rows`` is s_q * h_q / h_kv as in the pages' call.  In sparse mode
+    (``topk`` given) every query token is an item of ``topk`` keys and ``s_q``
+    must be passed.
+    """
+    _i32(cache_seqlens, "cache_seqlens")
+    _need(cache_seqlens.is_cuda, "cache_seqlens must be on the GPU")
+    batch = cache_seqlens.numel()
+    tk = int(topk or 0)
+    W, words, items = plan_dims(batch, s_q, num_q_rows, h_kv, tk, int(num_workers or 0))
+    dev = cache_seqlens.device
+    plan = torch.empty(words, dtype=torch.int32, device=dev)
+    num_splits = torch.empty(items + 1, dtype=torch.int32, device=dev)
+    _lib.check(_lib.lib().mla_get_metadata(_ptr(cache_seqlens), batch, s_q, num_q_rows, h_kv, tk, W,
+                                           _ptr(plan), _ptr(num_splits), _stream(dev)),
+               "mla_get_metadata")
+    return plan, num_splits
+
+
+def mla_decode_with_kvcache(q: torch.Tensor, kvcache: torch.Tensor, block_table: torch.Tensor,
+                            cache_seqlens: torch.Tensor, dv: int, tile_scheduler_metadata: torch.Tensor,
+                            num_splits: torch.Tensor, causal: bool = False,
+                            softmax_scale: float | None = None, indices: torch.Tensor | None = None,
+                            out: tuple | None = None, workspace: torch.Tensor | None = None,
+                            phases: int = 3):
+    """Paged MLA decode; returns ``(o [b, s_q, h_q, dv] bf16, lse [b, s_q, h_q] fp32)``.
+
+    ``phases`` (1 = split kernel, 2 = merge kernel, 3 = both) lets a caller
+    launch the two kernels separately with the same arguments and buffers.
+    """
+    _as_bits(q, "q")
+    _as_bits(kvcache, "kvcache")
+    _i32(block_table, "block_table")
+    _i32(cache_seqlens, "cache_seqlens")
+    _i32(tile_scheduler_metadata, "tile_scheduler_metadata")
+    _i32(num_splits, "num_splits")
+    _need(q.dim() == 4 and kvcache.dim() == 4, "q is [b, s_q, h_q, d], kvcache is [pages, 64, h_kv, d]")
+    B, s_q, h_q, d = q.shape
+    num_pages, page, h_kv, d2 = kvcache.shape
+    _need(d == d2, "q and kvcache disagree on d_qk")
+    _need(block_table.dim() == 2 and block_table.shape[0] == B, "block_table is [b, max_blocks]")
+    _need(cache_seqlens.numel() == B, "cache_seqlens is [b]")
+    topk = 0
+    if indices is not None:
+        _i32(indices, "indices")
+        _need(indices.dim() == 3 and tuple(indices.shape[:2]) == (B, s_q), "indices is [b, s_q, topk]")
+        topk = indices.shape[2]
+        _need(topk > 0, "indices needs topk > 0")
+    W = tile_scheduler_metadata.numel() // 8 - 1
+    _need(W >= 1, "tile_scheduler_metadata is too short")
+    scale = d ** -0.5 if softmax_scale is None else float(softmax_scale)
+    dev = q.device
+    if out is None:
+        o = torch.empty((B, s_q, h_q, dv), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((B, s_q, h_q), dtype=torch.float32, device=dev)
+    else:
+        o, lse = out
+    num_q_rows = s_q * h_q // max(h_kv, 1)
+    need = workspace_bytes(B, s_q, num_q_rows, h_kv, topk, dv, W) if dv > 0 else 0
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _lib.check(_lib.lib().mla_decode_with_kvcache_phase(
+        _ptr(q), _ptr(kvcache), num_pages, page, _ptr(block_table), block_table.shape[1],
+        _ptr(cache_seqlens), B, s_q, h_q, h_kv, d, dv, _ptr(tile_scheduler_metadata),
+        _ptr(num_splits), W, int(bool(causal)), ctypes.c_float(scale), _ptr(indices), topk,
+        _ptr(o), _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        int(phases), _stream(dev)), "mla_decode_with_kvcache")
+    return o, lse
+
+
+def debug_row_ids(block_table: torch.Tensor, cache_seqlens: torch.Tensor,
+                  indices: torch.Tensor | None = None, s_q: int = 1) -> torch.Tensor:
+    """Physical cache row of every key, as the decode kernels address it (int64, -1 = no key)."""
+    _i32(block_table, "block_table")
+    _i32(cache_seqlens, "cache_seqlens")
+    B, mb = block_table.shape
+    if indices is None:
+        out = torch.empty((B, mb * PAGE), dtype=torch.int64, device=block_table.device)
+        topk = 0
+    else:
+        _i32(indices, "indices")
+        s_q, topk = indices.shape[1], indices.shape[2]
+        out = torch.empty(tuple(indices.shape), dtype=torch.int64, device=block_table.device)
+    _lib.check(_lib.lib().mla_debug_row_ids(_ptr(block_table), mb, _ptr(cache_seqlens), B, s_q,
+                                            _ptr(indices), topk, _ptr(out), _stream(block_table.device)),
+               "mla_debug_row_ids")
+    return out
+
+
+def validate_inputs(block_table: torch.Tensor, cache_seqlens: torch.Tensor, num_pages: int,
+                    indices: torch.Tensor | None = None, s_q: int = 1) -> int:
+    """Number of out-of-range block-table entries / lengths (synchronises)."""
+    _i32(block_table, "block_table")
+    _i32(cache_seqlens, "cache_seqlens")
+    B, mb = block_table.shape
+    topk = 0
+    if indices is not None:
+        _i32(indices, "indices")
+        s_q, topk = indices.shape[1], indices.shape[2]
+    err = torch.empty(1, dtype=torch.int32, device=block_table.device)
+    _lib.check(_lib.lib().mla_validate_inputs(_ptr(block_table), mb, _ptr(cache_seqlens), B, s_q,
+                                              _ptr(indices), topk, num_pages, _ptr(err),
+                                              _stream(block_table.device)),
+               "mla_validate_inputs")
+    return int(err.item())

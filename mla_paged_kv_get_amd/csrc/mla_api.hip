@@ -1,0 +1,239 @@
+// C ABI of the paged MLA decode library (declared in include/mla_paged_kv.h).
+// Host-side argument checks, worker sizing and kernel launches; the kernels
+// are in mla_plan.hip, mla_decode.hip and mla_aux.hip.
+#include "mla_paged_kv.h"
+
+#include <math.h>
+
+#include "mla_common.h"
+
+namespace mla {
+int plan_max_items();
+}
+
+namespace {
+
+using namespace mla;
+
+constexpr int kMaxDevices = 64;
+int g_cu_count[kMaxDevices];   // 0 = not queried yet
+
+int cu_count(int* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MLA_ERR_HIP;
+  if (g_cu_count[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      return MLA_ERR_HIP;
+    g_cu_count[dev] = n;
+  }
+  *out = g_cu_count[dev];
+  return MLA_OK;
+}
+
+struct Shape {
+  int items;        // work items
+  int rows;         // query rows per item
+  int variant;
+  int m_tiles;      // workgroups per worker
+};
+
+int shape_of(int batch, int s_q, int num_q_rows, int h_kv, int topk, Shape* s) {
+  if (batch < 0 || s_q < 1 || num_q_rows < 1 || h_kv < 1) return MLA_ERR_INVALID_ARGUMENT;
+  if (h_kv != 1) return MLA_ERR_UNSUPPORTED;
+  if (topk > 0) {
+    if (num_q_rows % s_q) return MLA_ERR_INVALID_ARGUMENT;
+    const int64_t items = (int64_t)batch * s_q;
+    if (items > (1 << 30)) return MLA_ERR_INVALID_ARGUMENT;
+    s->items = (int)items;
+    s->rows = num_q_rows / s_q;
+  } else {
+    s->items = batch;
+    s->rows = num_q_rows;
+  }
+  s->variant = pick_variant(s->rows);
+  const int vr = variant_rows(s->variant);
+  s->m_tiles = (s->rows + vr - 1) / vr;
+  return MLA_OK;
+}
+
+int workers_for(const Shape& s, int request, int* W) {
+  if (request > 0) {
+    *W = request;
+    return MLA_OK;
+  }
+  int cus = 0;
+  const int st = cu_count(&cus);
+  if (st != MLA_OK) return st;
+  // One workgroup per CU (each holds two 72 KB tiles of LDS); the row tiles of
+  // a worker share the CUs.
+  *W = cus / s.m_tiles > 0 ? cus / s.m_tiles : 1;
+  return MLA_OK;
+}
+
+size_t workspace_for(const Shape& s, int dv, int W) {
+  const size_t slots = (size_t)s.items + (size_t)W;
+  return slots * (size_t)s.rows * ((size_t)dv + 1) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(int status) {
+  switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "unsupported shape (needs d_qk=576, dv=512, page 64, h_kv=1)";
+    case MLA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MLA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int mla_plan_dims(int batch, int s_q, int num_q_rows, int h_kv, int topk, int num_workers_request,
+                  int* out_num_workers, int* out_plan_words, int* out_num_items) {
+  if (!out_num_workers || !out_plan_words || !out_num_items) return MLA_ERR_INVALID_ARGUMENT;
+  if (num_workers_request < 0) return MLA_ERR_INVALID_ARGUMENT;
+  Shape s;
+  int st = shape_of(batch, s_q, num_q_rows, h_kv, topk, &s);
+  if (st != MLA_OK) return st;
+  if (num_workers_request > (1 << 20)) return MLA_ERR_INVALID_ARGUMENT;
+  int W = 0;
+  st = workers_for(s, num_workers_request, &W);
+  if (st != MLA_OK) return st;
+  *out_num_workers = W;
+  *out_plan_words = kPlanWords * (W + 1);
+  *out_num_items = s.items;
+  return MLA_OK;
+}
+
+int mla_get_metadata(const int32_t* cache_seqlens, int batch, int s_q, int num_q_rows, int h_kv,
+                     int topk, int num_workers, int32_t* plan, int32_t* num_splits, void* stream) {
+  if (!plan || !num_splits) return MLA_ERR_INVALID_ARGUMENT;
+  if (topk <= 0 && !cache_seqlens && batch > 0) return MLA_ERR_INVALID_ARGUMENT;
+  if (num_workers < 1 || num_workers > (1 << 20)) return MLA_ERR_INVALID_ARGUMENT;
+  Shape s;
+  const int st = shape_of(batch, s_q, num_q_rows, h_kv, topk, &s);
+  if (st != MLA_OK) return st;
+  if (s.items > mla::plan_max_items()) return MLA_ERR_UNSUPPORTED;
+  const int overhead = variant_overhead(s.variant);
+  const hipError_t e = launch_plan(cache_seqlens, batch, s_q, topk > 0 ? topk : 0, s.items,
+                                   num_workers, overhead, plan, num_splits,
+                                   reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+size_t mla_workspace_bytes(int batch, int s_q, int num_q_rows, int h_kv, int topk, int dv,
+                           int num_workers) {
+  Shape s;
+  if (shape_of(batch, s_q, num_q_rows, h_kv, topk, &s) != MLA_OK || dv < 1 || num_workers < 1)
+    return 0;
+  return workspace_for(s, dv, num_workers);
+}
+
+int mla_decode_with_kvcache_phase(const void* q, const void* kvcache, int64_t num_pages,
+                                  int page_size, const int32_t* block_table, int max_blocks,
+                                  const int32_t* cache_seqlens, int batch, int s_q, int h_q,
+                                  int h_kv, int d_qk, int dv, const int32_t* plan,
+                                  const int32_t* num_splits, int num_workers, int causal,
+                                  float softmax_scale, const int32_t* indices, int topk, void* o,
+                                  float* lse, void* workspace, size_t workspace_bytes, int phases,
+                                  void* stream) {
+  if (phases < 1 || phases > 3) return MLA_ERR_INVALID_ARGUMENT;
+  if (batch < 0 || s_q < 1 || h_q < 1 || h_kv < 1 || max_blocks < 1 || num_pages < 1)
+    return MLA_ERR_INVALID_ARGUMENT;
+  if (h_q % h_kv) return MLA_ERR_INVALID_ARGUMENT;
+  if (page_size != kPage || d_qk != kDqk || dv != kDv || h_kv != 1) return MLA_ERR_UNSUPPORTED;
+  if (causal != 0 && causal != 1) return MLA_ERR_INVALID_ARGUMENT;
+  if ((indices != nullptr) != (topk > 0)) return MLA_ERR_INVALID_ARGUMENT;
+  if (indices && causal) return MLA_ERR_INVALID_ARGUMENT;
+  if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return MLA_ERR_INVALID_ARGUMENT;
+  if (num_workers < 1 || num_workers > (1 << 20)) return MLA_ERR_INVALID_ARGUMENT;
+  if (!q || !kvcache || !block_table || !cache_seqlens || !plan || !num_splits || !o || !lse)
+    return MLA_ERR_INVALID_ARGUMENT;
+  if ((int64_t)max_blocks * kPage > (int64_t)0x7fffffff) return MLA_ERR_INVALID_ARGUMENT;
+  if (num_pages > ((int64_t)1 << 31) / kPage) return MLA_ERR_UNSUPPORTED;
+  Shape s;
+  const int num_q_rows = s_q * h_q / h_kv;
+  int st = shape_of(batch, s_q, num_q_rows, h_kv, topk, &s);
+  if (st != MLA_OK) return st;
+  const size_t need = workspace_for(s, dv, num_workers);
+  if (workspace_bytes < need) return MLA_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace) return MLA_ERR_INVALID_ARGUMENT;
+  if (batch == 0) return MLA_OK;
+
+  DecodeArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.kv = static_cast<const uint16_t*>(kvcache);
+  a.block_table = block_table;
+  a.seqlens = cache_seqlens;
+  a.indices = indices;
+  a.plan = plan;
+  a.num_splits = num_splits;
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  const size_t slots = (size_t)s.items + (size_t)num_workers;
+  a.part_o = static_cast<float*>(workspace);
+  a.part_lse = a.part_o + slots * (size_t)s.rows * kDv;
+  a.max_blocks = max_blocks;
+  a.batch = batch;
+  a.s_q = s_q;
+  a.h_q = h_q;
+  a.M = s.rows;
+  a.num_items = s.items;
+  a.num_workers = num_workers;
+  a.m_tiles = s.m_tiles;
+  a.topk = topk > 0 ? topk : 0;
+  a.causal = causal;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (phases & 1) {
+    if (launch_decode(a, s.variant, hs) != hipSuccess) return MLA_ERR_HIP;
+  }
+  if (phases & 2) {
+    if (launch_combine(a, hs) != hipSuccess) return MLA_ERR_HIP;
+  }
+  return MLA_OK;
+}
+
+int mla_decode_with_kvcache(const void* q, const void* kvcache, int64_t num_pages, int page_size,
+                            const int32_t* block_table, int max_blocks,
+                            const int32_t* cache_seqlens, int batch, int s_q, int h_q, int h_kv,
+                            int d_qk, int dv, const int32_t* plan, const int32_t* num_splits,
+                            int num_workers, int causal, float softmax_scale,
+                            const int32_t* indices, int topk, void* o, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return mla_decode_with_kvcache_phase(q, kvcache, num_pages, page_size, block_table, max_blocks,
+                                       cache_seqlens, batch, s_q, h_q, h_kv, d_qk, dv, plan,
+                                       num_splits, num_workers, causal, softmax_scale, indices,
+                                       topk, o, lse, workspace, workspace_bytes, 3, stream);
+}
+
+int mla_debug_row_ids(const int32_t* block_table, int max_blocks, const int32_t* cache_seqlens,
+                      int batch, int s_q, const int32_t* indices, int topk, int64_t* out,
+                      void* stream) {
+  if (!block_table || !cache_seqlens || !out || max_blocks < 1 || batch < 0 || s_q < 1)
+    return MLA_ERR_INVALID_ARGUMENT;
+  if ((indices != nullptr) != (topk > 0)) return MLA_ERR_INVALID_ARGUMENT;
+  if (batch == 0) return MLA_OK;
+  const hipError_t e = launch_row_ids(block_table, max_blocks, cache_seqlens, batch, s_q, indices,
+                                      topk, out, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int mla_validate_inputs(const int32_t* block_table, int max_blocks, const int32_t* cache_seqlens,
+                        int batch, int s_q, const int32_t* indices, int topk, int64_t num_pages,
+                        int32_t* error_count, void* stream) {
+  if (!block_table || !cache_seqlens || !error_count || max_blocks < 1 || batch < 0 || s_q < 1 ||
+      num_pages < 1)
+    return MLA_ERR_INVALID_ARGUMENT;
+  if ((indices != nullptr) != (topk > 0)) return MLA_ERR_INVALID_ARGUMENT;
+  const hipError_t e = launch_validate(block_table, max_blocks, cache_seqlens, batch, s_q, indices,
+                                       topk, num_pages, error_count,
+                                       reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,88 @@
+// Shared constants, device helpers and launch descriptors of the gfx950 paged
+// MLA decode library.  Kernels live in mla_plan.hip, mla_decode.hip and
+// mla_aux.hip; the C ABI in mla_api.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+constexpr int kPage = 64;                 // tokens per cache page
+constexpr int kDqk = 576;                 // values per latent row (512 latent + 64 RoPE)
+constexpr int kDv = 512;                  // V = first 512 values of the row
+constexpr int kRowBytes = kDqk * 2;       // 1152 B per cached row
+constexpr int kChunks = kRowBytes / 16;   // 72 chunks of 16 B per row
+constexpr int kTileBytes = kPage * kRowBytes;  // 73728 B per 64-row tile
+constexpr int kPlanWords = 8;
+constexpr int kPlanVersion = 1;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+#define MLA_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+#define MLA_GBL(p) ((const __attribute__((address_space(1))) void*)(p))
+
+// Physical cache row of logical key position `pos` of a sequence whose block
+// table row is `bt_row` (page = bt_row[pos / 64], slot = pos % 64).  The decode
+// kernels and the indexing probe both address the cache through this function.
+__device__ __forceinline__ int64_t cache_row(const int32_t* __restrict__ bt_row, int pos) {
+  return (int64_t)bt_row[pos >> 6] * kPage + (pos & (kPage - 1));
+}
+
+// Whether an index-list entry is a key of a sequence of length L.
+__device__ __forceinline__ bool sparse_key_valid(int idx, int L) {
+  return idx >= 0 && idx < L;
+}
+
+// Arguments of the decode kernels (passed by value).
+struct DecodeArgs {
+  const uint16_t* q;          // [items * M, 576]   (dense: [B, s_q, h_q, 576])
+  const uint16_t* kv;         // [num_pages * 64, 576]
+  const int32_t* block_table; // [B, max_blocks]
+  const int32_t* seqlens;     // [B]
+  const int32_t* indices;     // [B * s_q, topk] or null
+  const int32_t* plan;        // [(W + 1) * 8]
+  const int32_t* num_splits;  // [items + 1]
+  uint16_t* o;                // [items * M, 512]
+  float* lse;                 // [items * M]
+  float* part_o;              // [slots * M, 512]
+  float* part_lse;            // [slots * M]
+  int max_blocks;
+  int batch;
+  int s_q;
+  int h_q;
+  int M;                      // query rows per item
+  int num_items;
+  int num_workers;
+  int m_tiles;                // workgroups per worker (row tiles)
+  int topk;                   // 0 = dense
+  int causal;
+  float scale_log2;           // softmax_scale * log2(e)
+};
+
+// Launchers (defined next to their kernels).
+hipError_t launch_plan(const int32_t* seqlens, int batch, int s_q, int topk, int num_items,
+                       int num_workers, int overhead, int32_t* plan, int32_t* num_splits,
+                       hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, int variant, hipStream_t stream);
+hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_row_ids(const int32_t* block_table, int max_blocks, const int32_t* seqlens,
+                          int batch, int s_q, const int32_t* indices, int topk, int64_t* out,
+                          hipStream_t stream);
+hipError_t launch_validate(const int32_t* block_table, int max_blocks, const int32_t* seqlens,
+                           int batch, int s_q, const int32_t* indices, int topk,
+                           int64_t num_pages, int32_t* error_count, hipStream_t stream);
+
+// Decode variants: how a workgroup covers an item's query rows.
+enum Variant : int {
+  kVariantRows16 = 0,    // <= 16 rows: 4 waves split each 64-token tile 4 ways
+  kVariantRows64 = 1,    // > 16 rows: 4 waves x 16 rows = 64-row tiles
+};
+constexpr int variant_rows(int v) { return v == kVariantRows16 ? 16 : 64; }
+constexpr int variant_overhead(int v) { return v == kVariantRows16 ? 2 : 2; }
+inline int pick_variant(int rows_per_item) { return rows_per_item <= 16 ? kVariantRows16 : kVariantRows64; }
+
+}  // namespace mla

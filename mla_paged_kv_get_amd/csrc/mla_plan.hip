@@ -1,0 +1,161 @@
+// Split-KV tile scheduler ("get_mla_metadata" of "What is FlashMLA",
+// topnet.top, installation-and-use section, step 2: it returns the tile
+// scheduler metadata and num_splits).  The pages do not say how work is split;
+// this kernel implements the rule stated in the C header:
+//   n_i = ceil(len_i / 64) blocks, item cost = overhead + n_i, items laid end
+//   to end on a cost axis (start C_i, total T), P = max(1, ceil(T / W)) units
+//   per worker, worker w owning units [w P, (w + 1) P), block b of item i on
+//   unit C_i + overhead + b.
+// One workgroup computes it from closed forms: the workers touching item i's
+// blocks are floor((C_i + overhead) / P) .. floor((C_{i+1} - 1) / P), so the
+// split count and every worker's split number follow without a walk.
+#include "mla_common.h"
+
+namespace mla {
+namespace {
+
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanMaxItems = 16384;
+
+// Inclusive scan of one int per thread over the workgroup.
+__device__ int block_inclusive_scan(int v, int* wave_sums) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int o = __shfl_up(v, d, 64);
+    if (lane >= d) v += o;
+  }
+  if (lane == 63) wave_sums[wave] = v;
+  __syncthreads();
+  if (wave == 0) {
+    int s = lane < (kPlanThreads / 64) ? wave_sums[lane] : 0;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      int o = __shfl_up(s, d, 64);
+      if (lane >= d) s += o;
+    }
+    if (lane < kPlanThreads / 64) wave_sums[lane] = s;
+  }
+  __syncthreads();
+  const int before = wave > 0 ? wave_sums[wave - 1] : 0;
+  __syncthreads();
+  return v + before;
+}
+
+__device__ __forceinline__ int item_blocks(const int32_t* seqlens, int topk, int i) {
+  const int len = topk > 0 ? topk : seqlens[i];
+  return len > 0 ? (len + kPage - 1) / kPage : 0;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ seqlens,
+                                                            int topk, int num_items, int W, int c,
+                                                            int32_t* __restrict__ plan,
+                                                            int32_t* __restrict__ num_splits) {
+  __shared__ int start[kPlanMaxItems + 1];
+  __shared__ int wave_sums[kPlanThreads / 64];
+  const int tid = threadIdx.x;
+  const int per = (num_items + kPlanThreads - 1) / kPlanThreads;
+  const int i0 = min(tid * per, num_items), i1 = min(i0 + per, num_items);
+
+  // Start of every item on the cost axis.
+  int local = 0;
+  for (int i = i0; i < i1; ++i) local += c + item_blocks(seqlens, topk, i);
+  const int incl = block_inclusive_scan(local, wave_sums);
+  int run = incl - local;
+  for (int i = i0; i < i1; ++i) {
+    start[i] = run;
+    run += c + item_blocks(seqlens, topk, i);
+  }
+  if (tid == kPlanThreads - 1) start[num_items] = incl;
+  __syncthreads();
+  const int T = start[num_items];
+  const int P = max(1, (T + W - 1) / W);
+
+  // Split counts and their exclusive prefix.
+  local = 0;
+  for (int i = i0; i < i1; ++i) {
+    const int first = start[i] + c, end = start[i + 1];
+    if (end > first) local += (end - 1) / P - first / P + 1;
+  }
+  const int sincl = block_inclusive_scan(local, wave_sums);
+  run = sincl - local;
+  for (int i = i0; i < i1; ++i) {
+    num_splits[i] = run;
+    const int first = start[i] + c, end = start[i + 1];
+    if (end > first) run += (end - 1) / P - first / P + 1;
+  }
+  if (tid == kPlanThreads - 1) num_splits[num_items] = sincl;
+
+  // One row per worker.
+  for (int w = tid; w < W; w += kPlanThreads) {
+    int32_t* row = plan + kPlanWords * (1 + w);
+    const int lo = w * P, hi = min(lo + P, T);
+    int first_item = -1, first_blk = 0, last_item = -1, last_end = 0, split = 0;
+    if (lo < hi) {
+      // Last item starting at or before lo.
+      int a = 0, b = num_items - 1;
+      while (a < b) {
+        const int m = (a + b + 1) >> 1;
+        if (start[m] <= lo) a = m; else b = m - 1;
+      }
+      for (int i = a; i < num_items && start[i] < hi; ++i) {
+        const int bl = max(lo, start[i] + c), bh = min(hi, start[i + 1]);
+        if (bl < bh) {
+          first_item = i;
+          first_blk = bl - start[i] - c;
+          split = w - (start[i] + c) / P;
+          break;
+        }
+      }
+      if (first_item >= 0) {
+        // Last item starting before hi.
+        a = first_item;
+        b = num_items - 1;
+        while (a < b) {
+          const int m = (a + b + 1) >> 1;
+          if (start[m] < hi) a = m; else b = m - 1;
+        }
+        for (int i = a; i >= first_item; --i) {
+          const int bl = max(lo, start[i] + c), bh = min(hi, start[i + 1]);
+          if (bl < bh) {
+            last_item = i;
+            last_end = bh - start[i] - c;
+            break;
+          }
+        }
+      }
+    }
+    row[0] = first_item;
+    row[1] = first_item >= 0 ? first_blk : 0;
+    row[2] = last_item;
+    row[3] = last_end;
+    row[4] = first_item >= 0 ? split : 0;
+    row[5] = 0;
+    row[6] = 0;
+    row[7] = 0;
+  }
+  if (tid == 0) {
+    plan[0] = W;
+    plan[1] = c;
+    plan[2] = P;
+    plan[3] = num_items;
+    plan[4] = kPlanVersion;
+    plan[5] = kPage;
+    plan[6] = T;
+    plan[7] = 0;
+  }
+}
+
+}  // namespace
+
+int plan_max_items() { return kPlanMaxItems; }
+
+hipError_t launch_plan(const int32_t* seqlens, int /*batch*/, int /*s_q*/, int topk, int num_items,
+                       int num_workers, int overhead, int32_t* plan, int32_t* num_splits,
+                       hipStream_t stream) {
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, seqlens, topk, num_items,
+                     num_workers, overhead, plan, num_splits);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -3,7 +3,7 @@
 This module only draws random numbers and lays them out (sequence lengths,
 page permutations, block tables, bf16 bit patterns of N(0, 1) values, sparse
 top-k index lists).  It holds none of the decode arithmetic; the tests and the
-benchmark feed the same arrays to the HIP library and to the CPU oracle.
+benchmark feed the same arrays to the HIP library and to the CPU reference.
 
 Recipe (NumPy PCG64, seed = workload number): draw the lengths, then the page
 permutation, then q, then the cache, then (sparse only) the indices.  Normal

@@ -1,0 +1,139 @@
+"""The C-ABI library on the CPU: it loads, exports what the header declares,
+and rejects bad arguments before enqueuing anything (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mla_paged_kv_get_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            txt = open(os.path.join(ROOT, "include", fn)).read()
+            txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+            names += re.findall(r"^\s*(?:const\s+)?[\w\*\s]+?\b(mla_\w+)\s*\(", txt, flags=re.M)
+    return sorted(set(names))
+
+
+def test_exports_every_declared_symbol():
+    l = _lib.lib()
+    names = _declared()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(l, n), n
+    assert set(names) == set(_lib.EXPORTS)
+
+
+def test_one_hip_runtime_mapped():
+    _lib.lib()
+    maps = open("/proc/self/maps").read()
+    paths = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(paths) <= 1, paths
+
+
+def test_status_strings():
+    l = _lib.lib()
+    for s in range(5):
+        assert l.mla_status_string(s)
+    assert l.mla_status_string(99) == b"unknown status"
+
+
+def _dims(*a):
+    W, w, it = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    st = _lib.lib().mla_plan_dims(*a, ctypes.byref(W), ctypes.byref(w), ctypes.byref(it))
+    return st, W.value, w.value, it.value
+
+
+def test_plan_dims():
+    assert _dims(64, 1, 16, 1, 0, 256) == (0, 256, 8 * 257, 64)
+    assert _dims(16, 8, 8 * 128, 1, 2048, 100) == (0, 100, 8 * 101, 128)       # sparse: items = b * s_q
+    assert _dims(4, 1, 16, 2, 0, 8)[0] == _lib.MLA_ERR_UNSUPPORTED              # h_kv = 2
+    assert _dims(4, 3, 16, 1, 64, 8)[0] == _lib.MLA_ERR_INVALID_ARGUMENT        # rows not a multiple of s_q
+    assert _dims(-1, 1, 16, 1, 0, 8)[0] == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert _dims(4, 1, 16, 1, 0, -3)[0] == _lib.MLA_ERR_INVALID_ARGUMENT
+
+
+def test_workspace_bytes():
+    l = _lib.lib()
+    assert l.mla_workspace_bytes(64, 1, 16, 1, 0, 512, 256) == (64 + 256) * 16 * 513 * 4
+    assert l.mla_workspace_bytes(16, 8, 1024, 1, 2048, 512, 256) == (128 + 256) * 128 * 513 * 4
+    assert l.mla_workspace_bytes(64, 1, 16, 1, 0, 512, 0) == 0
+
+
+DUMMY = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails its host checks
+
+
+def _decode(**kw):
+    a = dict(q=DUMMY, kv=DUMMY, num_pages=10, page=64, bt=DUMMY, mb=4, sl=DUMMY, batch=2, s_q=1,
+             h_q=16, h_kv=1, d=576, dv=512, plan=DUMMY, ns=DUMMY, W=8, causal=0, scale=0.05,
+             idx=None, topk=0, o=DUMMY, lse=DUMMY, ws=DUMMY, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return _lib.lib().mla_decode_with_kvcache(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=512), _lib.MLA_ERR_UNSUPPORTED),
+    (dict(dv=256), _lib.MLA_ERR_UNSUPPORTED),
+    (dict(page=32), _lib.MLA_ERR_UNSUPPORTED),
+    (dict(h_kv=2, h_q=16), _lib.MLA_ERR_UNSUPPORTED),
+    (dict(h_q=15, h_kv=2), _lib.MLA_ERR_INVALID_ARGUMENT),
+    (dict(q=None), _lib.MLA_ERR_INVALID_ARGUMENT),
+    (dict(o=None), _lib.MLA_ERR_INVALID_ARGUMENT),
+    (dict(causal=2), _lib.MLA_ERR_INVALID_ARGUMENT),
+    (dict(idx=DUMMY, topk=0), _lib.MLA_ERR_INVALID_ARGUMENT),
+    (dict(idx=None, topk=16), _lib.MLA_ERR_INVALID_ARGUMENT),
+    (dict(idx=DUMMY, topk=16, causal=1), _lib.MLA_ERR_INVALID_ARGUMENT),
+    (dict(scale=0.0), _lib.MLA_ERR_INVALID_ARGUMENT),
+    (dict(scale=float("nan")), _lib.MLA_ERR_INVALID_ARGUMENT),
+    (dict(W=0), _lib.MLA_ERR_INVALID_ARGUMENT),
+    (dict(ws_bytes=100), _lib.MLA_ERR_WORKSPACE_TOO_SMALL),
+    (dict(s_q=0), _lib.MLA_ERR_INVALID_ARGUMENT),
+    (dict(mb=0), _lib.MLA_ERR_INVALID_ARGUMENT),
+])
+def test_decode_rejects(kw, code):
+    assert _decode(**kw) == code
+
+
+def test_decode_empty_batch_is_noop():
+    assert _decode(batch=0) == _lib.MLA_OK
+
+
+def test_phase_argument_checked():
+    l = _lib.lib()
+    args = [DUMMY, DUMMY, 10, 64, DUMMY, 4, DUMMY, 2, 1, 16, 1, 576, 512, DUMMY, DUMMY, 8, 0,
+            ctypes.c_float(0.05), None, 0, DUMMY, DUMMY, DUMMY, 1 << 40]
+    assert l.mla_decode_with_kvcache_phase(*args, 0, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert l.mla_decode_with_kvcache_phase(*args, 4, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+
+
+def test_metadata_rejects():
+    l = _lib.lib()
+    assert l.mla_get_metadata(DUMMY, 4, 1, 16, 1, 0, 8, None, DUMMY, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert l.mla_get_metadata(DUMMY, 4, 1, 16, 1, 0, 0, DUMMY, DUMMY, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert l.mla_get_metadata(DUMMY, 4, 1, 16, 2, 0, 8, DUMMY, DUMMY, None) == _lib.MLA_ERR_UNSUPPORTED
+    assert l.mla_get_metadata(None, 4, 1, 16, 1, 0, 8, DUMMY, DUMMY, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert l.mla_get_metadata(DUMMY, 20000, 1, 16, 1, 0, 8, DUMMY, DUMMY, None) == _lib.MLA_ERR_UNSUPPORTED
+
+
+def test_debug_and_validate_reject():
+    l = _lib.lib()
+    assert l.mla_debug_row_ids(None, 4, DUMMY, 2, 1, None, 0, DUMMY, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert l.mla_debug_row_ids(DUMMY, 4, DUMMY, 2, 1, DUMMY, 0, DUMMY, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert l.mla_validate_inputs(DUMMY, 4, DUMMY, 2, 1, None, 0, 10, None, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert l.mla_validate_inputs(DUMMY, 4, DUMMY, 2, 1, None, 0, 0, DUMMY, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+
+
+def test_product_path_does_not_use_the_oracle():
+    import mla_paged_kv_get_amd
+    pkg = os.path.dirname(mla_paged_kv_get_amd.__file__)
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".h", ".cpp")):
+                txt = open(os.path.join(dirpath, fn)).read()
+                assert not re.search(r"^\s*(from|import)\s+oracle\b|\boracle\.|mla_oracle", txt, re.M), fn

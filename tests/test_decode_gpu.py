@@ -1,0 +1,243 @@
+"""GPU parity of the HIP path against the CPU oracle (through the C ABI).
+
+Floating point: max|dO| <= 2e-2 against the oracle's float64 O and
+max|dLSE| <= 1e-3.  Integer work (plan, num_splits, row addressing) is
+compared bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import mla_oracle as orc
+from mla_paged_kv_get_amd import workloads as wl
+from tests.helpers import Dev, compare, run_gpu, i32_dev, bits_to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _m():
+    import mla_paged_kv_get_amd as m
+    return m
+
+
+# ---------------------------------------------------------------------------
+# Scheduler and addressing: bit-exact
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("W", [1, 3, 64, 256, 1000, None])
+def test_plan_bit_exact(W):
+    m = _m()
+    rng = np.random.default_rng(123)
+    cases = [
+        ([37, 130], 16, 1, None),
+        (list(wl.memory_bound().cache_seqlens) if W in (256, None) else list(rng.integers(1, 4097, 64)), 16, 1, None),
+        (list(rng.integers(0, 300, 50)) + [0, 0, 5000], 128, 2, None),
+        ([65536] * 4, 128, 8, 2048),
+    ]
+    for lengths, h_q, s_q, topk in cases:
+        sl = i32_dev(np.array(lengths))
+        plan, ns = m.get_mla_metadata(sl, s_q * h_q, 1, s_q=s_q, topk=topk, num_workers=W)
+        torch.cuda.synchronize()
+        p = plan.cpu().numpy()
+        Wg, c = int(p[0]), int(p[1])
+        if W is not None:
+            assert Wg == W
+        items = [topk] * (len(lengths) * s_q) if topk else lengths
+        ref_p, ref_ns = orc.plan(items, Wg, c)
+        assert (p == ref_p).all(), f"plan differs for W={Wg} lengths={lengths[:5]}"
+        assert (ns.cpu().numpy() == ref_ns).all()
+
+
+@pytest.mark.parametrize("name", ["tiny", "memory_bound", "mtp_causal"])
+def test_row_ids_dense_bit_exact(name):
+    m = _m()
+    w = wl.NAMED[name]()
+    rows = m.debug_row_ids(i32_dev(w.block_table), i32_dev(w.cache_seqlens)).cpu().numpy()
+    mb = w.block_table.shape[1]
+    for b in range(w.B):
+        L = int(w.cache_seqlens[b])
+        ref = orc.physical_rows(w.block_table, b, np.arange(L))
+        assert (rows[b, :L] == ref).all()
+        assert (rows[b, L:mb * 64] == -1).all()
+
+
+def test_row_ids_sparse_bit_exact():
+    m = _m()
+    w = wl.sparse_topk(B=4)
+    idx = w.indices.copy()
+    idx[0, 0, :5] = [-1, 65536, 70000, -7, 3]
+    rows = m.debug_row_ids(i32_dev(w.block_table), i32_dev(w.cache_seqlens), i32_dev(idx)).cpu().numpy()
+    for b in range(w.B):
+        for s in range(w.s_q):
+            v = idx[b, s]
+            ok = (v >= 0) & (v < w.cache_seqlens[b])
+            ref = np.full(v.shape, -1, dtype=np.int64)
+            ref[ok] = orc.physical_rows(w.block_table, b, v[ok])
+            assert (rows[b, s] == ref).all()
+
+
+# ---------------------------------------------------------------------------
+# Decode parity on the named workloads
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("poison", [False, True])
+def test_tiny(poison):
+    w = wl.tiny(poison=poison)
+    o, lse, _ = run_gpu(Dev(w))
+    compare(w, o, lse, label=f"tiny poison={poison}")
+
+
+@pytest.mark.parametrize("poison", [False, True])
+def test_memory_bound_full(poison):
+    w = wl.memory_bound(poison=poison)
+    o, lse, _ = run_gpu(Dev(w))
+    compare(w, o, lse, label=f"memory-bound poison={poison}")
+
+
+def test_near_ridge_sampled():
+    w = wl.near_ridge()
+    o, lse, _ = run_gpu(Dev(w))
+    items = [(b, 0) for b in (0, 1, 31, 64, 100, 127)]
+    compare(w, o, lse, items=items, label="near-ridge")
+
+
+def test_mtp_causal_sampled():
+    w = wl.mtp_causal()
+    o, lse, _ = run_gpu(Dev(w))
+    order = np.argsort(w.cache_seqlens)
+    bs = sorted({int(order[0]), int(order[1]), int(order[15]), int(order[-1]), 7})
+    compare(w, o, lse, items=[(b, s) for b in bs for s in range(2)], label="mtp-causal")
+
+
+def test_sparse_topk_sampled():
+    w = wl.sparse_topk()
+    o, lse, _ = run_gpu(Dev(w))
+    items = [(0, 0), (0, 7), (5, 3), (11, 1), (15, 7)]
+    compare(w, o, lse, items=items, label="sparse-topk")
+
+
+# ---------------------------------------------------------------------------
+# Edge cases
+# ---------------------------------------------------------------------------
+EDGE_L = [1, 2, 63, 64, 65, 127, 128, 129, 0, 200, 4097]
+
+
+@pytest.mark.parametrize("h_q", [16, 32, 64, 128])
+def test_edge_lengths(h_q):
+    w = wl.build("edge", 31, np.array(EDGE_L), B=len(EDGE_L), s_q=1, h_q=h_q, num_pages=200, poison=True)
+    o, lse, _ = run_gpu(Dev(w))
+    compare(w, o, lse, label=f"edge h_q={h_q}")
+
+
+@pytest.mark.parametrize("h_q,s_q", [(16, 2), (8, 2), (128, 2), (64, 4)])
+def test_causal_edges(h_q, s_q):
+    L = [1, 2, 3, 64, 65, 130, 0]
+    w = wl.build("causal-edge", 32, np.array(L), B=len(L), s_q=s_q, h_q=h_q, num_pages=40,
+                 causal=True, poison=True)
+    o, lse, _ = run_gpu(Dev(w))
+    compare(w, o, lse, label=f"causal h_q={h_q} s_q={s_q}")
+
+
+def test_noncausal_multi_token():
+    w = wl.build("mtp-noncausal", 33, np.array([100, 7, 300]), B=3, s_q=2, h_q=64, num_pages=20)
+    o, lse, _ = run_gpu(Dev(w))
+    compare(w, o, lse, label="s_q=2 non-causal")
+
+
+def test_sparse_pads_and_empty():
+    w = wl.build("sparse-pad", 34, np.array([300, 90, 0]), B=3, s_q=2, h_q=128, num_pages=20,
+                 poison=True, topk=None)
+    rng = np.random.default_rng(4)
+    idx = np.full((3, 2, 150), -1, dtype=np.int32)
+    idx[0, 0, :100] = rng.choice(300, 100, replace=False)
+    idx[0, 1, :150] = rng.choice(300, 150, replace=False)
+    idx[0, 1, 7] = 300          # out of range -> padding
+    idx[1, 0, 20:40] = np.arange(20)
+    # idx[1, 1] all padding; sequence 2 is empty
+    w.indices = idx
+    o, lse, _ = run_gpu(Dev(w))
+    compare(w, o, lse, label="sparse pads")
+    lg = lse.cpu().numpy()
+    assert np.isneginf(lg[1, 1]).all() and np.isneginf(lg[2]).all()
+    assert (o[1, 1].float().cpu().numpy() == 0).all()
+
+
+def test_softmax_scale():
+    w = wl.tiny()
+    o, lse, _ = run_gpu(Dev(w), softmax_scale=0.11)
+    compare(w, o, lse, softmax_scale=0.11, label="scale 0.11")
+
+
+# ---------------------------------------------------------------------------
+# Invariants
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("W", [1, 5, 33, 700])
+def test_split_count_invariance(W):
+    w = wl.build("splits", 35, np.array([4096, 1, 2000, 777, 64, 65]), B=6, s_q=2, h_q=16,
+                 num_pages=200, causal=True, poison=True)
+    o, lse, plan = run_gpu(Dev(w), num_workers=W)
+    compare(w, o, lse, label=f"W={W}")
+
+
+def test_split_count_invariance_wide_rows():
+    w = wl.build("splits-wide", 36, np.array([3000, 129, 64]), B=3, s_q=1, h_q=128, num_pages=80)
+    for W in (1, 4, 90):
+        o, lse, _ = run_gpu(Dev(w), num_workers=W)
+        compare(w, o, lse, label=f"h128 W={W}")
+
+
+def test_page_permutation_bit_exact():
+    w = wl.memory_bound()
+    d = Dev(w)
+    o1, l1, plan = run_gpu(d)
+    perm = np.random.default_rng(8).permutation(w.kv.shape[0])
+    kv2 = np.empty_like(w.kv)
+    kv2[perm] = w.kv
+    d.kv = bits_to_dev(kv2)
+    d.bt = i32_dev(perm[w.block_table].astype(np.int32))
+    o2, l2, _ = run_gpu(d, plan=plan)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
+
+
+def test_single_key_gives_v_exactly():
+    w = wl.build("single", 37, np.array([1, 1, 1]), B=3, s_q=1, h_q=128, num_pages=6)
+    o, lse, _ = run_gpu(Dev(w))
+    og = o.view(torch.int16).cpu().numpy().view(np.uint16)
+    for b in range(3):
+        v0 = w.kv[w.block_table[b, 0], 0, 0, :512]
+        assert (og[b, 0] == v0[None, :]).all()
+    compare(w, o, lse, label="single key")
+
+
+def test_deterministic():
+    w = wl.mtp_causal()
+    d = Dev(w)
+    o1, l1, plan = run_gpu(d)
+    o2, l2, _ = run_gpu(d, plan=plan)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def test_plan_reused_across_layers():
+    # one plan, several "layers" (different q and cache, same lengths)
+    m = _m()
+    base = wl.build("layers", 38, np.array([500, 33, 1200]), B=3, s_q=1, h_q=16, num_pages=40)
+    d = Dev(base)
+    plan = m.get_mla_metadata(d.sl, 16, 1)
+    for layer in range(3):
+        w = wl.build("layers", 100 + layer, np.array([500, 33, 1200]), B=3, s_q=1, h_q=16, num_pages=40)
+        dl = Dev(w)
+        dl.sl = d.sl
+        o, lse, _ = run_gpu(dl, plan=plan)
+        compare(w, o, lse, label=f"layer {layer}")
+
+
+def test_validate_inputs():
+    m = _m()
+    w = wl.memory_bound()
+    bt, sl = i32_dev(w.block_table), i32_dev(w.cache_seqlens)
+    assert m.validate_inputs(bt, sl, w.kv.shape[0]) == 0
+    bad = w.block_table.copy()
+    bad[3, 0] = w.kv.shape[0] + 5
+    assert m.validate_inputs(i32_dev(bad), sl, w.kv.shape[0]) >= 1
+    ws = wl.sparse_topk(B=2)
+    assert m.validate_inputs(i32_dev(ws.block_table), i32_dev(ws.cache_seqlens), ws.kv.shape[0],
+                             indices=i32_dev(ws.indices)) == 0
