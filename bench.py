@@ -2,8 +2,9 @@
 """Benchmark of the paged MLA decode hot path on one MI355X.
 
 A step is one pass of the whole path over one batch: the split-KV plan
-(mla_get_metadata), the split decode kernel and the merge kernel
-(mla_decode_with_kvcache).  The default workload is the memory-bound decode:
+(mla_get_metadata), then mla_decode_with_kvcache, i.e. the split decode
+kernel and the kernel that merges the partial results of split sequences
+(launched as its two phases so that each kernel is timed on its own).  The default workload is the memory-bound decode:
 b=64, s_q=1, h_q=16, h_kv=1, d_qk=576, dv=512, lengths uniform in [1, 4096]
 (seeded), 64-token pages, shuffled block table over a 6000-page pool, bf16
 N(0, 1) data.
@@ -117,8 +118,7 @@ def run_workload(torch, m, w, steps, warmup, ncopies=NCOPIES):
     comb_ms = [e[2].elapsed_time(e[3]) for e in evs]
     return dict(ms_per_step=total_ms / steps, wall_s=wall, plan_ms=float(np.mean(plan_ms)),
                 decode_ms=float(np.mean(dec_ms)), decode_ms_med=float(np.median(dec_ms)),
-                combine_ms=float(np.mean(comb_ms)), num_workers=W,
-                o=o, lse=lse)
+                combine_ms=float(np.mean(comb_ms)), num_workers=W, o=o, lse=lse)
 
 
 def cpu_baseline(w, budget_s=10.0):
@@ -197,7 +197,7 @@ def main():
                               "combine": round(r["combine_ms"], 5)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "decode split kernel", "launch_ms": round(r["decode_ms"], 5),
+                     "kernel": "split decode kernel", "launch_ms": round(r["decode_ms"], 5),
                      "mfma_tflops": round(flops / dec_s / 1e12, 2),
                      "mfma_frac": round(flops / dec_s / 1e12 / BF16_PEAK_TFLOPS, 4)},
     }

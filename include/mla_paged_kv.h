@@ -84,6 +84,14 @@ int mla_plan_dims(int batch, int s_q, int num_q_rows, int h_kv, int topk,
                   int* out_plan_words, int* out_num_items);
 
 /*
+ * mla_plan_num_workers — host only; the W of a plan of `plan_words` words made
+ * for this call shape (inverse of mla_plan_dims), or -1 if the size does not
+ * fit the shape.
+ */
+int mla_plan_num_workers(int plan_words, int batch, int s_q, int num_q_rows, int h_kv,
+                         int topk);
+
+/*
  * mla_get_metadata — split-KV tile scheduler ("get_mla_metadata" of the
  * pages, topnet.top installation-and-use section, step 2).
  *
@@ -94,9 +102,15 @@ int mla_plan_dims(int batch, int s_q, int num_q_rows, int h_kv, int topk,
  *
  *   cache_seqlens  [batch] int32, device (read in sparse mode as well: index
  *                  entries outside [0, L_b) are padding)
+ * Rule: item i has n_i = ceil(len_i / 64) blocks and costs overhead + n_i
+ * units; items are laid end to end on a cost axis (total T); the first
+ * W' = min(W, T) workers share it evenly, worker w owning the units
+ * [floor(w T / W'), floor((w + 1) T / W')); block b of item i sits on unit
+ * (start of item i) + overhead + b, and a worker gets the blocks on its units.
+ *
  *   plan           [8 * (W + 1)] int32, device (output).  Row 0 = {W, per-run
- *                  overhead in blocks, blocks per worker P, items, version 1,
- *                  64, total cost T, 0}; row 1 + w = {first item, its first
+ *                  overhead in blocks, W', items, version 2, 64, total cost T,
+ *                  0}; row 1 + w = {first item, its first
  *                  block, last item, end block (exclusive) in the last item,
  *                  split number of the run in the first item, 0, 0, 0}, or
  *                  {-1, 0, -1, 0, 0, 0, 0, 0} for a worker with no blocks.
@@ -139,7 +153,7 @@ size_t mla_workspace_bytes(int batch, int s_q, int num_q_rows, int h_kv, int top
  *   plan, num_splits, num_workers   from mla_get_metadata with the same
  *                   lengths / batch / s_q / topk and num_q_rows = s_q*h_q/h_kv
  *   causal          0 or 1 (must be 0 in sparse mode)
- *   softmax_scale   > 0 (the pages' default for d_qk = 576 is 576^-0.5)
+ *   softmax_scale   > 0 (the Python binding defaults to d_qk^-0.5)
  *   indices, topk   NULL and 0 for dense mode
  *   workspace       device scratch of at least mla_workspace_bytes(...) bytes
  */
@@ -158,8 +172,8 @@ int mla_decode_with_kvcache(const void* q, const void* kvcache, int64_t num_page
  * kernel only (items covered by one worker get their final o / lse, the others
  * get fp32 partials in `workspace`); phases = 2 runs the merge of the partials
  * only (it must follow phase 1 on the same stream with the same arguments);
- * phases = 3 runs both and is mla_decode_with_kvcache.  Any other value returns
- * MLA_ERR_INVALID_ARGUMENT.  Same arguments, checks and ownership rules as
+ * phases = 3 runs both and is mla_decode_with_kvcache.  Any other value
+ * returns MLA_ERR_INVALID_ARGUMENT.  Same arguments, checks and ownership rules as
  * mla_decode_with_kvcache.
  */
 int mla_decode_with_kvcache_phase(const void* q, const void* kvcache, int64_t num_pages,

@@ -21,7 +21,8 @@ MLA_ERR_WORKSPACE_TOO_SMALL = 3
 MLA_ERR_HIP = 4
 
 EXPORTS = (
-    "mla_status_string", "mla_plan_dims", "mla_get_metadata", "mla_workspace_bytes",
+    "mla_status_string", "mla_plan_dims", "mla_plan_num_workers", "mla_get_metadata",
+    "mla_workspace_bytes",
     "mla_decode_with_kvcache", "mla_decode_with_kvcache_phase", "mla_debug_row_ids",
     "mla_validate_inputs",
 )
@@ -34,6 +35,7 @@ _ip = ctypes.POINTER(ctypes.c_int)
 _SIGS = {
     "mla_status_string": (ctypes.c_char_p, [_c_int]),
     "mla_plan_dims": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _ip, _ip, _ip]),
+    "mla_plan_num_workers": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
     "mla_get_metadata": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp]),
     "mla_workspace_bytes": (ctypes.c_size_t, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
     "mla_decode_with_kvcache": (_c_int, [

@@ -106,8 +106,10 @@ def mla_decode_with_kvcache(q: torch.Tensor, kvcache: torch.Tensor, block_table:
         _need(indices.dim() == 3 and tuple(indices.shape[:2]) == (B, s_q), "indices is [b, s_q, topk]")
         topk = indices.shape[2]
         _need(topk > 0, "indices needs topk > 0")
-    W = tile_scheduler_metadata.numel() // 8 - 1
-    _need(W >= 1, "tile_scheduler_metadata is too short")
+    num_q_rows = s_q * h_q // max(h_kv, 1)
+    W = int(_lib.lib().mla_plan_num_workers(tile_scheduler_metadata.numel(), B, s_q, num_q_rows,
+                                             h_kv, topk))
+    _need(W >= 1, "tile_scheduler_metadata does not match this call's shape")
     scale = d ** -0.5 if softmax_scale is None else float(softmax_scale)
     dev = q.device
     if out is None:
@@ -115,7 +117,6 @@ def mla_decode_with_kvcache(q: torch.Tensor, kvcache: torch.Tensor, block_table:
         lse = torch.empty((B, s_q, h_q), dtype=torch.float32, device=dev)
     else:
         o, lse = out
-    num_q_rows = s_q * h_q // max(h_kv, 1)
     need = workspace_bytes(B, s_q, num_q_rows, h_kv, topk, dv, W) if dv > 0 else 0
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)

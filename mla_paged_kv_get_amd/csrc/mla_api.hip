@@ -109,6 +109,13 @@ int mla_plan_dims(int batch, int s_q, int num_q_rows, int h_kv, int topk, int nu
   return MLA_OK;
 }
 
+int mla_plan_num_workers(int plan_words, int batch, int s_q, int num_q_rows, int h_kv, int topk) {
+  Shape s;
+  if (shape_of(batch, s_q, num_q_rows, h_kv, topk, &s) != MLA_OK) return -1;
+  if (plan_words < 2 * kPlanWords || plan_words % kPlanWords) return -1;
+  return plan_words / kPlanWords - 1;
+}
+
 int mla_get_metadata(const int32_t* cache_seqlens, int batch, int s_q, int num_q_rows, int h_kv,
                      int topk, int num_workers, int32_t* plan, int32_t* num_splits, void* stream) {
   if (!plan || !num_splits) return MLA_ERR_INVALID_ARGUMENT;
@@ -119,8 +126,8 @@ int mla_get_metadata(const int32_t* cache_seqlens, int batch, int s_q, int num_q
   if (st != MLA_OK) return st;
   if (s.items > mla::plan_max_items()) return MLA_ERR_UNSUPPORTED;
   const int overhead = variant_overhead(s.variant);
-  const hipError_t e = launch_plan(cache_seqlens, batch, s_q, topk > 0 ? topk : 0, s.items,
-                                   num_workers, overhead, plan, num_splits,
+  const hipError_t e = launch_plan(cache_seqlens, topk > 0 ? topk : 0, s.items, num_workers,
+                                   overhead, plan, num_splits,
                                    reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }

@@ -15,7 +15,7 @@ constexpr int kRowBytes = kDqk * 2;       // 1152 B per cached row
 constexpr int kChunks = kRowBytes / 16;   // 72 chunks of 16 B per row
 constexpr int kTileBytes = kPage * kRowBytes;  // 73728 B per 64-row tile
 constexpr int kPlanWords = 8;
-constexpr int kPlanVersion = 1;
+constexpr int kPlanVersion = 2;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -64,9 +64,8 @@ struct DecodeArgs {
 };
 
 // Launchers (defined next to their kernels).
-hipError_t launch_plan(const int32_t* seqlens, int batch, int s_q, int topk, int num_items,
-                       int num_workers, int overhead, int32_t* plan, int32_t* num_splits,
-                       hipStream_t stream);
+hipError_t launch_plan(const int32_t* seqlens, int topk, int num_items, int num_workers,
+                       int overhead, int32_t* plan, int32_t* num_splits, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int variant, hipStream_t stream);
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_row_ids(const int32_t* block_table, int max_blocks, const int32_t* seqlens,

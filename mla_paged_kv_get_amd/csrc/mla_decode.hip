@@ -8,30 +8,36 @@
 //
 // How it maps onto the chip:
 //  * A persistent grid: workgroup = (worker, row tile).  A worker walks the
-//    runs of 64-key tiles the scheduler gave it (see mla_plan.hip).
+//    runs of 64-key tiles the scheduler gave it (see mla_plan.hip) as one flat
+//    stream of tiles that crosses item boundaries, so the first tile of the
+//    next item is already on its way while the current item is finished.
 //  * Every 64-row tile (73,728 B) is copied HBM -> LDS with
 //    global_load_lds_dwordx4: one instruction moves 8 rows x 128 B, so each
 //    wave instruction reads whole 128-byte lines.  Rows are placed in LDS in
 //    8-row x 128-B blocks with an XOR swizzle of the 16-byte chunks, which
 //    spreads both the row-fragment reads of QK^T and the transposed reads of
-//    PV over the LDS banks.  Two tiles are in flight (double buffer in two
-//    distinct LDS arrays, so the compiler does not serialise the copy into one
-//    with the reads of the other).
+//    PV over the LDS banks.  Two stages live in two distinct LDS arrays, so
+//    the compiler does not serialise the copy into one with the reads of the
+//    other.
 //  * S^T = K Q^T with v_mfma_f32_16x16x32_bf16: A = 16 key rows read from LDS,
-//    B = 16 query rows held in registers for the whole run (Q is loaded once
-//    per run).  The accumulator gives every lane 4 keys of one query row.
-//  * Online softmax in base 2 (scores pre-multiplied by scale*log2(e)); the
-//    row max is reduced over the 4 lanes holding a row with two xor-shuffles;
-//    row sums stay per lane until the end.
+//    B = 16 query rows held in registers (Q of the next item is fetched as soon
+//    as the last QK^T of the current item has been issued).
+//  * Online softmax in base 2 (scores pre-multiplied by scale*log2(e)).  The
+//    running reference of a row only moves when the row max exceeds it by more
+//    than 8 (a factor 2^8), so the O accumulators are rescaled a few times per
+//    run instead of every tile; numerator and denominator share the reference,
+//    so the result is the same.
 //  * O^T += V^T P^T with the same MFMA: P^T comes straight from the S^T
 //    accumulators (the key order inside the contraction is permuted to match),
-//    V^T fragments come from LDS through ds_read_b64_tr_b16 (a transposing
-//    read: 16 lanes read 4 rows x 16 values and each lane receives one column).
+//    V^T fragments come from LDS through ds_read_b64_tr_b16.
 //  * Keys past a sequence's length inside its last page, and sparse padding
 //    entries, are loaded from a valid row of the same sequence and masked to
 //    -inf, so no value outside the key set (e.g. NaN garbage) is ever read.
-//  * Runs covering a whole item write bf16 O and fp32 LSE directly; other
-//    runs write fp32 partials that the combine kernel merges (log-sum-exp).
+//  * Runs covering a whole item write bf16 O and fp32 LSE directly; other runs
+//    write fp32 partials that combine_kernel merges (log-sum-exp).  (Merging
+//    inside this kernel, by the last run of an item to finish, needs a
+//    device-scope release/acquire per run; on MI355X that writes back and
+//    invalidates the XCD's L2 and cost several times the decode itself.)
 #include "mla_common.h"
 
 #include <math.h>
@@ -40,14 +46,18 @@ namespace mla {
 namespace {
 
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLazy = 8.f;   // log2 of the growth allowed before a rescale
 
 // XOR pattern of tile row t (bijection on t & 7).
 __device__ __forceinline__ int swz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
 
-// LDS byte offset of 16-byte chunk c (0..71) of tile row t (0..63): 8-row x
-// 128-byte blocks of 1 KB, block (t / 8, c / 8) at index (t / 8) * 9 + c / 8.
-__device__ __forceinline__ int lds_off(int t, int c) {
-  return (((t >> 3) * 9 + (c >> 3)) << 10) + ((t & 7) << 7) + (((c & 7) ^ swz(t)) << 4);
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane i
+// receives element i % 4 of the 8-byte words addressed by lanes 4 e + i / 4,
+// e = 0..3, i.e. one column of the 4 x 16 block the group points at.
+__device__ __forceinline__ bf16x4 read_tr(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(p));
 }
 
 template <int NR, int NT>
@@ -62,30 +72,86 @@ struct Cfg {
   static_assert(72 % kWaves == 0 && kLoads % 9 == 0, "tile copy must split evenly");
 };
 
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// s_waitcnt operand (gfx9 layout: vmcnt in bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8) that waits until at most n vector-memory operations of the
+// wave are outstanding and does not wait on the other counters.
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kWaitLds = (15) | (3 << 14) | (7 << 4);   // lgkmcnt(0) only
 
-// Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane i
-// receives element i % 4 of the 8-byte words addressed by lanes 4 e + i / 4,
-// e = 0..3, i.e. one column of the 4 x 16 block the group points at.
-__device__ __forceinline__ bf16x4 read_tr(const char* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(p));
+// Wave-uniform read of one int through the scalar data cache (the tables read
+// this way are never written by these kernels).  It is counted by lgkmcnt, so
+// waiting for it never waits for the tile copies in flight.
+__device__ __forceinline__ int read_scalar(const int32_t* p) {
+  int v;
+  asm volatile("s_load_dword %0, %1, 0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return v;
 }
 
-// Per-run state of one wave.
-template <int KSUB>
-struct WaveState {
-  bf16x8 qf[18];        // B operand of S^T: Q[row][32 ks + 8 g .. + 7]
-  floatx4 oacc[32];     // O^T[16 dt + 4 g + i][row]
-  float m_run;          // running max (base-2 scaled units)
-  float l_lane;         // running sum over this lane's keys
-};
+// Workgroup barrier that does not wait for the wave's outstanding global
+// loads (the copies into the other LDS stage stay in flight across it).  The
+// caller has already waited for whatever the barrier must publish; the LDS
+// accesses of this wave are completed first, and the memory clobber keeps the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void barrier_keep_loads() {
+  __builtin_amdgcn_s_waitcnt(kWaitLds);
+  asm volatile("s_barrier" ::: "memory");
+}
+
+// o = 0, lse = -inf for rows [r0, r0 + nr) of an item with no key.
+__device__ void write_empty(const DecodeArgs& a, int item, int r0, int nr, int tid, int nthreads) {
+  for (int e = tid; e < nr * 64; e += nthreads) {
+    const int64_t orow = (int64_t)item * a.M + r0 + e / 64;
+    *reinterpret_cast<uint4*>(a.o + orow * kDv + (e & 63) * 8) = uint4{0, 0, 0, 0};
+    if ((e & 63) == 0) a.lse[orow] = -INFINITY;
+  }
+}
+
+// Log-sum-exp merge of the n partials of rows [r0, r0 + nr) of an item.
+__device__ void merge_rows(const DecodeArgs& a, int item, int slot0, int n, int r0, int nr, int tid,
+                           int nthreads) {
+  for (int e = tid; e < nr * 64; e += nthreads) {
+    const int r = r0 + e / 64;
+    const int c8 = (e & 63) * 8;
+    const int64_t orow = (int64_t)item * a.M + r;
+    float mx = -INFINITY;
+    for (int k = 0; k < n; ++k) mx = fmaxf(mx, a.part_lse[(int64_t)(slot0 + k) * a.M + r]);
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    float tot = 0.f;
+    if (mx != -INFINITY) {
+      for (int k = 0; k < n; ++k) {
+        const int64_t prow = (int64_t)(slot0 + k) * a.M + r;
+        const float lk = a.part_lse[prow];
+        const float wk = lk == -INFINITY ? 0.f : expf(lk - mx);
+        tot += wk;
+        const floatx4* src = reinterpret_cast<const floatx4*>(a.part_o + prow * kDv + c8);
+        const floatx4 v0 = src[0], v1 = src[1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[i] += wk * v0[i];
+          acc[4 + i] += wk * v1[i];
+        }
+      }
+    }
+    const float inv = tot > 0.f ? 1.f / tot : 0.f;
+    bf16x8 v;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (__bf16)(acc[i] * inv);
+    *reinterpret_cast<bf16x8*>(a.o + orow * kDv + c8) = v;
+    if ((e & 63) == 0) a.lse[orow] = tot > 0.f ? mx + logf(tot) : -INFINITY;
+  }
+}
 
 template <int NR, int NT>
 __global__ __launch_bounds__(64 * NR * NT, 1) void decode_kernel(DecodeArgs a) {
   using C = Cfg<NR, NT>;
+  static_assert(NT == 1 || NT == 4, "key split of a tile: 1 or 4 waves");
+  constexpr int kWaitAllButCopy = waitcnt_vm(C::kLoads);
+  static_assert(C::kLoads < 64, "vmcnt holds 6 bits");
   __shared__ __attribute__((aligned(1024))) char s0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char s1[kTileBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char kvalid[2][64];   // sparse key validity per stage
+  __shared__ __attribute__((aligned(16))) unsigned char kvalid[4][64];   // sparse key validity, tile t -> t & 3
   __shared__ float red_m[NT][C::kRows];
   __shared__ float red_l[NT][C::kRows];
 
@@ -105,87 +171,112 @@ __global__ __launch_bounds__(64 * NR * NT, 1) void decode_kernel(DecodeArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int g = lane >> 4;      // lane group (k slice of MFMA operands)
   const int li = lane & 15;     // row (query row / key row) inside a 16-block
   const int rg = wave % NR;     // row group of this wave
   const int tg = wave / NR;     // key group of this wave
-  const int row = mt * C::kRows + rg * 16 + li;   // query row inside the item (S^T column)
+  const int row0 = mt * C::kRows;
+  const int row = row0 + rg * 16 + li;   // query row inside the item (S^T column)
   const bool row_ok = row < a.M;
+  const bool sparse = a.topk > 0;
 
   const int32_t* prow = a.plan + kPlanWords * (1 + w);
   const int it_first = prow[0], blk_first = prow[1], it_last = prow[2], blk_end = prow[3],
             split_first = prow[4];
-  if (it_first < 0) return;
 
-  // LDS read offsets of this lane (see lds_off).
-  //  K row fragments: key row t = tg*kTpw + li (+16 u), chunk 4 ks + g.
-  const int tk = tg * C::kTpw + li;
-  const int k_base = ((tk >> 3) * 9 << 10) + ((tk & 7) << 7);
-  const int k_x0 = ((g ^ swz(tk)) << 4);            // even ks: chunk & 7 == g
-  const int k_x1 = (((4 + g) ^ swz(tk)) << 4);      // odd ks:  chunk & 7 == 4 + g
-  //  V^T transposed reads: source row t = tg*kTpw + 4 g + li / 4 (+16 u),
-  //  columns 16 dt + 4 (li & 3) .. + 3, i.e. chunk 2 dt + (li & 3) / 2, half li & 1.
-  const int tv = tg * C::kTpw + 4 * g + (li >> 2);
-  const int v_base = ((tv >> 3) * 9 << 10) + ((tv & 7) << 7) + ((li & 1) << 3);
-  int v_x[4];
+  if (it_first >= 0) {
+    // LDS read offsets of this lane (byte offset of chunk c of tile row t:
+    // ((t / 8) * 9 + c / 8) * 1024 + (t % 8) * 128 + ((c % 8) ^ swz(t)) * 16).
+    //  K row fragments: key row t = tg*kTpw + li (+16 u), chunk 4 ks + g.
+    const int tk = tg * C::kTpw + li;
+    const int k_base = ((tk >> 3) * 9 << 10) + ((tk & 7) << 7);
+    const int k_x0 = ((g ^ swz(tk)) << 4);            // even ks: chunk & 7 == g
+    const int k_x1 = (((4 + g) ^ swz(tk)) << 4);      // odd ks:  chunk & 7 == 4 + g
+    //  V^T transposed reads: source row t = tg*kTpw + 4 g + li / 4 (+16 u),
+    //  columns 16 dt + 4 (li & 3) .. + 3, i.e. chunk 2 dt + (li & 3) / 2, half li & 1.
+    const int tv = tg * C::kTpw + 4 * g + (li >> 2);
+    const int v_base = ((tv >> 3) * 9 << 10) + ((tv & 7) << 7) + ((li & 1) << 3);
+    int v_x[4];
 #pragma unroll
-  for (int d = 0; d < 4; ++d) v_x[d] = (((2 * d + ((li & 3) >> 1)) ^ swz(tv)) << 4);
+    for (int d = 0; d < 4; ++d) v_x[d] = (((2 * d + ((li & 3) >> 1)) ^ swz(tv)) << 4);
 
-  // Tile rows this lane copies: t = 8 * (wave * kLoads / 9 + r) + lane / 8.
-  int cp_row[C::kLaneRows];
-  int cp_swz[C::kLaneRows];
+    // Tile rows this lane copies: t = 8 * (wave * kLoads / 9 + r) + lane / 8.
+    int cp_row[C::kLaneRows];
+    int cp_swz[C::kLaneRows];
 #pragma unroll
-  for (int r = 0; r < C::kLaneRows; ++r) {
-    cp_row[r] = 8 * (wave * C::kLoads / 9 + r) + (lane >> 3);
-    cp_swz[r] = swz(cp_row[r]);
-  }
-
-  const char* kv_bytes = reinterpret_cast<const char*>(a.kv);
-
-  for (int item = it_first; item <= it_last; ++item) {
-    const bool sparse = a.topk > 0;
-    const int b = sparse ? item / a.s_q : item;
-    const int L = a.seqlens[b];
-    const int len = sparse ? a.topk : L;
-    const int nblk = len > 0 ? (len + kPage - 1) / kPage : 0;
-    const int lo = item == it_first ? blk_first : 0;
-    const int hi = item == it_last ? blk_end : nblk;
-    if (lo >= hi) continue;
-    const int split = item == it_first ? split_first : 0;
-    const int slot0 = a.num_splits[item];
-    const int nsplit = a.num_splits[item + 1] - slot0;
-    const int32_t* bt_row = a.block_table + (int64_t)b * a.max_blocks;
-    const int32_t* idx_row = sparse ? a.indices + (int64_t)item * a.topk : nullptr;
-    const bool load = !sparse || L > 0;   // a sparse item of an empty sequence has no keys
-
-    // Key limit of this lane's query row (dense); sparse validity comes from LDS.
-    int lim = 0;
-    if (row_ok) {
-      lim = L;
-      if (!sparse && a.causal) lim = L - a.s_q + row / a.h_q + 1;
+    for (int r = 0; r < C::kLaneRows; ++r) {
+      cp_row[r] = 8 * (wave * C::kLoads / 9 + r) + (lane >> 3);
+      cp_swz[r] = swz(cp_row[r]);
     }
+    const char* kv_bytes = reinterpret_cast<const char*>(a.kv);
 
-    // Query fragments of this wave's 16 rows.
-    WaveState<C::kSub> st;
-    {
-      const uint16_t* qrow = a.q + ((int64_t)item * a.M + (row_ok ? row : 0)) * kDqk + 8 * g;
-#pragma unroll
-      for (int ks = 0; ks < 18; ++ks) {
-        bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
-        if (!row_ok) v = bf16x8{};
-        st.qf[ks] = v;
+    // Sequence length of each of this worker's items, lane j holding item
+    // it_first + j, read once here: a vector load issued after a tile's copy
+    // would make its wait cover the copy too.
+    int lens_v = 0;
+    if (lane <= it_last - it_first) {
+      const int x = it_first + lane;
+      lens_v = a.seqlens[sparse ? x / a.s_q : x];
+    }
+    auto item_len = [&](int x) __attribute__((always_inline)) -> int {      // x is wave-uniform
+      const int j = x - it_first;
+      if (j < 64) return __builtin_amdgcn_readlane(lens_v, j);
+      return read_scalar(a.seqlens + (sparse ? x / a.s_q : x));
+    };
+    auto seg_hi = [&](int x) __attribute__((always_inline)) -> int {         // end block of this worker's run in item x
+      if (x == it_last) return blk_end;
+      const int len = sparse ? a.topk : item_len(x);
+      return len > 0 ? (len + kPage - 1) / kPage : 0;
+    };
+    // Tile after (item, blk) in this worker's runs (hi = end block of the run
+    // in `item`); ni = -1 at the end.
+    auto advance = [&](int item, int blk, int hi, int& ni, int& nb, int& nhi) __attribute__((always_inline)) {
+      if (blk + 1 < hi) {
+        ni = item;
+        nb = blk + 1;
+        nhi = hi;
+        return;
       }
-    }
-#pragma unroll
-    for (int d = 0; d < 32; ++d) st.oacc[d] = floatx4{0.f, 0.f, 0.f, 0.f};
-    st.m_run = -INFINITY;
-    st.l_lane = 0.f;
+      for (int x = item + 1; x <= it_last; ++x) {
+        const int h = seg_hi(x);
+        if (h > 0) {
+          ni = x;
+          nb = 0;
+          nhi = h;
+          return;
+        }
+      }
+      ni = -1;
+      nb = 0;
+      nhi = 0;
+    };
 
-    // Byte offsets of the rows this lane copies for tile `blk`.
-    auto tile_rows = [&](int blk, int64_t (&off)[C::kLaneRows], unsigned char* vstage) {
+    // Copy addresses of a tile are found in two steps so that the index loads
+    // can be issued a whole tile ahead: tile_fetch loads the raw index data
+    // (dense: the tile's page id; sparse: this lane's index-list entries),
+    // tile_finish turns it into byte offsets (in the cache) of the rows this
+    // lane copies, and the sparse key validity of the tile.
+    struct TileRaw {
+      int v[C::kLaneRows];
+    };
+    auto tile_fetch = [&](int item, int blk, TileRaw& raw) __attribute__((always_inline)) {
       if (!sparse) {
-        const int64_t page = bt_row[blk];
+        raw.v[0] = a.block_table[(int64_t)item * a.max_blocks + blk];
+      } else {
+        const int32_t* idx_row = a.indices + (int64_t)item * a.topk;
+#pragma unroll
+        for (int r = 0; r < C::kLaneRows; ++r) {
+          const int sl = blk * kPage + cp_row[r];
+          raw.v[r] = sl < a.topk ? idx_row[sl] : -1;
+        }
+      }
+    };
+    auto tile_finish = [&](int item, int blk, const TileRaw& raw, int64_t (&off)[C::kLaneRows],
+                           unsigned char* vslot) __attribute__((always_inline)) {
+      const int L = item_len(item);
+      if (!sparse) {
+        const int64_t page = raw.v[0];
         const int nvalid = min(kPage, L - blk * kPage);
 #pragma unroll
         for (int r = 0; r < C::kLaneRows; ++r) {
@@ -193,13 +284,15 @@ __global__ __launch_bounds__(64 * NR * NT, 1) void decode_kernel(DecodeArgs a) {
           off[r] = (page * kPage + t) * (int64_t)kRowBytes;
         }
       } else {
+        const int32_t* bt_row = a.block_table + (int64_t)(item / a.s_q) * a.max_blocks;
 #pragma unroll
         for (int r = 0; r < C::kLaneRows; ++r) {
-          const int sl = blk * kPage + cp_row[r];
-          const int idx = sl < a.topk ? idx_row[sl] : -1;
+          const int idx = raw.v[r];
           const bool ok = sparse_key_valid(idx, L);
-          off[r] = cache_row(bt_row, ok ? idx : 0) * (int64_t)kRowBytes;
-          if ((lane & 7) == 0) vstage[cp_row[r]] = ok ? 1 : 0;
+          // padding reads the sequence's first row (page 0 of the pool if it has none)
+          off[r] = ok ? cache_row(bt_row, idx) * (int64_t)kRowBytes
+                      : (L > 0 ? cache_row(bt_row, 0) * (int64_t)kRowBytes : 0);
+          if ((lane & 7) == 0) vslot[cp_row[r]] = ok ? 1 : 0;
         }
       }
     };
@@ -213,28 +306,67 @@ __global__ __launch_bounds__(64 * NR * NT, 1) void decode_kernel(DecodeArgs a) {
       }
     };
 
+    // Per-run state of this wave.
+    bf16x8 qf[18];        // B operand of S^T: Q[row][32 ks + 8 g .. + 7]
+    floatx4 oacc[32];     // O^T[16 dt + 4 g + i][row], scaled by 2^-m_ref
+    float m_ref = -INFINITY;
+    float l_lane = 0.f;   // sum over this lane's keys of 2^(x - m_ref)
+
+    // Rows past M borrow row 0's values (their scores are masked to -inf), so
+    // no select on the loaded data forces an early wait on the loads.
+    auto load_q = [&](int item) __attribute__((always_inline)) {
+      const uint16_t* qrow = a.q + ((int64_t)item * a.M + (row_ok ? row : 0)) * kDqk + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < 18; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
+    };
+    auto key_limit = [&](int item) __attribute__((always_inline)) -> int {   // dense: keys of this lane's row are < limit
+      const int L = item_len(item);
+      if (!row_ok) return 0;
+      return (!sparse && a.causal) ? L - a.s_q + row / a.h_q + 1 : L;
+    };
+
     // Consume one tile held in `stage` (keys blk*64 .. blk*64 + 63 of the item).
-    auto compute = [&](const char* stage, const unsigned char* vstage, int blk) {
+    // If next_q >= 0, the query rows of item next_q are fetched once the
+    // tile's QK^T no longer needs the current ones.
+    auto compute = [&](const char* stage, const unsigned char* vslot, int blk, int lim, int next_q) __attribute__((always_inline)) {
       floatx4 sacc[C::kSub];
 #pragma unroll
       for (int u = 0; u < C::kSub; ++u) sacc[u] = floatx4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (C::kSub == 1) {
+        // all 18 K fragments first: one LDS latency for the whole chain
+        bf16x8 kf[18];
 #pragma unroll
-      for (int ks = 0; ks < 18; ++ks) {
+        for (int ks = 0; ks < 18; ++ks)
+          kf[ks] = *reinterpret_cast<const bf16x8*>(stage + k_base + ((ks >> 1) << 10) + ((ks & 1) ? k_x1 : k_x0));
 #pragma unroll
-        for (int u = 0; u < C::kSub; ++u) {
-          const int off = k_base + u * (2 * 9 * 1024) + ((ks >> 1) << 10) + ((ks & 1) ? k_x1 : k_x0);
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(stage + off);
-          sacc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, st.qf[ks], sacc[u], 0, 0, 0);
+        for (int ks = 0; ks < 18; ++ks) sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[ks], sacc[0], 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < 18; ++ks) {
+#pragma unroll
+          for (int u = 0; u < C::kSub; ++u) {
+            const int off = k_base + u * (2 * 9 * 1024) + ((ks >> 1) << 10) + ((ks & 1) ? k_x1 : k_x0);
+            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(stage + off);
+            sacc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], sacc[u], 0, 0, 0);
+          }
         }
       }
-      // Scale, mask, running max.
+      if (next_q >= 0) load_q(next_q);
+      // V^T fragments of the one-subtile case are read before the softmax so
+      // that their latency hides behind it.
+      bf16x4 vf[C::kSub == 1 ? 32 : 1];
+      if constexpr (C::kSub == 1) {
+#pragma unroll
+        for (int dt = 0; dt < 32; ++dt) vf[dt] = read_tr(stage + v_base + ((dt >> 2) << 10) + v_x[dt & 3]);
+      }
+      // Scale, mask, row max.
       float x[C::kSub][4];
       float mx = -INFINITY;
 #pragma unroll
       for (int u = 0; u < C::kSub; ++u) {
         const int t0 = tg * C::kTpw + 16 * u + 4 * g;       // tile row of element i = 0
         unsigned vb = 0;
-        if (sparse) vb = *reinterpret_cast<const unsigned*>(vstage + t0);
+        if (sparse) vb = *reinterpret_cast<const unsigned*>(vslot + t0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           bool ok;
@@ -246,22 +378,24 @@ __global__ __launch_bounds__(64 * NR * NT, 1) void decode_kernel(DecodeArgs a) {
       }
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(st.m_run, mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2(st.m_run - m_use);
-      float psum = 0.f;
+      // Move the reference (and rescale) only when some row outgrew it by 2^8.
+      if (__builtin_amdgcn_ballot_w64(mx > m_ref + kLazy)) {
+        const float m_new = fmaxf(m_ref, mx);
+        const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_ref - m_new);
+        l_lane *= alpha;
+#pragma unroll
+        for (int d = 0; d < 32; ++d) oacc[d] *= alpha;
+        m_ref = m_new;
+      }
+      const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
       float p[C::kSub][4];
 #pragma unroll
       for (int u = 0; u < C::kSub; ++u)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           p[u][i] = fast_exp2(x[u][i] - m_use);
-          psum += p[u][i];
+          l_lane += p[u][i];
         }
-      st.l_lane = st.l_lane * alpha + psum;
-      st.m_run = m_new;
-#pragma unroll
-      for (int d = 0; d < 32; ++d) st.oacc[d] *= alpha;
 
       // O^T += V^T P^T.
       if constexpr (C::kSub == 1) {
@@ -271,14 +405,11 @@ __global__ __launch_bounds__(64 * NR * NT, 1) void decode_kernel(DecodeArgs a) {
           pb[i] = (__bf16)p[0][i];
           pb[4 + i] = (__bf16)0.f;
         }
-        const char* vrow = stage + v_base;
         const bf16x4 zero4 = {};
 #pragma unroll
         for (int dt = 0; dt < 32; ++dt) {
-          const int off = ((dt >> 2) << 10) + v_x[dt & 3];
-          const bf16x4 v0 = read_tr(vrow + off);
-          const bf16x8 va = __builtin_shufflevector(v0, zero4, 0, 1, 2, 3, 4, 5, 6, 7);
-          st.oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, st.oacc[dt], 0, 0, 0);
+          const bf16x8 va = __builtin_shufflevector(vf[dt], zero4, 0, 1, 2, 3, 4, 5, 6, 7);
+          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, oacc[dt], 0, 0, 0);
         }
       } else {
 #pragma unroll
@@ -297,190 +428,219 @@ __global__ __launch_bounds__(64 * NR * NT, 1) void decode_kernel(DecodeArgs a) {
             const bf16x4 v0 = read_tr(vrow0 + off);
             const bf16x4 v1 = read_tr(vrow1 + off);
             const bf16x8 va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-            st.oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, st.oacc[dt], 0, 0, 0);
+            oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, oacc[dt], 0, 0, 0);
           }
         }
       }
     };
 
-    // Double-buffered walk over tiles lo .. hi - 1.
-    if (load) {
-      int64_t off[C::kLaneRows];
-      tile_rows(lo, off, kvalid[0]);
+    // Finish the run of `item` (its last tile was computed from `stage`, which
+    // is free once every wave is past the barrier below): write O/LSE or the
+    // fp32 partial.
+    auto finish = [&](int item, int split, char* stage) __attribute__((always_inline)) {
+      const int slot0 = read_scalar(a.num_splits + item);
+      const int nsplit = read_scalar(a.num_splits + item + 1) - slot0;
+      const bool final_out = nsplit == 1;
+      const int64_t orow_base = final_out ? (int64_t)item * a.M : (int64_t)(slot0 + split) * a.M;
+      float l_tot = l_lane;
+      l_tot += __shfl_xor(l_tot, 16, 64);
+      l_tot += __shfl_xor(l_tot, 32, 64);
+
+      if constexpr (NT == 1) {
+        if (row_ok) {
+          const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+          const int64_t orow = orow_base + row;
+          if (final_out) {
+            uint16_t* orp = a.o + orow * kDv + 4 * g;
+#pragma unroll
+            for (int dt = 0; dt < 32; ++dt) {
+              bf16x4 v;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) v[i] = (__bf16)(oacc[dt][i] * inv);
+              *reinterpret_cast<bf16x4*>(orp + 16 * dt) = v;
+            }
+          } else {
+            float* orp = a.part_o + orow * kDv + 4 * g;
+#pragma unroll
+            for (int dt = 0; dt < 32; ++dt) *reinterpret_cast<floatx4*>(orp + 16 * dt) = oacc[dt] * inv;
+          }
+          if (g == 0) {
+            const float lse = l_tot > 0.f ? m_ref * kLn2 + logf(l_tot) : -INFINITY;
+            if (final_out) a.lse[orow] = lse; else a.part_lse[orow] = lse;
+          }
+        }
+      } else {
+        // Merge the 4 key groups of each row through the free stage.
+        barrier_keep_loads();                               // stage and red_* are free
+        if (g == 0) {
+          red_m[tg][rg * 16 + li] = m_ref;
+          red_l[tg][rg * 16 + li] = l_tot;
+        }
+        barrier_keep_loads();
+        float m_all = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) m_all = fmaxf(m_all, red_m[j][rg * 16 + li]);
+        float l_all = 0.f;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          const float mj = red_m[j][rg * 16 + li];
+          l_all += mj == -INFINITY ? 0.f : red_l[j][rg * 16 + li] * fast_exp2(mj - m_all);
+        }
+        const float f = m_ref == -INFINITY ? 0.f : fast_exp2(m_ref - m_all);
+        const float sc = f * (l_all > 0.f ? 1.f / l_all : 0.f);
+#pragma unroll
+        for (int d = 0; d < 32; ++d) oacc[d] *= sc;
+        // Region j = [16 rows][516] fp32 (row stride padded against bank conflicts).
+        constexpr int kStride = 516;
+        constexpr int kRegion = 16 * kStride * 4;
+        static_assert(2 * kRegion <= kTileBytes, "merge regions must fit a stage");
+        float* reg0 = reinterpret_cast<float*>(stage);
+        float* reg1 = reinterpret_cast<float*>(stage + kRegion);
+        const int eo = li * kStride + 4 * g;                // this lane's element offset (dt = 0)
+        // Round 1: key groups 2, 3 hand their sums to groups 0, 1.
+        if (tg >= 2) {
+          float* dst = tg == 2 ? reg0 : reg1;
+#pragma unroll
+          for (int dt = 0; dt < 32; ++dt) *reinterpret_cast<floatx4*>(dst + eo + 16 * dt) = oacc[dt];
+        }
+        barrier_keep_loads();
+        if (tg < 2) {
+          const float* src = tg == 0 ? reg0 : reg1;
+#pragma unroll
+          for (int dt = 0; dt < 32; ++dt) oacc[dt] += *reinterpret_cast<const floatx4*>(src + eo + 16 * dt);
+        }
+        // Round 2: group 1 hands its sum to group 0, which writes the result.
+        if (tg == 1) {
+#pragma unroll
+          for (int dt = 0; dt < 32; ++dt) *reinterpret_cast<floatx4*>(reg1 + eo + 16 * dt) = oacc[dt];
+        }
+        barrier_keep_loads();
+        if (tg == 0) {
+#pragma unroll
+          for (int dt = 0; dt < 32; ++dt) oacc[dt] += *reinterpret_cast<const floatx4*>(reg1 + eo + 16 * dt);
+          if (row_ok) {
+            const int64_t orow = orow_base + row;
+            if (final_out) {
+              uint16_t* orp = a.o + orow * kDv + 4 * g;
+#pragma unroll
+              for (int dt = 0; dt < 32; ++dt) {
+                bf16x4 v;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[i] = (__bf16)oacc[dt][i];
+                *reinterpret_cast<bf16x4*>(orp + 16 * dt) = v;
+              }
+            } else {
+              float* orp = a.part_o + orow * kDv + 4 * g;
+#pragma unroll
+              for (int dt = 0; dt < 32; ++dt) *reinterpret_cast<floatx4*>(orp + 16 * dt) = oacc[dt];
+            }
+            if (g == 0) {
+              const float lse = l_all > 0.f ? m_all * kLn2 + logf(l_all) : -INFINITY;
+              if (final_out) a.lse[orow] = lse; else a.part_lse[orow] = lse;
+            }
+          }
+        }
+      }
+
+      // reset for the next run
+#pragma unroll
+      for (int d = 0; d < 32; ++d) oacc[d] = floatx4{0.f, 0.f, 0.f, 0.f};
+      m_ref = -INFINITY;
+      l_lane = 0.f;
+    };
+
+    // ---- the tile stream ----
+    int cur_item = it_first, cur_blk = blk_first, cur_hi = seg_hi(it_first);
+    int nx_item, nx_blk, nx_hi;
+    advance(cur_item, cur_blk, cur_hi, nx_item, nx_blk, nx_hi);
+    int cur_lim = key_limit(cur_item);
+    int cur_split = split_first;
+    int t = 0;   // tile counter (validity slot t & 3)
+    int64_t off[C::kLaneRows];
+    load_q(cur_item);
+#pragma unroll
+    for (int d = 0; d < 32; ++d) oacc[d] = floatx4{0.f, 0.f, 0.f, 0.f};
+    {
+      TileRaw raw;
+      tile_fetch(cur_item, cur_blk, raw);
+      tile_finish(cur_item, cur_blk, raw, off, kvalid[0]);
       issue(s0, off);
-      for (int blk = lo; blk < hi; blk += 2) {
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (blk + 1 < hi) {
-          tile_rows(blk + 1, off, kvalid[1]);
-          issue(s1, off);
-        }
-        compute(s0, kvalid[0], blk);
-        if (blk + 1 >= hi) break;
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (blk + 2 < hi) {
-          tile_rows(blk + 2, off, kvalid[0]);
-          issue(s0, off);
-        }
-        compute(s1, kvalid[1], blk + 1);
+      if (nx_item >= 0) {
+        tile_fetch(nx_item, nx_blk, raw);
+        tile_finish(nx_item, nx_blk, raw, off, kvalid[1]);
       }
     }
-    __syncthreads();   // every wave is done with the stages
 
-    // Row sums over the 4 lanes of a row.
-    float l_tot = st.l_lane;
-    l_tot += __shfl_xor(l_tot, 16, 64);
-    l_tot += __shfl_xor(l_tot, 32, 64);
-    float m_fin = st.m_run;
-
-    const bool final_out = nsplit == 1;
-    const int64_t orow_base = final_out ? (int64_t)item * a.M : (int64_t)(slot0 + split) * a.M;
-
-    if constexpr (NT == 1) {
-      if (row_ok) {
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        const int64_t orow = orow_base + row;
-        if (final_out) {
-          uint16_t* orp = a.o + orow * kDv + 4 * g;
-#pragma unroll
-          for (int dt = 0; dt < 32; ++dt) {
-            bf16x4 v;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = (__bf16)(st.oacc[dt][i] * inv);
-            *reinterpret_cast<bf16x4*>(orp + 16 * dt) = v;
-          }
-        } else {
-          float* orp = a.part_o + orow * kDv + 4 * g;
-#pragma unroll
-          for (int dt = 0; dt < 32; ++dt) *reinterpret_cast<floatx4*>(orp + 16 * dt) = st.oacc[dt] * inv;
-        }
-        if (g == 0) {
-          const float lse = l_tot > 0.f ? m_fin * kLn2 + logf(l_tot) : -INFINITY;
-          if (final_out) a.lse[orow] = lse; else a.part_lse[orow] = lse;
+    // One step: tile t sits in `cur`; tile t + 1 goes into `nxt`.  Tile t + 1
+    // is requested before waiting for tile t, so two tiles are in flight while
+    // a wave waits; the wait below counts only this wave's copy of tile t + 1
+    // as still outstanding (memory loads complete in order).
+    auto step = [&](char* cur, char* nxt) __attribute__((always_inline)) -> bool {
+      const bool has_next = nx_item >= 0;
+      int n2_item = -1, n2_blk = 0, n2_hi = 0;
+      if (has_next) advance(nx_item, nx_blk, nx_hi, n2_item, n2_blk, n2_hi);
+      barrier_keep_loads();                              // every wave is done with `nxt`
+      TileRaw raw;
+      if (n2_item >= 0) tile_fetch(n2_item, n2_blk, raw);  // index data of tile t + 2
+      if (has_next) {
+        issue(nxt, off);
+        __builtin_amdgcn_s_waitcnt(kWaitAllButCopy);     // all but tile t + 1's copy
+      } else {
+        __builtin_amdgcn_s_waitcnt(0);
+      }
+      barrier_keep_loads();                              // tile t is in LDS for every wave
+      if (n2_item >= 0) tile_finish(n2_item, n2_blk, raw, off, kvalid[(t + 2) & 3]);
+      const bool ends = !has_next || nx_item != cur_item;
+      compute(cur, kvalid[t & 3], cur_blk, cur_lim, ends && has_next ? nx_item : -1);
+      if (ends) {
+        finish(cur_item, cur_split, cur);
+        if (has_next) {
+          cur_lim = key_limit(nx_item);
+          cur_split = 0;
         }
       }
-    } else {
-      // Merge the NT key groups of each row through LDS.
-      if (g == 0) {
-        red_m[tg][rg * 16 + li] = m_fin;
-        red_l[tg][rg * 16 + li] = l_tot;
-      }
-      __syncthreads();
-      float m_all = -INFINITY;
-#pragma unroll
-      for (int j = 0; j < NT; ++j) m_all = fmaxf(m_all, red_m[j][rg * 16 + li]);
-      float l_all = 0.f;
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        const float mj = red_m[j][rg * 16 + li];
-        l_all += mj == -INFINITY ? 0.f : red_l[j][rg * 16 + li] * fast_exp2(mj - m_all);
-      }
-      const float f = m_fin == -INFINITY ? 0.f : fast_exp2(m_fin - m_all);
-      const float inv = l_all > 0.f ? 1.f / l_all : 0.f;
-      // Each wave parks its scaled accumulator: region [tg] = [16 rows][516] fp32.
-      constexpr int kStride = 516;
-      constexpr int kRegion = 16 * kStride * 4;
-      static_assert(2 * kRegion <= kTileBytes, "merge regions must fit the stages");
-      char* region = (tg < 2 ? s0 : s1) + (tg & 1) * kRegion;
-      float* myreg = reinterpret_cast<float*>(region) + li * kStride + 4 * g;
-#pragma unroll
-      for (int dt = 0; dt < 32; ++dt) *reinterpret_cast<floatx4*>(myreg + 16 * dt) = st.oacc[dt] * (f * inv);
-      __syncthreads();
-      // Wave tg sums columns [128 tg, 128 tg + 128): lane -> row lane / 4, 32 columns.
-      const int orow_l = lane >> 2;
-      const int col0 = 128 * tg + 32 * (lane & 3);
-      floatx4 acc[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        const float* rj = reinterpret_cast<const float*>((j < 2 ? s0 : s1) + (j & 1) * kRegion) +
-                          orow_l * kStride + col0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += *reinterpret_cast<const floatx4*>(rj + 4 * e);
-      }
-      const int r_out = mt * C::kRows + rg * 16 + orow_l;
-      if (r_out < a.M) {
-        const int64_t orow = orow_base + r_out;
-        if (final_out) {
-          uint16_t* orp = a.o + orow * kDv + col0;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            bf16x4 v;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = (__bf16)acc[e][i];
-            *reinterpret_cast<bf16x4*>(orp + 4 * e) = v;
-          }
-        } else {
-          float* orp = a.part_o + orow * kDv + col0;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) *reinterpret_cast<floatx4*>(orp + 4 * e) = acc[e];
-        }
-      }
-      if (tg == 0 && g == 0 && row_ok) {
-        const float lse = l_all > 0.f ? m_all * kLn2 + logf(l_all) : -INFINITY;
-        const int64_t orow = orow_base + row;
-        if (final_out) a.lse[orow] = lse; else a.part_lse[orow] = lse;
-      }
-      __syncthreads();   // regions are reused by the next run's tiles
+      cur_item = nx_item;
+      cur_blk = nx_blk;
+      cur_hi = nx_hi;
+      nx_item = n2_item;
+      nx_blk = n2_blk;
+      nx_hi = n2_hi;
+      ++t;
+      return has_next;
+    };
+    while (step(s0, s1) && step(s1, s0)) {
     }
   }
+
 }
 
 // Merge of the partial results of items split over several workers, and the
-// empty result of items with no key.
+// empty result of items with no key (the unfused path).
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   const int item = blockIdx.x;
   const int slot0 = a.num_splits[item];
   const int n = a.num_splits[item + 1] - slot0;
   if (n == 1) return;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  typedef __bf16 bf16x8l __attribute__((ext_vector_type(8)));
-  for (int r = blockIdx.y * 4 + wave; r < a.M; r += 4 * gridDim.y) {
-    const int64_t orow = (int64_t)item * a.M + r;
-    float mx = -INFINITY;
-    for (int k = 0; k < n; ++k) mx = fmaxf(mx, a.part_lse[(int64_t)(slot0 + k) * a.M + r]);
-    float acc[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-    float tot = 0.f;
-    if (mx != -INFINITY) {
-      for (int k = 0; k < n; ++k) {
-        const int64_t prow = (int64_t)(slot0 + k) * a.M + r;
-        const float lk = a.part_lse[prow];
-        const float wk = lk == -INFINITY ? 0.f : expf(lk - mx);
-        tot += wk;
-        const floatx4* src = reinterpret_cast<const floatx4*>(a.part_o + prow * kDv + 8 * lane);
-        const floatx4 v0 = src[0], v1 = src[1];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc[e] += wk * v0[e];
-          acc[4 + e] += wk * v1[e];
-        }
-      }
-    }
-    const float inv = tot > 0.f ? 1.f / tot : 0.f;
-    bf16x8l v;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = (__bf16)(acc[e] * inv);
-    *reinterpret_cast<bf16x8l*>(a.o + orow * kDv + 8 * lane) = v;
-    if (lane == 0) a.lse[orow] = tot > 0.f ? mx + logf(tot) : -INFINITY;
+  for (int rr = blockIdx.y * 4; rr < a.M; rr += 4 * gridDim.y) {
+    const int nrr = min(4, a.M - rr);
+    if (n == 0) write_empty(a, item, rr, nrr, threadIdx.x, 256);
+    else merge_rows(a, item, slot0, n, rr, nrr, threadIdx.x, 256);
   }
+}
+
+template <int NR, int NT>
+hipError_t launch_variant(const DecodeArgs& a, hipStream_t stream) {
+  const int groups = (a.num_workers + 7) / 8;
+  const int grid = a.m_tiles == 1 ? a.num_workers : groups * 8 * a.m_tiles;
+  hipLaunchKernelGGL((decode_kernel<NR, NT>), dim3(grid), dim3(64 * NR * NT), 0, stream, a);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, int variant, hipStream_t stream) {
-  const int groups = (a.num_workers + 7) / 8;
-  if (variant == kVariantRows16) {
-    const int grid = a.m_tiles == 1 ? a.num_workers : groups * 8 * a.m_tiles;
-    hipLaunchKernelGGL((decode_kernel<1, 4>), dim3(grid), dim3(256), 0, stream, a);
-  } else {
-    const int grid = a.m_tiles == 1 ? a.num_workers : groups * 8 * a.m_tiles;
-    hipLaunchKernelGGL((decode_kernel<4, 1>), dim3(grid), dim3(256), 0, stream, a);
-  }
-  return hipGetLastError();
+  if (variant == kVariantRows16) return launch_variant<1, 4>(a, stream);
+  return launch_variant<4, 1>(a, stream);
 }
 
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream) {

@@ -3,12 +3,14 @@
 // scheduler metadata and num_splits).  The pages do not say how work is split;
 // this kernel implements the rule stated in the C header:
 //   n_i = ceil(len_i / 64) blocks, item cost = overhead + n_i, items laid end
-//   to end on a cost axis (start C_i, total T), P = max(1, ceil(T / W)) units
-//   per worker, worker w owning units [w P, (w + 1) P), block b of item i on
-//   unit C_i + overhead + b.
-// One workgroup computes it from closed forms: the workers touching item i's
-// blocks are floor((C_i + overhead) / P) .. floor((C_{i+1} - 1) / P), so the
-// split count and every worker's split number follow without a walk.
+//   to end on a cost axis (start C_i, total T); the first W' = min(W, T)
+//   workers share the axis evenly, worker w owning units
+//   [floor(w T / W'), floor((w + 1) T / W')); block b of item i sits on unit
+//   C_i + overhead + b.
+// One workgroup computes it from closed forms: unit x belongs to worker
+// floor(((x + 1) W' - 1) / T), so the workers touching item i's blocks are
+// owner(C_i + overhead) .. owner(C_{i+1} - 1), every one of them with at
+// least one block, and the split count and split numbers follow without a walk.
 #include "mla_common.h"
 
 namespace mla {
@@ -69,27 +71,33 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
   if (tid == kPlanThreads - 1) start[num_items] = incl;
   __syncthreads();
   const int T = start[num_items];
-  const int P = max(1, (T + W - 1) / W);
+  const int We = min(W, T);
+  // Owner of unit x (T >= 1 whenever an item has a block).
+  auto owner = [&](int x) -> int { return T > 0 ? (int)((((int64_t)x + 1) * We - 1) / T) : 0; };
 
   // Split counts and their exclusive prefix.
   local = 0;
   for (int i = i0; i < i1; ++i) {
     const int first = start[i] + c, end = start[i + 1];
-    if (end > first) local += (end - 1) / P - first / P + 1;
+    if (end > first) local += owner(end - 1) - owner(first) + 1;
   }
   const int sincl = block_inclusive_scan(local, wave_sums);
   run = sincl - local;
   for (int i = i0; i < i1; ++i) {
     num_splits[i] = run;
     const int first = start[i] + c, end = start[i + 1];
-    if (end > first) run += (end - 1) / P - first / P + 1;
+    if (end > first) run += owner(end - 1) - owner(first) + 1;
   }
   if (tid == kPlanThreads - 1) num_splits[num_items] = sincl;
 
   // One row per worker.
   for (int w = tid; w < W; w += kPlanThreads) {
     int32_t* row = plan + kPlanWords * (1 + w);
-    const int lo = w * P, hi = min(lo + P, T);
+    int lo = T, hi = T;
+    if (w < We) {
+      lo = (int)(((int64_t)w * T) / We);
+      hi = (int)(((int64_t)(w + 1) * T) / We);
+    }
     int first_item = -1, first_blk = 0, last_item = -1, last_end = 0, split = 0;
     if (lo < hi) {
       // Last item starting at or before lo.
@@ -103,7 +111,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
         if (bl < bh) {
           first_item = i;
           first_blk = bl - start[i] - c;
-          split = w - (start[i] + c) / P;
+          split = w - owner(start[i] + c);
           break;
         }
       }
@@ -137,7 +145,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
   if (tid == 0) {
     plan[0] = W;
     plan[1] = c;
-    plan[2] = P;
+    plan[2] = We;
     plan[3] = num_items;
     plan[4] = kPlanVersion;
     plan[5] = kPage;
@@ -150,9 +158,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
 
 int plan_max_items() { return kPlanMaxItems; }
 
-hipError_t launch_plan(const int32_t* seqlens, int /*batch*/, int /*s_q*/, int topk, int num_items,
-                       int num_workers, int overhead, int32_t* plan, int32_t* num_splits,
-                       hipStream_t stream) {
+hipError_t launch_plan(const int32_t* seqlens, int topk, int num_items, int num_workers,
+                       int overhead, int32_t* plan, int32_t* num_splits, hipStream_t stream) {
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, seqlens, topk, num_items,
                      num_workers, overhead, plan, num_splits);
   return hipGetLastError();

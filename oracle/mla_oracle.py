@@ -160,7 +160,7 @@ def merge_splits(o_parts: np.ndarray, lse_parts: np.ndarray):
 # Split-KV scheduler ("tile_scheduler_metadata" / "num_splits")
 # --------------------------------------------------------------------------
 PLAN_WORDS = 8        # int32 words per plan row
-PLAN_VERSION = 1
+PLAN_VERSION = 2
 
 
 def plan(lengths, num_workers: int, overhead: int):
@@ -169,16 +169,17 @@ def plan(lengths, num_workers: int, overhead: int):
     Each item (a sequence; in sparse mode a query token) of length ``len``
     has n = ceil(len / 64) blocks and costs ``overhead + n`` units, the
     overhead standing for loading its queries and writing its result.  Items
-    are laid end to end on a cost axis of total T; every worker owns an equal
-    interval of P = max(1, ceil(T / W)) units, worker w owning [w*P, (w+1)*P).
-    The block b of item i occupies the unit [C_i + overhead + b, ... + 1),
-    C_i being the item's start.  A worker processes, for every item, the
-    blocks whose units fall inside its interval (a contiguous run, possibly
-    empty); the non-empty runs of one item, in worker order, are the item's
-    splits, numbered 0, 1, ...
+    are laid end to end on a cost axis of total T.  The first W' = min(W, T)
+    workers share the axis evenly: worker w owns the units
+    [floor(w T / W'), floor((w + 1) T / W')), at least one unit each; the
+    others get nothing.  Block b of item i occupies the unit
+    C_i + overhead + b, C_i being the item's start.  A worker processes, for
+    every item, the blocks whose units fall inside its interval (a contiguous
+    run, possibly empty); the non-empty runs of one item, in worker order, are
+    the item's splits, numbered 0, 1, ...
 
     Returns (plan int32 [(W + 1) * 8], num_splits int32 [num_items + 1]):
-      plan row 0  = [W, overhead, P, num_items, version, 64, T, 0]
+      plan row 0  = [W, overhead, W', num_items, version, 64, T, 0]
       plan row 1+w = [first item, its first block, last item, end block of the
                       last item, split number of the first item's run, 0, 0, 0]
                     or [-1, 0, -1, 0, 0, 0, 0, 0] for a worker with no blocks.
@@ -196,12 +197,15 @@ def plan(lengths, num_workers: int, overhead: int):
         start.append(acc)
         acc += c + n
     T = acc
-    P = max(1, -(-T // W))
+    We = min(W, T)
     rows = np.zeros((W + 1, PLAN_WORDS), dtype=np.int64)
-    rows[0] = [W, c, P, len(lengths), PLAN_VERSION, PAGE, T, 0]
+    rows[0] = [W, c, We, len(lengths), PLAN_VERSION, PAGE, T, 0]
     counts = [0] * len(lengths)
     for w in range(W):
-        lo, hi = w * P, min((w + 1) * P, T)
+        if w < We:
+            lo, hi = (w * T) // We, ((w + 1) * T) // We
+        else:
+            lo = hi = T
         runs = []
         for i, n in enumerate(nblk):
             if n == 0:

@@ -53,6 +53,7 @@ def _dims(*a):
 def test_plan_dims():
     assert _dims(64, 1, 16, 1, 0, 256) == (0, 256, 8 * 257, 64)
     assert _dims(16, 8, 8 * 128, 1, 2048, 100) == (0, 100, 8 * 101, 128)       # sparse: items = b * s_q
+    assert _dims(32, 2, 256, 1, 0, 128) == (0, 128, 8 * 129, 32)
     assert _dims(4, 1, 16, 2, 0, 8)[0] == _lib.MLA_ERR_UNSUPPORTED              # h_kv = 2
     assert _dims(4, 3, 16, 1, 64, 8)[0] == _lib.MLA_ERR_INVALID_ARGUMENT        # rows not a multiple of s_q
     assert _dims(-1, 1, 16, 1, 0, 8)[0] == _lib.MLA_ERR_INVALID_ARGUMENT
@@ -137,3 +138,15 @@ def test_product_path_does_not_use_the_oracle():
             if fn.endswith((".py", ".hip", ".h", ".cpp")):
                 txt = open(os.path.join(dirpath, fn)).read()
                 assert not re.search(r"^\s*(from|import)\s+oracle\b|\boracle\.|mla_oracle", txt, re.M), fn
+
+
+def test_plan_num_workers_inverts_plan_dims():
+    l = _lib.lib()
+    for shape in [(64, 1, 16, 1, 0), (16, 8, 1024, 1, 2048), (32, 2, 256, 1, 0), (3, 1, 40, 1, 0)]:
+        for W in (1, 7, 256):
+            st, Wd, words, _ = _dims(*shape, W)
+            assert st == 0 and Wd == W
+            assert l.mla_plan_num_workers(words, *shape) == W
+    assert l.mla_plan_num_workers(5, 64, 1, 16, 1, 0) == -1
+    assert l.mla_plan_num_workers(8 * 10 + 3, 64, 1, 16, 1, 0) == -1  # not whole rows
+    assert l.mla_plan_num_workers(8, 64, 1, 16, 1, 0) == -1           # header only

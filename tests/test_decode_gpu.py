@@ -241,3 +241,22 @@ def test_validate_inputs():
     ws = wl.sparse_topk(B=2)
     assert m.validate_inputs(i32_dev(ws.block_table), i32_dev(ws.cache_seqlens), ws.kv.shape[0],
                              indices=i32_dev(ws.indices)) == 0
+
+
+def test_phase_split_equals_one_call():
+    m = _m()
+    w = wl.build("phases", 39, np.array([4096, 1, 2000, 777, 64, 65, 0]), B=7, s_q=2, h_q=16,
+                 num_pages=200, causal=True, poison=True)
+    d = Dev(w)
+    plan, ns = m.get_mla_metadata(d.sl, 32, 1, num_workers=37)
+    o3, l3 = m.mla_decode_with_kvcache(d.q, d.kv, d.bt, d.sl, 512, plan, ns, causal=True)
+    o1 = torch.empty_like(o3)
+    l1 = torch.empty_like(l3)
+    ws = torch.empty(1 << 24, dtype=torch.uint8, device="cuda")
+    m.mla_decode_with_kvcache(d.q, d.kv, d.bt, d.sl, 512, plan, ns, causal=True, out=(o1, l1),
+                              workspace=ws, phases=1)
+    m.mla_decode_with_kvcache(d.q, d.kv, d.bt, d.sl, 512, plan, ns, causal=True, out=(o1, l1),
+                              workspace=ws, phases=2)
+    torch.cuda.synchronize()
+    assert torch.equal(o3.view(torch.int16), o1.view(torch.int16)) and torch.equal(l3, l1)
+    compare(w, o3, l3, label="phases")

@@ -287,7 +287,7 @@ def _read_plan_examples():
 
 def test_plan_hand_worked_examples():
     exs = _read_plan_examples()
-    assert len(exs) == 3
+    assert len(exs) == 4
     for e in exs:
         p, ns = orc.plan(e["lengths"], e["workers"][0], e["overhead"][0])
         rows = p.reshape(-1, 8)
@@ -300,7 +300,8 @@ def _check_plan_invariants(lengths, W, c):
     p, ns = orc.plan(lengths, W, c)
     rows = p.reshape(-1, 8)
     nblk = [-(-L // 64) for L in lengths]
-    P = rows[0, 2]
+    T, We = rows[0, 6], rows[0, 2]
+    P = -(-T // We) if We else 0          # the longest worker interval
     runs = orc.plan_runs(p, lengths)
     cover = [np.zeros(n, dtype=int) for n in nblk]
     per_item = {i: [] for i in range(len(lengths))}
