@@ -16,11 +16,19 @@ over a fresh layer would.  A GPU sleep queued ahead of the timed steps lets
 the host enqueue them all before the GPU reaches them, so the K steps run
 back to back and the HIP events measure GPU time, not Python launch time.
 
+`roofline.traffic` is the HBM traffic of one decode launch measured with
+rocprofv3 counters (FETCH_SIZE and WRITE_SIZE, each calibrated against a plain
+device copy of known size, see --calibrate-copy) and stored in
+profiles/decode_memory_bound_traffic.json together with the SHA-256 of the
+kernel source it was taken on; it is reported only while that source is
+unchanged, else null.
+
 Prints one JSON line (the last line of stdout).
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -121,6 +129,43 @@ def run_workload(torch, m, w, steps, warmup, ncopies=NCOPIES):
                 combine_ms=float(np.mean(comb_ms)), num_workers=W, o=o, lse=lse)
 
 
+HERE = os.path.dirname(os.path.abspath(__file__))
+DECODE_SRC = os.path.join(HERE, "mla_paged_kv_get_amd", "csrc", "mla_decode.hip")
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "decode_memory_bound_traffic.json")
+
+
+def source_sha256(path=DECODE_SRC):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per decode launch from the committed counter run, if it was
+    taken on this workload and on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("workload") != workload or t.get("source_sha256") != source_sha256():
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def calibrate_copy(torch, mib, reps=10):
+    """Plain device-to-device copies of `mib` MiB: the reference dispatches
+    for scaling the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n, "reps": reps}), flush=True)
+
+
 def cpu_baseline(w, budget_s=10.0):
     """The CPU oracle on the same workload, repeated until ~budget_s of CPU time."""
     from oracle import mla_oracle as orc
@@ -156,6 +201,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--secondary", action="store_true",
                     help="also time the near-ridge, MTP-causal and sparse top-k workloads")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run plain device copies of MIB MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the decode shards over sequences with no exchange, "
@@ -166,6 +213,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        calibrate_copy(torch, args.calibrate_copy)
+        return
     import mla_paged_kv_get_amd as m
     from mla_paged_kv_get_amd import workloads as wl
 
@@ -196,7 +246,8 @@ def main():
         "step_breakdown_ms": {"plan": round(r["plan_ms"], 5), "decode": round(r["decode_ms"], 5),
                               "combine": round(r["combine_ms"], 5)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(w.name),
                      "kernel": "split decode kernel", "launch_ms": round(r["decode_ms"], 5),
                      "mfma_tflops": round(flops / dec_s / 1e12, 2),
                      "mfma_frac": round(flops / dec_s / 1e12 / BF16_PEAK_TFLOPS, 4)},

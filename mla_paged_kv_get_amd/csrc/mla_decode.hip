@@ -16,20 +16,22 @@
 //    wave instruction reads whole 128-byte lines.  Rows are placed in LDS in
 //    8-row x 128-B blocks with an XOR swizzle of the 16-byte chunks, which
 //    spreads both the row-fragment reads of QK^T and the transposed reads of
-//    PV over the LDS banks.  Two stages live in two distinct LDS arrays, so
-//    the compiler does not serialise the copy into one with the reads of the
-//    other.
+//    PV over the LDS banks.  Two stages: tile t + 1 is requested before the
+//    wait for tile t.  The copies are issued from inline assembly and waited
+//    for with explicit vmcnt counts (see copy_to_lds_16).
 //  * S^T = K Q^T with v_mfma_f32_16x16x32_bf16: A = 16 key rows read from LDS,
-//    B = 16 query rows held in registers (Q of the next item is fetched as soon
-//    as the last QK^T of the current item has been issued).
+//    B = 16 query rows held in registers.
 //  * Online softmax in base 2 (scores pre-multiplied by scale*log2(e)).  The
 //    running reference of a row only moves when the row max exceeds it by more
 //    than 8 (a factor 2^8), so the O accumulators are rescaled a few times per
 //    run instead of every tile; numerator and denominator share the reference,
 //    so the result is the same.
-//  * O^T += V^T P^T with the same MFMA: P^T comes straight from the S^T
-//    accumulators (the key order inside the contraction is permuted to match),
-//    V^T fragments come from LDS through ds_read_b64_tr_b16.
+//  * O^T += V^T P^T with the same MFMA; V^T fragments come from LDS through
+//    ds_read_b64_tr_b16.  Items of up to 16 query rows (the memory-bound
+//    decode case) split each tile's keys over the 4 waves for QK^T and the
+//    512 output columns for PV, exchanging P through LDS, so a run ends
+//    without merging partial outputs across waves.  Larger items use 16 rows
+//    per wave and all keys of the tile.
 //  * Keys past a sequence's length inside its last page, and sparse padding
 //    entries, are loaded from a valid row of the same sequence and masked to
 //    -inf, so no value outside the key set (e.g. NaN garbage) is ever read.
@@ -85,6 +87,27 @@ __device__ __forceinline__ int read_scalar(const int32_t* p) {
   int v;
   asm volatile("s_load_dword %0, %1, 0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
   return v;
+}
+
+// One global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane
+// l's bytes land at lds + 16 l.  Issued from inline assembly, M0 saved and
+// restored around it, so that the compiler does not see an LDS write: it
+// would otherwise make every later LDS read wait for all copies in flight,
+// which serialises the tile pipeline.  Whoever reads the destination waits
+// for the copy with an explicit vmcnt and a barrier.
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+__device__ __forceinline__ void copy_to_lds_16(const void* src, unsigned lds) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(src)
+      : "memory");
 }
 
 // Workgroup barrier that does not wait for the wave's outstanding global
@@ -143,17 +166,31 @@ __device__ void merge_rows(const DecodeArgs& a, int item, int slot0, int n, int 
   }
 }
 
-template <int NR, int NT>
+template <int NR, int NT, bool SPARSE>
 __global__ __launch_bounds__(64 * NR * NT, 1) void decode_kernel(DecodeArgs a) {
   using C = Cfg<NR, NT>;
-  static_assert(NT == 1 || NT == 4, "key split of a tile: 1 or 4 waves");
-  constexpr int kWaitAllButCopy = waitcnt_vm(C::kLoads);
-  static_assert(C::kLoads < 64, "vmcnt holds 6 bits");
+  static_assert((NR == 4 && NT == 1) || (NR == 1 && NT == 4), "64-row tiles or 16 rows x 4 key groups");
+  // Wave roles.  NT == 1: wave = 16 query rows, all 64 keys of a tile, all 512
+  // output columns.  NT == 4 (items of at most 16 rows): wave tg computes the
+  // scores of keys 16 tg .. 16 tg + 15 and, after the probabilities of the
+  // whole tile are exchanged through LDS, output columns 128 tg .. 128 tg + 127
+  // over all 64 keys; the waves share one softmax reference per row, so no
+  // merge of partial outputs is needed when a run ends.
+  constexpr bool kColSplit = NT == 4;
+  constexpr int kDt = kDv / 16 / NT;           // 16-column output blocks per wave
+  // vector-memory operations issued per wave for a tile: copy, sparse index loads
+  constexpr int kRaw = C::kLaneRows;
+  constexpr int kWaitKeepCopy = waitcnt_vm(C::kLoads);
+  constexpr int kWaitKeepRawCopy = waitcnt_vm(C::kLoads + kRaw);
+  static_assert(C::kLoads + kRaw < 64, "vmcnt holds 6 bits");
   __shared__ __attribute__((aligned(1024))) char s0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char s1[kTileBytes];
   __shared__ __attribute__((aligned(16))) unsigned char kvalid[4][64];   // sparse key validity, tile t -> t & 3
-  __shared__ float red_m[NT][C::kRows];
-  __shared__ float red_l[NT][C::kRows];
+  __shared__ float red_m[NT][16];     // column split: per-wave row maxima of the tile
+  __shared__ float red_l[NT][16];     // column split: per-wave row sums at the end of a run
+  // column split: P^T of the tile in bf16, [row][key pair block c][lane group g][8]:
+  // slot 4 h + i of (c, g) holds key 16 (2 c + h) + 4 g + i.
+  __shared__ __attribute__((aligned(16))) char pbuf[kColSplit ? 16 * 128 : 16];
 
   // Worker and row tile of this workgroup.  Row tiles of one worker are placed
   // 8 workgroups apart so that they land on the same XCD (workgroups are
@@ -175,11 +212,11 @@ __global__ __launch_bounds__(64 * NR * NT, 1) void decode_kernel(DecodeArgs a) {
   const int g = lane >> 4;      // lane group (k slice of MFMA operands)
   const int li = lane & 15;     // row (query row / key row) inside a 16-block
   const int rg = wave % NR;     // row group of this wave
-  const int tg = wave / NR;     // key group of this wave
+  const int tg = wave / NR;     // key group (and, split, column quarter) of this wave
   const int row0 = mt * C::kRows;
   const int row = row0 + rg * 16 + li;   // query row inside the item (S^T column)
   const bool row_ok = row < a.M;
-  const bool sparse = a.topk > 0;
+  constexpr bool sparse = SPARSE;      // top-k index lists (a.topk > 0)
 
   const int32_t* prow = a.plan + kPlanWords * (1 + w);
   const int it_first = prow[0], blk_first = prow[1], it_last = prow[2], blk_end = prow[3],
@@ -193,10 +230,12 @@ __global__ __launch_bounds__(64 * NR * NT, 1) void decode_kernel(DecodeArgs a) {
     const int k_base = ((tk >> 3) * 9 << 10) + ((tk & 7) << 7);
     const int k_x0 = ((g ^ swz(tk)) << 4);            // even ks: chunk & 7 == g
     const int k_x1 = (((4 + g) ^ swz(tk)) << 4);      // odd ks:  chunk & 7 == 4 + g
-    //  V^T transposed reads: source row t = tg*kTpw + 4 g + li / 4 (+16 u),
-    //  columns 16 dt + 4 (li & 3) .. + 3, i.e. chunk 2 dt + (li & 3) / 2, half li & 1.
-    const int tv = tg * C::kTpw + 4 * g + (li >> 2);
-    const int v_base = ((tv >> 3) * 9 << 10) + ((tv & 7) << 7) + ((li & 1) << 3);
+    //  V^T transposed reads: source row t = 16 s + 4 g + li / 4 for key subtile
+    //  s, columns c0 + 16 dt + 4 (li & 3) .. + 3 (c0 = first column of the
+    //  wave), i.e. chunk c0 / 8 + 2 dt + (li & 3) / 2, half li & 1.
+    const int tv = 4 * g + (li >> 2);
+    const int v_base = ((tv >> 3) * 9 << 10) + ((tv & 7) << 7) + ((li & 1) << 3) +
+                       (kColSplit ? (2 * tg) << 10 : 0);
     int v_x[4];
 #pragma unroll
     for (int d = 0; d < 4; ++d) v_x[d] = (((2 * d + ((li & 3) >> 1)) ^ swz(tv)) << 4);
@@ -212,8 +251,7 @@ __global__ __launch_bounds__(64 * NR * NT, 1) void decode_kernel(DecodeArgs a) {
     const char* kv_bytes = reinterpret_cast<const char*>(a.kv);
 
     // Sequence length of each of this worker's items, lane j holding item
-    // it_first + j, read once here: a vector load issued after a tile's copy
-    // would make its wait cover the copy too.
+    // it_first + j (read in the prologue, before any copy is in flight).
     int lens_v = 0;
     if (lane <= it_last - it_first) {
       const int x = it_first + lane;
@@ -261,8 +299,8 @@ __global__ __launch_bounds__(64 * NR * NT, 1) void decode_kernel(DecodeArgs a) {
       int v[C::kLaneRows];
     };
     auto tile_fetch = [&](int item, int blk, TileRaw& raw) __attribute__((always_inline)) {
-      if (!sparse) {
-        raw.v[0] = a.block_table[(int64_t)item * a.max_blocks + blk];
+      if constexpr (!sparse) {
+        raw.v[0] = read_scalar(a.block_table + (int64_t)item * a.max_blocks + blk);   // not a vector load
       } else {
         const int32_t* idx_row = a.indices + (int64_t)item * a.topk;
 #pragma unroll
@@ -275,7 +313,7 @@ __global__ __launch_bounds__(64 * NR * NT, 1) void decode_kernel(DecodeArgs a) {
     auto tile_finish = [&](int item, int blk, const TileRaw& raw, int64_t (&off)[C::kLaneRows],
                            unsigned char* vslot) __attribute__((always_inline)) {
       const int L = item_len(item);
-      if (!sparse) {
+      if constexpr (!sparse) {
         const int64_t page = raw.v[0];
         const int nvalid = min(kPage, L - blk * kPage);
 #pragma unroll
@@ -296,20 +334,20 @@ __global__ __launch_bounds__(64 * NR * NT, 1) void decode_kernel(DecodeArgs a) {
         }
       }
     };
-    auto issue = [&](char* stage, const int64_t (&off)[C::kLaneRows]) {
+    auto issue = [&](char* stage, const int64_t (&off)[C::kLaneRows]) __attribute__((always_inline)) {
 #pragma unroll
       for (int j = 0; j < C::kLoads; ++j) {
         const int ii = wave * C::kLoads + j;
         const int r = j / 9, cl = j % 9;
         const char* src = kv_bytes + off[r] + cl * 128 + (((lane & 7) ^ cp_swz[r]) << 4);
-        __builtin_amdgcn_global_load_lds(MLA_GBL(src), MLA_LDS(stage + ii * 1024), 16, 0, 0);
+        copy_to_lds_16(src, lds_addr(stage + ii * 1024));
       }
     };
 
     // Per-run state of this wave.
     bf16x8 qf[18];        // B operand of S^T: Q[row][32 ks + 8 g .. + 7]
-    floatx4 oacc[32];     // O^T[16 dt + 4 g + i][row], scaled by 2^-m_ref
-    float m_ref = -INFINITY;
+    floatx4 oacc[kDt];    // O^T[c0 + 16 dt + 4 g + i][row], scaled by 2^-m_ref
+    float m_ref = -INFINITY;   // softmax reference of row `row` (shared by the waves of a split)
     float l_lane = 0.f;   // sum over this lane's keys of 2^(x - m_ref)
 
     // Rows past M borrow row 0's values (their scores are masked to -inf), so
@@ -324,11 +362,16 @@ __global__ __launch_bounds__(64 * NR * NT, 1) void decode_kernel(DecodeArgs a) {
       if (!row_ok) return 0;
       return (!sparse && a.causal) ? L - a.s_q + row / a.h_q + 1 : L;
     };
+    auto rescale = [&](float m_new) __attribute__((always_inline)) {
+      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_ref - m_new);
+      l_lane *= alpha;
+#pragma unroll
+      for (int d = 0; d < kDt; ++d) oacc[d] *= alpha;
+      m_ref = m_new;
+    };
 
     // Consume one tile held in `stage` (keys blk*64 .. blk*64 + 63 of the item).
-    // If next_q >= 0, the query rows of item next_q are fetched once the
-    // tile's QK^T no longer needs the current ones.
-    auto compute = [&](const char* stage, const unsigned char* vslot, int blk, int lim, int next_q) __attribute__((always_inline)) {
+    auto compute = [&](const char* stage, const unsigned char* vslot, int blk, int lim) __attribute__((always_inline)) {
       floatx4 sacc[C::kSub];
 #pragma unroll
       for (int u = 0; u < C::kSub; ++u) sacc[u] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -351,26 +394,18 @@ __global__ __launch_bounds__(64 * NR * NT, 1) void decode_kernel(DecodeArgs a) {
           }
         }
       }
-      if (next_q >= 0) load_q(next_q);
-      // V^T fragments of the one-subtile case are read before the softmax so
-      // that their latency hides behind it.
-      bf16x4 vf[C::kSub == 1 ? 32 : 1];
-      if constexpr (C::kSub == 1) {
-#pragma unroll
-        for (int dt = 0; dt < 32; ++dt) vf[dt] = read_tr(stage + v_base + ((dt >> 2) << 10) + v_x[dt & 3]);
-      }
-      // Scale, mask, row max.
+      // Scale, mask, row max over this wave's keys.
       float x[C::kSub][4];
       float mx = -INFINITY;
 #pragma unroll
       for (int u = 0; u < C::kSub; ++u) {
         const int t0 = tg * C::kTpw + 16 * u + 4 * g;       // tile row of element i = 0
         unsigned vb = 0;
-        if (sparse) vb = *reinterpret_cast<const unsigned*>(vslot + t0);
+        if constexpr (sparse) vb = *reinterpret_cast<const unsigned*>(vslot + t0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           bool ok;
-          if (sparse) ok = row_ok && ((vb >> (8 * i)) & 0xff);
+          if constexpr (sparse) ok = row_ok && ((vb >> (8 * i)) & 0xff);
           else ok = blk * kPage + t0 + i < lim;
           x[u][i] = ok ? sacc[u][i] * a.scale_log2 : -INFINITY;
           mx = fmaxf(mx, x[u][i]);
@@ -378,40 +413,26 @@ __global__ __launch_bounds__(64 * NR * NT, 1) void decode_kernel(DecodeArgs a) {
       }
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      // Move the reference (and rescale) only when some row outgrew it by 2^8.
-      if (__builtin_amdgcn_ballot_w64(mx > m_ref + kLazy)) {
-        const float m_new = fmaxf(m_ref, mx);
-        const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_ref - m_new);
-        l_lane *= alpha;
-#pragma unroll
-        for (int d = 0; d < 32; ++d) oacc[d] *= alpha;
-        m_ref = m_new;
-      }
-      const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
       float p[C::kSub][4];
+      auto probs = [&]() __attribute__((always_inline)) {
+        const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
 #pragma unroll
-      for (int u = 0; u < C::kSub; ++u)
+        for (int u = 0; u < C::kSub; ++u)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[u][i] = fast_exp2(x[u][i] - m_use);
-          l_lane += p[u][i];
-        }
+          for (int i = 0; i < 4; ++i) p[u][i] = fast_exp2(x[u][i] - m_use);
+      };
 
-      // O^T += V^T P^T.
-      if constexpr (C::kSub == 1) {
-        bf16x8 pb;
+      if constexpr (!kColSplit) {
+        // Move the reference (and rescale) only when some row outgrew it by 2^8.
+        if (__builtin_amdgcn_ballot_w64(mx > m_ref + kLazy)) rescale(fmaxf(m_ref, mx));
+        probs();
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pb[i] = (__bf16)p[0][i];
-          pb[4 + i] = (__bf16)0.f;
-        }
-        const bf16x4 zero4 = {};
+        for (int u = 0; u < C::kSub; ++u)
 #pragma unroll
-        for (int dt = 0; dt < 32; ++dt) {
-          const bf16x8 va = __builtin_shufflevector(vf[dt], zero4, 0, 1, 2, 3, 4, 5, 6, 7);
-          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, oacc[dt], 0, 0, 0);
-        }
-      } else {
+          for (int i = 0; i < 4; ++i) l_lane += p[u][i];
+        // O^T += V^T P^T, P^T straight from the S^T accumulators: slots
+        // 0..3 of lane group g are keys 4 g + i of subtile 2 pr, slots 4..7
+        // the same keys of subtile 2 pr + 1.
 #pragma unroll
         for (int pr = 0; pr < C::kSub / 2; ++pr) {
           bf16x8 pb;
@@ -423,7 +444,51 @@ __global__ __launch_bounds__(64 * NR * NT, 1) void decode_kernel(DecodeArgs a) {
           const char* vrow0 = stage + v_base + (2 * pr) * (2 * 9 * 1024);
           const char* vrow1 = vrow0 + 2 * 9 * 1024;
 #pragma unroll
-          for (int dt = 0; dt < 32; ++dt) {
+          for (int dt = 0; dt < kDt; ++dt) {
+            const int off = ((dt >> 2) << 10) + v_x[dt & 3];
+            const bf16x4 v0 = read_tr(vrow0 + off);
+            const bf16x4 v1 = read_tr(vrow1 + off);
+            const bf16x8 va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+            oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, oacc[dt], 0, 0, 0);
+          }
+        }
+      } else {
+        // Probabilities against the current reference, published with the
+        // row maxima; every wave then sees the tile's row maxima and takes the
+        // same decision on moving the reference (when some row outgrew it by
+        // 2^8), in which case the probabilities are recomputed and published
+        // again.
+        char* pw = pbuf + li * 128 + (tg >> 1) * 64 + g * 16 + (tg & 1) * 8;
+        auto publish = [&]() __attribute__((always_inline)) {
+          bf16x4 pv;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pv[i] = (__bf16)p[0][i];
+          *reinterpret_cast<bf16x4*>(pw) = pv;
+        };
+        probs();
+        publish();
+        if (g == 0) red_m[tg][li] = mx;
+        barrier_keep_loads();
+        float m_tile = red_m[0][li];
+#pragma unroll
+        for (int j = 1; j < NT; ++j) m_tile = fmaxf(m_tile, red_m[j][li]);
+        if (__builtin_amdgcn_ballot_w64(m_tile > m_ref + kLazy)) {   // same outcome in every wave
+          rescale(fmaxf(m_ref, m_tile));
+          probs();
+          publish();
+          barrier_keep_loads();
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) l_lane += p[0][i];
+        // O^T += V^T P^T over the 64 keys, 32 at a time: slots 0..3 of lane
+        // group g are keys 4 g + i of subtile 2 c, slots 4..7 those of 2 c + 1.
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const bf16x8 pb = *reinterpret_cast<const bf16x8*>(pbuf + li * 128 + c * 64 + g * 16);
+          const char* vrow0 = stage + v_base + (2 * c) * (2 * 9 * 1024);
+          const char* vrow1 = vrow0 + 2 * 9 * 1024;
+#pragma unroll
+          for (int dt = 0; dt < kDt; ++dt) {
             const int off = ((dt >> 2) << 10) + v_x[dt & 3];
             const bf16x4 v0 = read_tr(vrow0 + off);
             const bf16x4 v1 = read_tr(vrow1 + off);
@@ -434,10 +499,9 @@ __global__ __launch_bounds__(64 * NR * NT, 1) void decode_kernel(DecodeArgs a) {
       }
     };
 
-    // Finish the run of `item` (its last tile was computed from `stage`, which
-    // is free once every wave is past the barrier below): write O/LSE or the
-    // fp32 partial.
-    auto finish = [&](int item, int split, char* stage) __attribute__((always_inline)) {
+    // Finish the run of `item`: write O/LSE, or the fp32 partial when the item
+    // is split over several runs.
+    auto finish = [&](int item, int split) __attribute__((always_inline)) {
       const int slot0 = read_scalar(a.num_splits + item);
       const int nsplit = read_scalar(a.num_splits + item + 1) - slot0;
       const bool final_out = nsplit == 1;
@@ -445,130 +509,70 @@ __global__ __launch_bounds__(64 * NR * NT, 1) void decode_kernel(DecodeArgs a) {
       float l_tot = l_lane;
       l_tot += __shfl_xor(l_tot, 16, 64);
       l_tot += __shfl_xor(l_tot, 32, 64);
-
-      if constexpr (NT == 1) {
-        if (row_ok) {
-          const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-          const int64_t orow = orow_base + row;
-          if (final_out) {
-            uint16_t* orp = a.o + orow * kDv + 4 * g;
-#pragma unroll
-            for (int dt = 0; dt < 32; ++dt) {
-              bf16x4 v;
-#pragma unroll
-              for (int i = 0; i < 4; ++i) v[i] = (__bf16)(oacc[dt][i] * inv);
-              *reinterpret_cast<bf16x4*>(orp + 16 * dt) = v;
-            }
-          } else {
-            float* orp = a.part_o + orow * kDv + 4 * g;
-#pragma unroll
-            for (int dt = 0; dt < 32; ++dt) *reinterpret_cast<floatx4*>(orp + 16 * dt) = oacc[dt] * inv;
-          }
-          if (g == 0) {
-            const float lse = l_tot > 0.f ? m_ref * kLn2 + logf(l_tot) : -INFINITY;
-            if (final_out) a.lse[orow] = lse; else a.part_lse[orow] = lse;
-          }
-        }
-      } else {
-        // Merge the 4 key groups of each row through the free stage.
-        barrier_keep_loads();                               // stage and red_* are free
-        if (g == 0) {
-          red_m[tg][rg * 16 + li] = m_ref;
-          red_l[tg][rg * 16 + li] = l_tot;
-        }
+      if constexpr (kColSplit) {
+        // row sums of the 4 key groups (same order in every wave)
+        if (g == 0) red_l[tg][li] = l_tot;
         barrier_keep_loads();
-        float m_all = -INFINITY;
+        l_tot = red_l[0][li];
 #pragma unroll
-        for (int j = 0; j < NT; ++j) m_all = fmaxf(m_all, red_m[j][rg * 16 + li]);
-        float l_all = 0.f;
+        for (int j = 1; j < NT; ++j) l_tot += red_l[j][li];
+      }
+      if (row_ok) {
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        const int64_t orow = orow_base + row;
+        const int c0 = kColSplit ? 128 * tg : 0;
+        if (final_out) {
+          uint16_t* orp = a.o + orow * kDv + c0 + 4 * g;
 #pragma unroll
-        for (int j = 0; j < NT; ++j) {
-          const float mj = red_m[j][rg * 16 + li];
-          l_all += mj == -INFINITY ? 0.f : red_l[j][rg * 16 + li] * fast_exp2(mj - m_all);
-        }
-        const float f = m_ref == -INFINITY ? 0.f : fast_exp2(m_ref - m_all);
-        const float sc = f * (l_all > 0.f ? 1.f / l_all : 0.f);
+          for (int dt = 0; dt < kDt; ++dt) {
+            bf16x4 v;
 #pragma unroll
-        for (int d = 0; d < 32; ++d) oacc[d] *= sc;
-        // Region j = [16 rows][516] fp32 (row stride padded against bank conflicts).
-        constexpr int kStride = 516;
-        constexpr int kRegion = 16 * kStride * 4;
-        static_assert(2 * kRegion <= kTileBytes, "merge regions must fit a stage");
-        float* reg0 = reinterpret_cast<float*>(stage);
-        float* reg1 = reinterpret_cast<float*>(stage + kRegion);
-        const int eo = li * kStride + 4 * g;                // this lane's element offset (dt = 0)
-        // Round 1: key groups 2, 3 hand their sums to groups 0, 1.
-        if (tg >= 2) {
-          float* dst = tg == 2 ? reg0 : reg1;
-#pragma unroll
-          for (int dt = 0; dt < 32; ++dt) *reinterpret_cast<floatx4*>(dst + eo + 16 * dt) = oacc[dt];
-        }
-        barrier_keep_loads();
-        if (tg < 2) {
-          const float* src = tg == 0 ? reg0 : reg1;
-#pragma unroll
-          for (int dt = 0; dt < 32; ++dt) oacc[dt] += *reinterpret_cast<const floatx4*>(src + eo + 16 * dt);
-        }
-        // Round 2: group 1 hands its sum to group 0, which writes the result.
-        if (tg == 1) {
-#pragma unroll
-          for (int dt = 0; dt < 32; ++dt) *reinterpret_cast<floatx4*>(reg1 + eo + 16 * dt) = oacc[dt];
-        }
-        barrier_keep_loads();
-        if (tg == 0) {
-#pragma unroll
-          for (int dt = 0; dt < 32; ++dt) oacc[dt] += *reinterpret_cast<const floatx4*>(reg1 + eo + 16 * dt);
-          if (row_ok) {
-            const int64_t orow = orow_base + row;
-            if (final_out) {
-              uint16_t* orp = a.o + orow * kDv + 4 * g;
-#pragma unroll
-              for (int dt = 0; dt < 32; ++dt) {
-                bf16x4 v;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) v[i] = (__bf16)oacc[dt][i];
-                *reinterpret_cast<bf16x4*>(orp + 16 * dt) = v;
-              }
-            } else {
-              float* orp = a.part_o + orow * kDv + 4 * g;
-#pragma unroll
-              for (int dt = 0; dt < 32; ++dt) *reinterpret_cast<floatx4*>(orp + 16 * dt) = oacc[dt];
-            }
-            if (g == 0) {
-              const float lse = l_all > 0.f ? m_all * kLn2 + logf(l_all) : -INFINITY;
-              if (final_out) a.lse[orow] = lse; else a.part_lse[orow] = lse;
-            }
+            for (int i = 0; i < 4; ++i) v[i] = (__bf16)(oacc[dt][i] * inv);
+            *reinterpret_cast<bf16x4*>(orp + 16 * dt) = v;
           }
+        } else {
+          float* orp = a.part_o + orow * kDv + c0 + 4 * g;
+#pragma unroll
+          for (int dt = 0; dt < kDt; ++dt) *reinterpret_cast<floatx4*>(orp + 16 * dt) = oacc[dt] * inv;
+        }
+        if (g == 0 && tg == 0) {
+          const float lse = l_tot > 0.f ? m_ref * kLn2 + logf(l_tot) : -INFINITY;
+          if (final_out) a.lse[orow] = lse; else a.part_lse[orow] = lse;
         }
       }
-
       // reset for the next run
 #pragma unroll
-      for (int d = 0; d < 32; ++d) oacc[d] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int d = 0; d < kDt; ++d) oacc[d] = floatx4{0.f, 0.f, 0.f, 0.f};
       m_ref = -INFINITY;
       l_lane = 0.f;
     };
 
     // ---- the tile stream ----
-    int cur_item = it_first, cur_blk = blk_first, cur_hi = seg_hi(it_first);
+    int cur_item = it_first, cur_blk = blk_first;
+    int t = 0;   // tile counter (validity slot t & 3)
+    int64_t off[C::kLaneRows];
+#pragma unroll
+    for (int d = 0; d < kDt; ++d) oacc[d] = floatx4{0.f, 0.f, 0.f, 0.f};
+    // Prologue.  The loads the compiler tracks (lengths, index data of tile 0,
+    // the first query rows) go out together and are waited for before the
+    // first copy is issued: a tracked load still pending behind a copy would
+    // make its first use wait for the copy as well.
+    TileRaw raw;
+    if constexpr (!sparse) raw.v[0] = a.block_table[(int64_t)cur_item * a.max_blocks + cur_blk];
+    else tile_fetch(cur_item, cur_blk, raw);
+    load_q(cur_item);
+    int cur_hi = seg_hi(cur_item);
     int nx_item, nx_blk, nx_hi;
     advance(cur_item, cur_blk, cur_hi, nx_item, nx_blk, nx_hi);
     int cur_lim = key_limit(cur_item);
     int cur_split = split_first;
-    int t = 0;   // tile counter (validity slot t & 3)
-    int64_t off[C::kLaneRows];
-    load_q(cur_item);
-#pragma unroll
-    for (int d = 0; d < 32; ++d) oacc[d] = floatx4{0.f, 0.f, 0.f, 0.f};
-    {
-      TileRaw raw;
-      tile_fetch(cur_item, cur_blk, raw);
-      tile_finish(cur_item, cur_blk, raw, off, kvalid[0]);
-      issue(s0, off);
-      if (nx_item >= 0) {
-        tile_fetch(nx_item, nx_blk, raw);
-        tile_finish(nx_item, nx_blk, raw, off, kvalid[1]);
-      }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    tile_finish(cur_item, cur_blk, raw, off, kvalid[0]);
+    issue(s0, off);
+    if (nx_item >= 0) {
+      tile_fetch(nx_item, nx_blk, raw);
+      if constexpr (sparse) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      tile_finish(nx_item, nx_blk, raw, off, kvalid[1]);
     }
 
     // One step: tile t sits in `cur`; tile t + 1 goes into `nxt`.  Tile t + 1
@@ -580,23 +584,33 @@ __global__ __launch_bounds__(64 * NR * NT, 1) void decode_kernel(DecodeArgs a) {
       int n2_item = -1, n2_blk = 0, n2_hi = 0;
       if (has_next) advance(nx_item, nx_blk, nx_hi, n2_item, n2_blk, n2_hi);
       barrier_keep_loads();                              // every wave is done with `nxt`
-      TileRaw raw;
+      if (has_next) issue(nxt, off);
       if (n2_item >= 0) tile_fetch(n2_item, n2_blk, raw);  // index data of tile t + 2
+      // Vector-memory operations issued after tile t's copy: the copy of tile
+      // t + 1 and, in sparse mode, the index loads of tile t + 2.  Waiting
+      // until no more than those are outstanding completes tile t's copy
+      // (loads complete in order).  The compiler barrier keeps the index loads
+      // above the wait.
+      asm volatile("" ::: "memory");
       if (has_next) {
-        issue(nxt, off);
-        __builtin_amdgcn_s_waitcnt(kWaitAllButCopy);     // all but tile t + 1's copy
+        if (sparse && n2_item >= 0) __builtin_amdgcn_s_waitcnt(kWaitKeepRawCopy);
+        else __builtin_amdgcn_s_waitcnt(kWaitKeepCopy);
       } else {
         __builtin_amdgcn_s_waitcnt(0);
       }
       barrier_keep_loads();                              // tile t is in LDS for every wave
       if (n2_item >= 0) tile_finish(n2_item, n2_blk, raw, off, kvalid[(t + 2) & 3]);
       const bool ends = !has_next || nx_item != cur_item;
-      compute(cur, kvalid[t & 3], cur_blk, cur_lim, ends && has_next ? nx_item : -1);
+      compute(cur, kvalid[t & 3], cur_blk, cur_lim);
       if (ends) {
-        finish(cur_item, cur_split, cur);
+        finish(cur_item, cur_split);
         if (has_next) {
           cur_lim = key_limit(nx_item);
           cur_split = 0;
+          // Query rows of the next item, completed before the next copy is
+          // issued (see the prologue).
+          load_q(nx_item);
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         }
       }
       cur_item = nx_item;
@@ -611,7 +625,6 @@ __global__ __launch_bounds__(64 * NR * NT, 1) void decode_kernel(DecodeArgs a) {
     while (step(s0, s1) && step(s1, s0)) {
     }
   }
-
 }
 
 // Merge of the partial results of items split over several workers, and the
@@ -632,7 +645,10 @@ template <int NR, int NT>
 hipError_t launch_variant(const DecodeArgs& a, hipStream_t stream) {
   const int groups = (a.num_workers + 7) / 8;
   const int grid = a.m_tiles == 1 ? a.num_workers : groups * 8 * a.m_tiles;
-  hipLaunchKernelGGL((decode_kernel<NR, NT>), dim3(grid), dim3(64 * NR * NT), 0, stream, a);
+  if (a.topk > 0)
+    hipLaunchKernelGGL((decode_kernel<NR, NT, true>), dim3(grid), dim3(64 * NR * NT), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<NR, NT, false>), dim3(grid), dim3(64 * NR * NT), 0, stream, a);
   return hipGetLastError();
 }
 
