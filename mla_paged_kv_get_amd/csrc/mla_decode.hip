@@ -44,14 +44,19 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace mla {
 namespace {
 
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLazy = 8.f;   // log2 of the growth allowed before a rescale
 
-// XOR pattern of tile row t (bijection on t & 7).
-__device__ __forceinline__ int swz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
+// XOR pattern of the 16-byte chunks of tile row t (a bijection on t & 7 for
+// each parity of t >> 3).  Any 16 consecutive rows then put a given chunk in
+// 16 distinct 16-byte bank groups, and so do the 4-row x 2-chunk patterns of
+// the transposed reads.
+__device__ __forceinline__ int swz(int t) { return (((t & 3) << 1) | ((t >> 2) & 1)) ^ (((t >> 3) & 1) << 1); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -62,15 +67,27 @@ __device__ __forceinline__ bf16x4 read_tr(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(p));
 }
 
-template <int NR, int NT>
+// Decode variants.  Both use 4 waves, 64-key tiles and two LDS stages.
+//  Rows16 (items of at most 16 query rows): wave tg computes the scores of
+//    keys 16 tg .. 16 tg + 15 (v_mfma_f32_16x16x32_bf16) and, once the
+//    probabilities of the whole tile are exchanged through LDS, output columns
+//    128 tg .. 128 tg + 127 over all 64 keys.
+//  Rows64 (larger items, 64-row tiles): wave = 2 pair + half; the pair owns 32
+//    query rows, and the wave computes the scores of keys 32 half .. + 31 and
+//    output columns 256 half .. + 255 (v_mfma_f32_32x32x16_bf16), exchanging
+//    the probabilities with its partner through LDS.
+// In both, the waves sharing a row share its softmax reference, so no partial
+// outputs are merged when a run ends.
+template <int V>
 struct Cfg {
-  static constexpr int kWaves = NR * NT;
+  static constexpr bool kWide = V == kVariantRows64;
+  static constexpr int kWaves = 4;
   static constexpr int kThreads = 64 * kWaves;
-  static constexpr int kTpw = 64 / NT;                 // keys per wave per tile
-  static constexpr int kSub = kTpw / 16;               // 16-key subtiles per wave
-  static constexpr int kRows = 16 * NR;                // query rows per workgroup
-  static constexpr int kLoads = 72 / kWaves;           // 1 KB copy instructions per wave per tile
-  static constexpr int kLaneRows = (kLoads + 8) / 9;   // tile rows each lane copies
+  static constexpr int kRows = kWide ? 64 : 16;          // query rows per workgroup
+  static constexpr int kLoads = 72 / kWaves;             // 1 KB copy instructions per wave per tile
+  static constexpr int kLaneRows = (kLoads + 8) / 9;     // tile rows each lane copies
+  static constexpr int kQf = kWide ? 36 : 18;            // bf16x8 B-operand fragments of Q per lane
+  static constexpr int kRowsPerWave = kWide ? 32 : 16;   // rows of the softmax state a wave holds
   static_assert(72 % kWaves == 0 && kLoads % 9 == 0, "tile copy must split evenly");
 };
 
@@ -166,18 +183,11 @@ __device__ void merge_rows(const DecodeArgs& a, int item, int slot0, int n, int 
   }
 }
 
-template <int NR, int NT, bool SPARSE>
-__global__ __launch_bounds__(64 * NR * NT, 1) void decode_kernel(DecodeArgs a) {
-  using C = Cfg<NR, NT>;
-  static_assert((NR == 4 && NT == 1) || (NR == 1 && NT == 4), "64-row tiles or 16 rows x 4 key groups");
-  // Wave roles.  NT == 1: wave = 16 query rows, all 64 keys of a tile, all 512
-  // output columns.  NT == 4 (items of at most 16 rows): wave tg computes the
-  // scores of keys 16 tg .. 16 tg + 15 and, after the probabilities of the
-  // whole tile are exchanged through LDS, output columns 128 tg .. 128 tg + 127
-  // over all 64 keys; the waves share one softmax reference per row, so no
-  // merge of partial outputs is needed when a run ends.
-  constexpr bool kColSplit = NT == 4;
-  constexpr int kDt = kDv / 16 / NT;           // 16-column output blocks per wave
+template <int V, bool SPARSE>
+__global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
+  using C = Cfg<V>;
+  constexpr bool kWide = C::kWide;
+  constexpr int kRw = C::kRowsPerWave;
   // vector-memory operations issued per wave for a tile: copy, sparse index loads
   constexpr int kRaw = C::kLaneRows;
   constexpr int kWaitKeepCopy = waitcnt_vm(C::kLoads);
@@ -186,11 +196,13 @@ __global__ __launch_bounds__(64 * NR * NT, 1) void decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) char s0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char s1[kTileBytes];
   __shared__ __attribute__((aligned(16))) unsigned char kvalid[4][64];   // sparse key validity, tile t -> t & 3
-  __shared__ float red_m[NT][16];     // column split: per-wave row maxima of the tile
-  __shared__ float red_l[NT][16];     // column split: per-wave row sums at the end of a run
-  // column split: P^T of the tile in bf16, [row][key pair block c][lane group g][8]:
-  // slot 4 h + i of (c, g) holds key 16 (2 c + h) + 4 g + i.
-  __shared__ __attribute__((aligned(16))) char pbuf[kColSplit ? 16 * 128 : 16];
+  __shared__ float red_m[4][kRw];     // per-wave row maxima of the tile
+  __shared__ float red_l[4][kRw];     // per-wave row sums at the end of a run
+  __shared__ int red_need[4];         // wide: wave wants the softmax reference moved
+  // Probabilities of the tile in bf16.  Rows16: P^T [row][key pair block c][lane
+  // group g][8], slot 4 h + i of (c, g) = key 16 (2 c + h) + 4 g + i.  Wide: the
+  // B operands of the wave's two PV k-steps, [wave][k-step][lane][8].
+  __shared__ __attribute__((aligned(16))) char pbuf[kWide ? 4 * 2 * 64 * 16 : 16 * 128];
 
   // Worker and row tile of this workgroup.  Row tiles of one worker are placed
   // 8 workgroups apart so that they land on the same XCD (workgroups are
@@ -209,12 +221,15 @@ __global__ __launch_bounds__(64 * NR * NT, 1) void decode_kernel(DecodeArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-  const int g = lane >> 4;      // lane group (k slice of MFMA operands)
-  const int li = lane & 15;     // row (query row / key row) inside a 16-block
-  const int rg = wave % NR;     // row group of this wave
-  const int tg = wave / NR;     // key group (and, split, column quarter) of this wave
+  const int g = lane >> 4;      // lane group of 16
+  const int li = lane & 15;
+  // rows16: the wave's key group / column quarter.  wide: pair and half.
+  const int tg = wave;
+  const int pair = wave >> 1, half = wave & 1;
+  const int lrow = kWide ? (lane & 31) : li;   // row of the lane inside its wave's rows
+  const int hl = lane >> 5;                    // wide: k half of the lane's MFMA operands
   const int row0 = mt * C::kRows;
-  const int row = row0 + rg * 16 + li;   // query row inside the item (S^T column)
+  const int row = row0 + (kWide ? 32 * pair : 0) + lrow;   // query row inside the item (S^T column)
   const bool row_ok = row < a.M;
   constexpr bool sparse = SPARSE;      // top-k index lists (a.topk > 0)
 
@@ -223,22 +238,41 @@ __global__ __launch_bounds__(64 * NR * NT, 1) void decode_kernel(DecodeArgs a) {
             split_first = prow[4];
 
   if (it_first >= 0) {
-    // LDS read offsets of this lane (byte offset of chunk c of tile row t:
-    // ((t / 8) * 9 + c / 8) * 1024 + (t % 8) * 128 + ((c % 8) ^ swz(t)) * 16).
-    //  K row fragments: key row t = tg*kTpw + li (+16 u), chunk 4 ks + g.
-    const int tk = tg * C::kTpw + li;
-    const int k_base = ((tk >> 3) * 9 << 10) + ((tk & 7) << 7);
-    const int k_x0 = ((g ^ swz(tk)) << 4);            // even ks: chunk & 7 == g
-    const int k_x1 = (((4 + g) ^ swz(tk)) << 4);      // odd ks:  chunk & 7 == 4 + g
-    //  V^T transposed reads: source row t = 16 s + 4 g + li / 4 for key subtile
-    //  s, columns c0 + 16 dt + 4 (li & 3) .. + 3 (c0 = first column of the
-    //  wave), i.e. chunk c0 / 8 + 2 dt + (li & 3) / 2, half li & 1.
-    const int tv = 4 * g + (li >> 2);
-    const int v_base = ((tv >> 3) * 9 << 10) + ((tv & 7) << 7) + ((li & 1) << 3) +
-                       (kColSplit ? (2 * tg) << 10 : 0);
-    int v_x[4];
+    // LDS read offsets of this lane.  Byte offset of chunk c of tile row t:
+    // ((t / 8) * 9 + c / 8) * 1024 + (t % 8) * 128 + ((c % 8) ^ swz(t)) * 16.
+    int k_base, v_base;
+    int k_x[4];       // rows16: [0] even ks, [1] odd ks; wide: by ks & 3
+    int v_x[2][4];    // rows16: [0][dt & 3]; wide: [second 4 keys][db & 1]
+    if constexpr (!kWide) {
+      //  K: key row t = 16 tg + li, chunk 4 ks + g.
+      const int tk = 16 * tg + li;
+      k_base = ((tk >> 3) * 9 << 10) + ((tk & 7) << 7);
+      k_x[0] = ((g ^ swz(tk)) << 4);
+      k_x[1] = (((4 + g) ^ swz(tk)) << 4);
+      //  V^T: source row t = 16 s + 4 g + li / 4 of key subtile s, columns
+      //  128 tg + 16 dt + 4 (li & 3) .. + 3: chunk 16 tg + 2 dt + (li & 3) / 2, half li & 1.
+      const int tv = 4 * g + (li >> 2);
+      v_base = ((tv >> 3) * 9 << 10) + ((tv & 7) << 7) + ((li & 1) << 3) + ((2 * tg) << 10);
 #pragma unroll
-    for (int d = 0; d < 4; ++d) v_x[d] = (((2 * d + ((li & 3) >> 1)) ^ swz(tv)) << 4);
+      for (int d = 0; d < 4; ++d) v_x[0][d] = (((2 * d + ((li & 3) >> 1)) ^ swz(tv)) << 4);
+    } else {
+      //  K: key row t = 32 half + lrow, chunk 2 ks + hl.
+      const int tk = 32 * half + lrow;
+      k_base = ((tk >> 3) * 9 << 10) + ((tk & 7) << 7);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) k_x[b] = (((2 * b + hl) ^ swz(tk)) << 4);
+      //  V^T for PV k-step j (keys 16 j .. 16 j + 15 in the order of the score
+      //  accumulators) and column block db: source rows 16 j + 4 hl + li / 4
+      //  (+ 8 for the second read), columns 256 half + 32 db + 16 (g & 1) +
+      //  4 (li & 3) .. + 3: chunk 32 half + 4 db + 2 (g & 1) + (li & 3) / 2.
+      const int tv = 4 * hl + (li >> 2);
+      v_base = (tv << 7) + ((li & 1) << 3) + ((4 * half) << 10);
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          v_x[e][b] = (((4 * b + 2 * (g & 1) + ((li & 3) >> 1)) ^ swz(tv + 8 * e)) << 4);
+    }
 
     // Tile rows this lane copies: t = 8 * (wave * kLoads / 9 + r) + lane / 8.
     int cp_row[C::kLaneRows];
@@ -345,17 +379,20 @@ __global__ __launch_bounds__(64 * NR * NT, 1) void decode_kernel(DecodeArgs a) {
     };
 
     // Per-run state of this wave.
-    bf16x8 qf[18];        // B operand of S^T: Q[row][32 ks + 8 g .. + 7]
-    floatx4 oacc[kDt];    // O^T[c0 + 16 dt + 4 g + i][row], scaled by 2^-m_ref
-    float m_ref = -INFINITY;   // softmax reference of row `row` (shared by the waves of a split)
+    using Acc = typename std::conditional<kWide, floatx16, floatx4>::type;
+    bf16x8 qf[C::kQf];    // B operand of S^T, 8 values of row `row` per fragment
+    Acc oacc[8];          // O^T of the wave's output columns, scaled by 2^-m_ref
+    float m_ref = -INFINITY;   // softmax reference of row `row` (shared by the waves holding it)
     float l_lane = 0.f;   // sum over this lane's keys of 2^(x - m_ref)
 
     // Rows past M borrow row 0's values (their scores are masked to -inf), so
     // no select on the loaded data forces an early wait on the loads.
     auto load_q = [&](int item) __attribute__((always_inline)) {
-      const uint16_t* qrow = a.q + ((int64_t)item * a.M + (row_ok ? row : 0)) * kDqk + 8 * g;
+      const uint16_t* qrow = a.q + ((int64_t)item * a.M + (row_ok ? row : 0)) * kDqk;
 #pragma unroll
-      for (int ks = 0; ks < 18; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
+      for (int ks = 0; ks < C::kQf; ++ks)
+        qf[ks] = kWide ? *reinterpret_cast<const bf16x8*>(qrow + 16 * ks + 8 * hl)
+                       : *reinterpret_cast<const bf16x8*>(qrow + 32 * ks + 8 * g);
     };
     auto key_limit = [&](int item) __attribute__((always_inline)) -> int {   // dense: keys of this lane's row are < limit
       const int L = item_len(item);
@@ -366,40 +403,26 @@ __global__ __launch_bounds__(64 * NR * NT, 1) void decode_kernel(DecodeArgs a) {
       const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_ref - m_new);
       l_lane *= alpha;
 #pragma unroll
-      for (int d = 0; d < kDt; ++d) oacc[d] *= alpha;
+      for (int d = 0; d < 8; ++d) oacc[d] *= alpha;
       m_ref = m_new;
     };
 
     // Consume one tile held in `stage` (keys blk*64 .. blk*64 + 63 of the item).
     auto compute = [&](const char* stage, const unsigned char* vslot, int blk, int lim) __attribute__((always_inline)) {
-      floatx4 sacc[C::kSub];
-#pragma unroll
-      for (int u = 0; u < C::kSub; ++u) sacc[u] = floatx4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (C::kSub == 1) {
-        // all 18 K fragments first: one LDS latency for the whole chain
+      constexpr int kX = kWide ? 16 : 4;     // scores per lane
+      float x[kX];
+      float mx = -INFINITY;
+      if constexpr (!kWide) {
+        // S^T (16 keys x 16 rows): all 18 K fragments first, one LDS latency for the chain.
+        floatx4 sacc = floatx4{0.f, 0.f, 0.f, 0.f};
         bf16x8 kf[18];
 #pragma unroll
         for (int ks = 0; ks < 18; ++ks)
-          kf[ks] = *reinterpret_cast<const bf16x8*>(stage + k_base + ((ks >> 1) << 10) + ((ks & 1) ? k_x1 : k_x0));
+          kf[ks] = *reinterpret_cast<const bf16x8*>(stage + k_base + ((ks >> 1) << 10) + k_x[ks & 1]);
 #pragma unroll
-        for (int ks = 0; ks < 18; ++ks) sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[ks], sacc[0], 0, 0, 0);
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < 18; ++ks) {
-#pragma unroll
-          for (int u = 0; u < C::kSub; ++u) {
-            const int off = k_base + u * (2 * 9 * 1024) + ((ks >> 1) << 10) + ((ks & 1) ? k_x1 : k_x0);
-            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(stage + off);
-            sacc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], sacc[u], 0, 0, 0);
-          }
-        }
-      }
-      // Scale, mask, row max over this wave's keys.
-      float x[C::kSub][4];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int u = 0; u < C::kSub; ++u) {
-        const int t0 = tg * C::kTpw + 16 * u + 4 * g;       // tile row of element i = 0
+        for (int ks = 0; ks < 18; ++ks) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[ks], sacc, 0, 0, 0);
+        // element i: key 16 tg + 4 g + i
+        const int t0 = 16 * tg + 4 * g;
         unsigned vb = 0;
         if constexpr (sparse) vb = *reinterpret_cast<const unsigned*>(vslot + t0);
 #pragma unroll
@@ -407,79 +430,101 @@ __global__ __launch_bounds__(64 * NR * NT, 1) void decode_kernel(DecodeArgs a) {
           bool ok;
           if constexpr (sparse) ok = row_ok && ((vb >> (8 * i)) & 0xff);
           else ok = blk * kPage + t0 + i < lim;
-          x[u][i] = ok ? sacc[u][i] * a.scale_log2 : -INFINITY;
-          mx = fmaxf(mx, x[u][i]);
+          x[i] = ok ? sacc[i] * a.scale_log2 : -INFINITY;
+          mx = fmaxf(mx, x[i]);
         }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      } else {
+        // S^T (32 keys x 32 rows) = K Q^T over 36 k-steps of 16.
+        floatx16 sacc = {};
+        constexpr int kPre = 6;
+        bf16x8 kf[kPre];
+#pragma unroll
+        for (int ks = 0; ks < kPre; ++ks)
+          kf[ks] = *reinterpret_cast<const bf16x8*>(stage + k_base + ((ks >> 2) << 10) + k_x[ks & 3]);
+#pragma unroll
+        for (int ks = 0; ks < 36; ++ks) {
+          const bf16x8 kcur = kf[ks % kPre];
+          if (ks + kPre < 36)
+            kf[ks % kPre] = *reinterpret_cast<const bf16x8*>(stage + k_base + (((ks + kPre) >> 2) << 10) +
+                                                             k_x[(ks + kPre) & 3]);
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur, qf[ks], sacc, 0, 0, 0);
+        }
+        // element r: key 32 half + 8 (r / 4) + 4 hl + r % 4
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int t0 = 32 * half + 8 * q4 + 4 * hl;
+          unsigned vb = 0;
+          if constexpr (sparse) vb = *reinterpret_cast<const unsigned*>(vslot + t0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            bool ok;
+            if constexpr (sparse) ok = row_ok && ((vb >> (8 * i)) & 0xff);
+            else ok = blk * kPage + t0 + i < lim;
+            x[4 * q4 + i] = ok ? sacc[4 * q4 + i] * a.scale_log2 : -INFINITY;
+            mx = fmaxf(mx, x[4 * q4 + i]);
+          }
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      float p[C::kSub][4];
+
+      // Probabilities against the current reference, published with the row
+      // maxima; the waves holding a row then see its maxima over the whole
+      // tile and move the reference together (when the row outgrew it by 2^8),
+      // recomputing and republishing the probabilities.  The decision to take
+      // that path is the same in every wave of the workgroup.
+      float p[kX];
       auto probs = [&]() __attribute__((always_inline)) {
         const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
 #pragma unroll
-        for (int u = 0; u < C::kSub; ++u)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) p[u][i] = fast_exp2(x[u][i] - m_use);
+        for (int i = 0; i < kX; ++i) p[i] = fast_exp2(x[i] - m_use);
       };
-
-      if constexpr (!kColSplit) {
-        // Move the reference (and rescale) only when some row outgrew it by 2^8.
-        if (__builtin_amdgcn_ballot_w64(mx > m_ref + kLazy)) rescale(fmaxf(m_ref, mx));
-        probs();
-#pragma unroll
-        for (int u = 0; u < C::kSub; ++u)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) l_lane += p[u][i];
-        // O^T += V^T P^T, P^T straight from the S^T accumulators: slots
-        // 0..3 of lane group g are keys 4 g + i of subtile 2 pr, slots 4..7
-        // the same keys of subtile 2 pr + 1.
-#pragma unroll
-        for (int pr = 0; pr < C::kSub / 2; ++pr) {
-          bf16x8 pb;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            pb[i] = (__bf16)p[2 * pr][i];
-            pb[4 + i] = (__bf16)p[2 * pr + 1][i];
-          }
-          const char* vrow0 = stage + v_base + (2 * pr) * (2 * 9 * 1024);
-          const char* vrow1 = vrow0 + 2 * 9 * 1024;
-#pragma unroll
-          for (int dt = 0; dt < kDt; ++dt) {
-            const int off = ((dt >> 2) << 10) + v_x[dt & 3];
-            const bf16x4 v0 = read_tr(vrow0 + off);
-            const bf16x4 v1 = read_tr(vrow1 + off);
-            const bf16x8 va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-            oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, oacc[dt], 0, 0, 0);
-          }
-        }
-      } else {
-        // Probabilities against the current reference, published with the
-        // row maxima; every wave then sees the tile's row maxima and takes the
-        // same decision on moving the reference (when some row outgrew it by
-        // 2^8), in which case the probabilities are recomputed and published
-        // again.
-        char* pw = pbuf + li * 128 + (tg >> 1) * 64 + g * 16 + (tg & 1) * 8;
-        auto publish = [&]() __attribute__((always_inline)) {
+      auto publish = [&]() __attribute__((always_inline)) {
+        if constexpr (!kWide) {
           bf16x4 pv;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) pv[i] = (__bf16)p[0][i];
-          *reinterpret_cast<bf16x4*>(pw) = pv;
-        };
+          for (int i = 0; i < 4; ++i) pv[i] = (__bf16)p[i];
+          *reinterpret_cast<bf16x4*>(pbuf + li * 128 + (tg >> 1) * 64 + g * 16 + (tg & 1) * 8) = pv;
+        } else {
+#pragma unroll
+          for (int m = 0; m < 2; ++m) {
+            bf16x8 pv;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) pv[i] = (__bf16)p[8 * m + i];
+            *reinterpret_cast<bf16x8*>(pbuf + ((wave * 2 + m) * 64 + lane) * 16) = pv;
+          }
+        }
+      };
+      probs();
+      publish();
+      if (lane < kRw) red_m[wave][lane] = mx;
+      if constexpr (kWide) {
+        const bool need = __builtin_amdgcn_ballot_w64(mx > m_ref + kLazy) != 0;   // all lanes vote
+        if (lane == 0) red_need[wave] = need;
+      }
+      barrier_keep_loads();
+      float m_tile;
+      bool move;
+      if constexpr (!kWide) {
+        m_tile = red_m[0][li];
+#pragma unroll
+        for (int j = 1; j < 4; ++j) m_tile = fmaxf(m_tile, red_m[j][li]);
+        move = __builtin_amdgcn_ballot_w64(m_tile > m_ref + kLazy) != 0;   // same in every wave
+      } else {
+        m_tile = fmaxf(red_m[2 * pair][lrow], red_m[2 * pair + 1][lrow]);
+        move = (red_need[0] | red_need[1] | red_need[2] | red_need[3]) != 0;
+      }
+      if (move) {
+        rescale(fmaxf(m_ref, m_tile));
         probs();
         publish();
-        if (g == 0) red_m[tg][li] = mx;
         barrier_keep_loads();
-        float m_tile = red_m[0][li];
+      }
 #pragma unroll
-        for (int j = 1; j < NT; ++j) m_tile = fmaxf(m_tile, red_m[j][li]);
-        if (__builtin_amdgcn_ballot_w64(m_tile > m_ref + kLazy)) {   // same outcome in every wave
-          rescale(fmaxf(m_ref, m_tile));
-          probs();
-          publish();
-          barrier_keep_loads();
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) l_lane += p[0][i];
+      for (int i = 0; i < kX; ++i) l_lane += p[i];
+
+      if constexpr (!kWide) {
         // O^T += V^T P^T over the 64 keys, 32 at a time: slots 0..3 of lane
         // group g are keys 4 g + i of subtile 2 c, slots 4..7 those of 2 c + 1.
 #pragma unroll
@@ -488,12 +533,37 @@ __global__ __launch_bounds__(64 * NR * NT, 1) void decode_kernel(DecodeArgs a) {
           const char* vrow0 = stage + v_base + (2 * c) * (2 * 9 * 1024);
           const char* vrow1 = vrow0 + 2 * 9 * 1024;
 #pragma unroll
-          for (int dt = 0; dt < kDt; ++dt) {
-            const int off = ((dt >> 2) << 10) + v_x[dt & 3];
+          for (int dt = 0; dt < 8; ++dt) {
+            const int off = ((dt >> 2) << 10) + v_x[0][dt & 3];
             const bf16x4 v0 = read_tr(vrow0 + off);
             const bf16x4 v1 = read_tr(vrow1 + off);
             const bf16x8 va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
             oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, oacc[dt], 0, 0, 0);
+          }
+        }
+      } else {
+        // O^T += V^T P^T over the 64 keys in k-steps of 16.  k-step j = 2 kb + m
+        // holds, for lane half hl, keys 16 j + 4 hl + i (slots 0..3) and
+        // 16 j + 8 + 4 hl + i (slots 4..7): exactly score elements 8 m .. 8 m + 7
+        // of the same lane in the wave with half == kb.
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          bf16x8 pb;
+          if ((j >> 1) == half) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) pb[i] = (__bf16)p[8 * (j & 1) + i];
+          } else {
+            pb = *reinterpret_cast<const bf16x8*>(pbuf + (((wave ^ 1) * 2 + (j & 1)) * 64 + lane) * 16);
+          }
+          const char* vr0 = stage + v_base + (2 * j) * (9 * 1024);
+          const char* vr1 = vr0 + 9 * 1024;
+#pragma unroll
+          for (int db = 0; db < 8; ++db) {
+            const int off = (db >> 1) << 10;
+            const bf16x4 v0 = read_tr(vr0 + off + v_x[0][db & 1]);
+            const bf16x4 v1 = read_tr(vr1 + off + v_x[1][db & 1]);
+            const bf16x8 va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, oacc[db], 0, 0, 0);
           }
         }
       }
@@ -506,43 +576,57 @@ __global__ __launch_bounds__(64 * NR * NT, 1) void decode_kernel(DecodeArgs a) {
       const int nsplit = read_scalar(a.num_splits + item + 1) - slot0;
       const bool final_out = nsplit == 1;
       const int64_t orow_base = final_out ? (int64_t)item * a.M : (int64_t)(slot0 + split) * a.M;
+      // row sums over the lanes and waves holding the row (same order everywhere)
       float l_tot = l_lane;
-      l_tot += __shfl_xor(l_tot, 16, 64);
+      if constexpr (!kWide) l_tot += __shfl_xor(l_tot, 16, 64);
       l_tot += __shfl_xor(l_tot, 32, 64);
-      if constexpr (kColSplit) {
-        // row sums of the 4 key groups (same order in every wave)
-        if (g == 0) red_l[tg][li] = l_tot;
-        barrier_keep_loads();
+      if (lane < kRw) red_l[wave][lane] = l_tot;
+      barrier_keep_loads();
+      if constexpr (!kWide) {
         l_tot = red_l[0][li];
 #pragma unroll
-        for (int j = 1; j < NT; ++j) l_tot += red_l[j][li];
+        for (int j = 1; j < 4; ++j) l_tot += red_l[j][li];
+      } else {
+        l_tot = red_l[2 * pair][lrow] + red_l[2 * pair + 1][lrow];
       }
       if (row_ok) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         const int64_t orow = orow_base + row;
-        const int c0 = kColSplit ? 128 * tg : 0;
+        // element (d, i) of the lane: column c0 + 16 d + 4 g + i (rows16),
+        // c0 + 32 d + 8 (i / 4) + 4 hl + i % 4 (wide)
+        const int c0 = kWide ? 256 * half + 4 * hl : 128 * tg + 4 * g;
         if (final_out) {
-          uint16_t* orp = a.o + orow * kDv + c0 + 4 * g;
+          uint16_t* orp = a.o + orow * kDv + c0;
 #pragma unroll
-          for (int dt = 0; dt < kDt; ++dt) {
-            bf16x4 v;
+          for (int d = 0; d < 8; ++d)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = (__bf16)(oacc[dt][i] * inv);
-            *reinterpret_cast<bf16x4*>(orp + 16 * dt) = v;
-          }
+            for (int q4 = 0; q4 < (kWide ? 4 : 1); ++q4) {
+              bf16x4 v;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) v[i] = (__bf16)(oacc[d][4 * q4 + i] * inv);
+              *reinterpret_cast<bf16x4*>(orp + (kWide ? 32 * d + 8 * q4 : 16 * d)) = v;
+            }
         } else {
-          float* orp = a.part_o + orow * kDv + c0 + 4 * g;
+          float* orp = a.part_o + orow * kDv + c0;
 #pragma unroll
-          for (int dt = 0; dt < kDt; ++dt) *reinterpret_cast<floatx4*>(orp + 16 * dt) = oacc[dt] * inv;
+          for (int d = 0; d < 8; ++d)
+#pragma unroll
+            for (int q4 = 0; q4 < (kWide ? 4 : 1); ++q4) {
+              floatx4 v;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) v[i] = oacc[d][4 * q4 + i] * inv;
+              *reinterpret_cast<floatx4*>(orp + (kWide ? 32 * d + 8 * q4 : 16 * d)) = v;
+            }
         }
-        if (g == 0 && tg == 0) {
+        const bool lse_lane = kWide ? (half == 0 && hl == 0) : (tg == 0 && g == 0);
+        if (lse_lane) {
           const float lse = l_tot > 0.f ? m_ref * kLn2 + logf(l_tot) : -INFINITY;
           if (final_out) a.lse[orow] = lse; else a.part_lse[orow] = lse;
         }
       }
       // reset for the next run
 #pragma unroll
-      for (int d = 0; d < kDt; ++d) oacc[d] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int d = 0; d < 8; ++d) oacc[d] = Acc{};
       m_ref = -INFINITY;
       l_lane = 0.f;
     };
@@ -552,7 +636,7 @@ __global__ __launch_bounds__(64 * NR * NT, 1) void decode_kernel(DecodeArgs a) {
     int t = 0;   // tile counter (validity slot t & 3)
     int64_t off[C::kLaneRows];
 #pragma unroll
-    for (int d = 0; d < kDt; ++d) oacc[d] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int d = 0; d < 8; ++d) oacc[d] = Acc{};
     // Prologue.  The loads the compiler tracks (lengths, index data of tile 0,
     // the first query rows) go out together and are waited for before the
     // first copy is issued: a tracked load still pending behind a copy would
@@ -641,22 +725,22 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   }
 }
 
-template <int NR, int NT>
+template <int V>
 hipError_t launch_variant(const DecodeArgs& a, hipStream_t stream) {
   const int groups = (a.num_workers + 7) / 8;
   const int grid = a.m_tiles == 1 ? a.num_workers : groups * 8 * a.m_tiles;
   if (a.topk > 0)
-    hipLaunchKernelGGL((decode_kernel<NR, NT, true>), dim3(grid), dim3(64 * NR * NT), 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<V, true>), dim3(grid), dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((decode_kernel<NR, NT, false>), dim3(grid), dim3(64 * NR * NT), 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<V, false>), dim3(grid), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, int variant, hipStream_t stream) {
-  if (variant == kVariantRows16) return launch_variant<1, 4>(a, stream);
-  return launch_variant<4, 1>(a, stream);
+  if (variant == kVariantRows16) return launch_variant<kVariantRows16>(a, stream);
+  return launch_variant<kVariantRows64>(a, stream);
 }
 
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream) {
