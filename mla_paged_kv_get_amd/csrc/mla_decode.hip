@@ -60,6 +60,27 @@ __device__ __forceinline__ int swz(int t) { return (((t & 3) << 1) | ((t >> 2) &
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Reductions over lane pairs (l, l ^ 32) and (l, l ^ 16) with the gfx950 lane
+// swaps (v_permlane32_swap / v_permlane16_swap on two copies of the value):
+// the first result holds the lower lane's value, the second the upper one's,
+// so both lanes of a pair combine the same operands in the same order.
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane i
 // receives element i % 4 of the 8-byte words addressed by lanes 4 e + i / 4,
 // e = 0..3, i.e. one column of the 4 x 16 block the group points at.
@@ -410,8 +431,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     // Consume one tile held in `stage` (keys blk*64 .. blk*64 + 63 of the item).
     auto compute = [&](const char* stage, const unsigned char* vslot, int blk, int lim) __attribute__((always_inline)) {
       constexpr int kX = kWide ? 16 : 4;     // scores per lane
-      float x[kX];
-      float mx = -INFINITY;
+      float x[kX];                           // raw scores of the lane's keys, -inf where masked
+      float mx;                              // raw row max over this wave's keys
       if constexpr (!kWide) {
         // S^T (16 keys x 16 rows): all 18 K fragments first, one LDS latency for the chain.
         floatx4 sacc = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -430,11 +451,10 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
           bool ok;
           if constexpr (sparse) ok = row_ok && ((vb >> (8 * i)) & 0xff);
           else ok = blk * kPage + t0 + i < lim;
-          x[i] = ok ? sacc[i] * a.scale_log2 : -INFINITY;
-          mx = fmaxf(mx, x[i]);
+          x[i] = ok ? sacc[i] : -INFINITY;
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+        mx = xor32_max(xor16_max(mx));
       } else {
         // S^T (32 keys x 32 rows) = K Q^T over 36 k-steps of 16.
         floatx16 sacc = {};
@@ -451,23 +471,34 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
                                                              k_x[(ks + kPre) & 3]);
           sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur, qf[ks], sacc, 0, 0, 0);
         }
-        // element r: key 32 half + 8 (r / 4) + 4 hl + r % 4
+        // element r: key 32 half + 8 (r / 4) + 4 hl + r % 4.  Tiles whose keys
+        // are all valid for every row of the wave skip the per-key mask.
+        const bool full = !sparse && __builtin_amdgcn_ballot_w64(blk * kPage + 32 * half + 32 <= lim) ==
+                                         __builtin_amdgcn_read_exec();
+        if (full) {
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int t0 = 32 * half + 8 * q4 + 4 * hl;
-          unsigned vb = 0;
-          if constexpr (sparse) vb = *reinterpret_cast<const unsigned*>(vslot + t0);
+          for (int r = 0; r < 16; ++r) x[r] = sacc[r];
+        } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            bool ok;
-            if constexpr (sparse) ok = row_ok && ((vb >> (8 * i)) & 0xff);
-            else ok = blk * kPage + t0 + i < lim;
-            x[4 * q4 + i] = ok ? sacc[4 * q4 + i] * a.scale_log2 : -INFINITY;
-            mx = fmaxf(mx, x[4 * q4 + i]);
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int t0 = 32 * half + 8 * q4 + 4 * hl;
+            unsigned vb = 0;
+            if constexpr (sparse) vb = *reinterpret_cast<const unsigned*>(vslot + t0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              bool ok;
+              if constexpr (sparse) ok = row_ok && ((vb >> (8 * i)) & 0xff);
+              else ok = blk * kPage + t0 + i < lim;
+              x[4 * q4 + i] = ok ? sacc[4 * q4 + i] : -INFINITY;
+            }
           }
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+        mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(x[8], x[9]), fmaxf(x[10], x[11])),
+                             fmaxf(fmaxf(x[12], x[13]), fmaxf(x[14], x[15]))));
+        mx = xor32_max(mx);
       }
+      mx *= a.scale_log2;    // scale > 0: the max of the scaled scores
 
       // Probabilities against the current reference, published with the row
       // maxima; the waves holding a row then see its maxima over the whole
@@ -475,10 +506,11 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
       // recomputing and republishing the probabilities.  The decision to take
       // that path is the same in every wave of the workgroup.
       float p[kX];
+      bf16x8 pown[kWide ? 2 : 1];   // wide: the lane's bf16 probabilities, PV k-steps 2 half + m
       auto probs = [&]() __attribute__((always_inline)) {
         const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
 #pragma unroll
-        for (int i = 0; i < kX; ++i) p[i] = fast_exp2(x[i] - m_use);
+        for (int i = 0; i < kX; ++i) p[i] = fast_exp2(__builtin_fmaf(x[i], a.scale_log2, -m_use));
       };
       auto publish = [&]() __attribute__((always_inline)) {
         if constexpr (!kWide) {
@@ -489,10 +521,9 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
         } else {
 #pragma unroll
           for (int m = 0; m < 2; ++m) {
-            bf16x8 pv;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) pv[i] = (__bf16)p[8 * m + i];
-            *reinterpret_cast<bf16x8*>(pbuf + ((wave * 2 + m) * 64 + lane) * 16) = pv;
+            for (int i = 0; i < 8; ++i) pown[m][i] = (__bf16)p[8 * m + i];
+            *reinterpret_cast<bf16x8*>(pbuf + ((wave * 2 + m) * 64 + lane) * 16) = pown[m];
           }
         }
       };
@@ -527,44 +558,62 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
       if constexpr (!kWide) {
         // O^T += V^T P^T over the 64 keys, 32 at a time: slots 0..3 of lane
         // group g are keys 4 g + i of subtile 2 c, slots 4..7 those of 2 c + 1.
+        // 16 MFMAs, (c, dt) in order; the V^T fragments are read kPv MFMAs ahead.
+        bf16x8 pb[2];
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const bf16x8 pb = *reinterpret_cast<const bf16x8*>(pbuf + li * 128 + c * 64 + g * 16);
-          const char* vrow0 = stage + v_base + (2 * c) * (2 * 9 * 1024);
-          const char* vrow1 = vrow0 + 2 * 9 * 1024;
+        for (int c = 0; c < 2; ++c) pb[c] = *reinterpret_cast<const bf16x8*>(pbuf + li * 128 + c * 64 + g * 16);
+        constexpr int kPv = 6;
+        auto vaddr = [&](int n, int e) __attribute__((always_inline)) -> const char* {
+          const int c = n >> 3, dt = n & 7;
+          return stage + v_base + (2 * c + e) * (2 * 9 * 1024) + ((dt >> 2) << 10) + v_x[0][dt & 3];
+        };
+        bf16x4 vq0[kPv], vq1[kPv];
 #pragma unroll
-          for (int dt = 0; dt < 8; ++dt) {
-            const int off = ((dt >> 2) << 10) + v_x[0][dt & 3];
-            const bf16x4 v0 = read_tr(vrow0 + off);
-            const bf16x4 v1 = read_tr(vrow1 + off);
-            const bf16x8 va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-            oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, oacc[dt], 0, 0, 0);
+        for (int n = 0; n < kPv; ++n) {
+          vq0[n] = read_tr(vaddr(n, 0));
+          vq1[n] = read_tr(vaddr(n, 1));
+        }
+#pragma unroll
+        for (int n = 0; n < 16; ++n) {
+          const bf16x8 va = __builtin_shufflevector(vq0[n % kPv], vq1[n % kPv], 0, 1, 2, 3, 4, 5, 6, 7);
+          if (n + kPv < 16) {
+            vq0[n % kPv] = read_tr(vaddr(n + kPv, 0));
+            vq1[n % kPv] = read_tr(vaddr(n + kPv, 1));
           }
+          oacc[n & 7] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[n >> 3], oacc[n & 7], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);   // keep the reads kPv MFMAs ahead
         }
       } else {
         // O^T += V^T P^T over the 64 keys in k-steps of 16.  k-step j = 2 kb + m
         // holds, for lane half hl, keys 16 j + 4 hl + i (slots 0..3) and
         // 16 j + 8 + 4 hl + i (slots 4..7): exactly score elements 8 m .. 8 m + 7
         // of the same lane in the wave with half == kb.
+        bf16x8 pb[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          bf16x8 pb;
-          if ((j >> 1) == half) {
+        for (int j = 0; j < 4; ++j)
+          pb[j] = (j >> 1) == half ? pown[j & 1]
+                                   : *reinterpret_cast<const bf16x8*>(pbuf + (((wave ^ 1) * 2 + (j & 1)) * 64 + lane) * 16);
+        // 32 MFMAs, (j, db) in order; the V^T fragments are read kPv MFMAs ahead.
+        constexpr int kPv = 6;
+        auto vaddr = [&](int n, int e) __attribute__((always_inline)) -> const char* {
+          const int j = n >> 3, db = n & 7;
+          return stage + v_base + (2 * j + e) * (9 * 1024) + ((db >> 1) << 10) + v_x[e][db & 1];
+        };
+        bf16x4 vq0[kPv], vq1[kPv];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) pb[i] = (__bf16)p[8 * (j & 1) + i];
-          } else {
-            pb = *reinterpret_cast<const bf16x8*>(pbuf + (((wave ^ 1) * 2 + (j & 1)) * 64 + lane) * 16);
+        for (int n = 0; n < kPv; ++n) {
+          vq0[n] = read_tr(vaddr(n, 0));
+          vq1[n] = read_tr(vaddr(n, 1));
+        }
+#pragma unroll
+        for (int n = 0; n < 32; ++n) {
+          const bf16x8 va = __builtin_shufflevector(vq0[n % kPv], vq1[n % kPv], 0, 1, 2, 3, 4, 5, 6, 7);
+          if (n + kPv < 32) {
+            vq0[n % kPv] = read_tr(vaddr(n + kPv, 0));
+            vq1[n % kPv] = read_tr(vaddr(n + kPv, 1));
           }
-          const char* vr0 = stage + v_base + (2 * j) * (9 * 1024);
-          const char* vr1 = vr0 + 9 * 1024;
-#pragma unroll
-          for (int db = 0; db < 8; ++db) {
-            const int off = (db >> 1) << 10;
-            const bf16x4 v0 = read_tr(vr0 + off + v_x[0][db & 1]);
-            const bf16x4 v1 = read_tr(vr1 + off + v_x[1][db & 1]);
-            const bf16x8 va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, oacc[db], 0, 0, 0);
-          }
+          oacc[n & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[n >> 3], oacc[n & 7], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);   // keep the reads kPv MFMAs ahead
         }
       }
     };
@@ -578,8 +627,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
       const int64_t orow_base = final_out ? (int64_t)item * a.M : (int64_t)(slot0 + split) * a.M;
       // row sums over the lanes and waves holding the row (same order everywhere)
       float l_tot = l_lane;
-      if constexpr (!kWide) l_tot += __shfl_xor(l_tot, 16, 64);
-      l_tot += __shfl_xor(l_tot, 32, 64);
+      if constexpr (!kWide) l_tot = xor16_sum(l_tot);
+      l_tot = xor32_sum(l_tot);
       if (lane < kRw) red_l[wave][lane] = l_tot;
       barrier_keep_loads();
       if constexpr (!kWide) {
