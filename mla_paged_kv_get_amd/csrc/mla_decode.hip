@@ -470,6 +470,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
             kf[ks % kPre] = *reinterpret_cast<const bf16x8*>(stage + k_base + (((ks + kPre) >> 2) << 10) +
                                                              k_x[(ks + kPre) & 3]);
           sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur, qf[ks], sacc, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);   // keep the reads kPre MFMAs ahead
         }
         // element r: key 32 half + 8 (r / 4) + 4 hl + r % 4.  Tiles whose keys
         // are all valid for every row of the wave skip the per-key mask.
