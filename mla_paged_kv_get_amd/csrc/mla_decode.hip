@@ -148,6 +148,19 @@ __device__ __forceinline__ void copy_to_lds_16(const void* src, unsigned lds) {
       : "memory");
 }
 
+// Same for 4 bytes per lane (global_load_lds_dword): lane l's word lands at lds + 4 l.
+__device__ __forceinline__ void copy_to_lds_4(const void* src, unsigned lds) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dword %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(src)
+      : "memory");
+}
+
 // Workgroup barrier that does not wait for the wave's outstanding global
 // loads (the copies into the other LDS stage stay in flight across it).  The
 // caller has already waited for whatever the barrier must publish; the LDS
@@ -224,6 +237,9 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
   // group g][8], slot 4 h + i of (c, g) = key 16 (2 c + h) + 4 g + i.  Wide: the
   // B operands of the wave's two PV k-steps, [wave][k-step][lane][8].
   __shared__ __attribute__((aligned(16))) char pbuf[kWide ? 4 * 2 * 64 * 16 : 16 * 128];
+  // Wide, sparse: index-list entries of the next tiles, copied in by each wave
+  // ([tile & 3][wave][64]), so that no register load waits behind a tile copy.
+  __shared__ __attribute__((aligned(256))) int idxbuf[kWide && SPARSE ? 4 : 1][4][64];
 
   // Worker and row tile of this workgroup.  Row tiles of one worker are placed
   // 8 workgroups apart so that they land on the same XCD (workgroups are
@@ -389,15 +405,30 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
         }
       }
     };
+    // Copy instruction j (0 .. kLoads - 1) of this wave for a tile: 8 rows x 128 B.
+    auto issue_one = [&](char* stage, const int64_t (&off)[C::kLaneRows], int j) __attribute__((always_inline)) {
+      const int ii = wave * C::kLoads + j;
+      const int r = j / 9, cl = j % 9;
+      const char* src = kv_bytes + off[r] + cl * 128 + (((lane & 7) ^ cp_swz[r]) << 4);
+      copy_to_lds_16(src, lds_addr(stage + ii * 1024));
+    };
     auto issue = [&](char* stage, const int64_t (&off)[C::kLaneRows]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int j = 0; j < C::kLoads; ++j) {
-        const int ii = wave * C::kLoads + j;
-        const int r = j / 9, cl = j % 9;
-        const char* src = kv_bytes + off[r] + cl * 128 + (((lane & 7) ^ cp_swz[r]) << 4);
-        copy_to_lds_16(src, lds_addr(stage + ii * 1024));
-      }
+      for (int j = 0; j < C::kLoads; ++j) issue_one(stage, off, j);
     };
+    // Wide, sparse: copy the 64 index-list entries of tile (item, blk) into ring
+    // slot `slot` (entries past topk repeat the last one; they are padding).
+    auto idx_dma = [&](int item, int blk, int slot) __attribute__((always_inline)) {
+      const int sl = min(blk * kPage + lane, a.topk - 1);
+      copy_to_lds_4(a.indices + (int64_t)item * a.topk + sl, lds_addr(&idxbuf[slot & 3][wave][0]));
+    };
+    auto idx_from_lds = [&](int blk, int slot, TileRaw& raw) __attribute__((always_inline)) {
+#pragma unroll
+      for (int r = 0; r < C::kLaneRows; ++r)
+        raw.v[r] = blk * kPage + cp_row[r] < a.topk ? idxbuf[slot & 3][wave][cp_row[r]] : -1;
+    };
+
+    int64_t off[C::kLaneRows];   // cache byte offsets of the rows this lane copies for the next tile issued
 
     // Per-run state of this wave.
     using Acc = typename std::conditional<kWide, floatx16, floatx4>::type;
@@ -429,7 +460,11 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     };
 
     // Consume one tile held in `stage` (keys blk*64 .. blk*64 + 63 of the item).
-    auto compute = [&](const char* stage, const unsigned char* vslot, int blk, int lim) __attribute__((always_inline)) {
+    // Wide: if dma_stage is set, the copy of the next tile into it (offsets in
+    // `off`) is issued interleaved with the QK^T MFMAs, one instruction every
+    // second k-step, so that issuing it never holds the wave up.
+    auto compute = [&](const char* stage, const unsigned char* vslot, int blk, int lim,
+                       char* dma_stage) __attribute__((always_inline)) {
       constexpr int kX = kWide ? 16 : 4;     // scores per lane
       float x[kX];                           // raw scores of the lane's keys, -inf where masked
       float mx;                              // raw row max over this wave's keys
@@ -470,6 +505,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
             kf[ks % kPre] = *reinterpret_cast<const bf16x8*>(stage + k_base + (((ks + kPre) >> 2) << 10) +
                                                              k_x[(ks + kPre) & 3]);
           sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur, qf[ks], sacc, 0, 0, 0);
+          if ((ks & 1) == 0 && dma_stage != nullptr) issue_one(dma_stage, off, ks >> 1);
           __builtin_amdgcn_sched_barrier(0);   // keep the reads kPre MFMAs ahead
         }
         // element r: key 32 half + 8 (r / 4) + 4 hl + r % 4.  Tiles whose keys
@@ -684,7 +720,6 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     // ---- the tile stream ----
     int cur_item = it_first, cur_blk = blk_first;
     int t = 0;   // tile counter (validity slot t & 3)
-    int64_t off[C::kLaneRows];
 #pragma unroll
     for (int d = 0; d < 8; ++d) oacc[d] = Acc{};
     // Prologue.  The loads the compiler tracks (lengths, index data of tile 0,
@@ -703,7 +738,9 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     tile_finish(cur_item, cur_blk, raw, off, kvalid[0]);
     issue(s0, off);
-    if (nx_item >= 0) {
+    if constexpr (kWide) {
+      if (sparse && nx_item >= 0) idx_dma(nx_item, nx_blk, 1);   // tile 1's offsets are made in step 0
+    } else if (nx_item >= 0) {
       tile_fetch(nx_item, nx_blk, raw);
       if constexpr (sparse) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
       tile_finish(nx_item, nx_blk, raw, off, kvalid[1]);
@@ -717,6 +754,37 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
       const bool has_next = nx_item >= 0;
       int n2_item = -1, n2_blk = 0, n2_hi = 0;
       if (has_next) advance(nx_item, nx_blk, nx_hi, n2_item, n2_blk, n2_hi);
+      if constexpr (kWide) {
+        // Tile t was requested during the previous step's QK^T (and, sparse,
+        // the index list of tile t + 1 before it): nothing else is in flight.
+        if (!sparse && has_next) tile_fetch(nx_item, nx_blk, raw);   // scalar loads
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        barrier_keep_loads();          // tile t in LDS for every wave; every wave is done with `nxt`
+        if (has_next) {
+          if constexpr (sparse) idx_from_lds(nx_blk, t + 1, raw);
+          tile_finish(nx_item, nx_blk, raw, off, kvalid[(t + 1) & 3]);
+        }
+        if (sparse && n2_item >= 0) idx_dma(n2_item, n2_blk, t + 2);
+        const bool ends = !has_next || nx_item != cur_item;
+        compute(cur, kvalid[t & 3], cur_blk, cur_lim, has_next ? nxt : nullptr);
+        if (ends) {
+          finish(cur_item, cur_split);
+          if (has_next) {
+            cur_lim = key_limit(nx_item);
+            cur_split = 0;
+            load_q(nx_item);     // completed here (see the prologue)
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+          }
+        }
+        cur_item = nx_item;
+        cur_blk = nx_blk;
+        cur_hi = nx_hi;
+        nx_item = n2_item;
+        nx_blk = n2_blk;
+        nx_hi = n2_hi;
+        ++t;
+        return has_next;
+      }
       barrier_keep_loads();                              // every wave is done with `nxt`
       if (has_next) issue(nxt, off);
       if (n2_item >= 0) tile_fetch(n2_item, n2_blk, raw);  // index data of tile t + 2
@@ -735,7 +803,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
       barrier_keep_loads();                              // tile t is in LDS for every wave
       if (n2_item >= 0) tile_finish(n2_item, n2_blk, raw, off, kvalid[(t + 2) & 3]);
       const bool ends = !has_next || nx_item != cur_item;
-      compute(cur, kvalid[t & 3], cur_blk, cur_lim);
+      compute(cur, kvalid[t & 3], cur_blk, cur_lim, nullptr);
       if (ends) {
         finish(cur_item, cur_split);
         if (has_next) {
