@@ -237,9 +237,11 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
   // group g][8], slot 4 h + i of (c, g) = key 16 (2 c + h) + 4 g + i.  Wide: the
   // B operands of the wave's two PV k-steps, [wave][k-step][lane][8].
   __shared__ __attribute__((aligned(16))) char pbuf[kWide ? 4 * 2 * 64 * 16 : 16 * 128];
-  // Wide, sparse: index-list entries of the next tiles, copied in by each wave
-  // ([tile & 3][wave][64]), so that no register load waits behind a tile copy.
-  __shared__ __attribute__((aligned(256))) int idxbuf[kWide && SPARSE ? 4 : 1][4][64];
+  // Wide: index data of the next tiles (sparse: the 64 index-list entries;
+  // dense: the page id, in every entry), copied in by each wave ([tile & 3]
+  // [wave][64]) so that neither a register load left behind a tile copy nor a
+  // scalar round trip sits on the critical path of a step.
+  __shared__ __attribute__((aligned(256))) int idxbuf[kWide ? 4 : 1][4][64];
 
   // Worker and row tile of this workgroup.  Row tiles of one worker are placed
   // 8 workgroups apart so that they land on the same XCD (workgroups are
@@ -416,16 +418,23 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int j = 0; j < C::kLoads; ++j) issue_one(stage, off, j);
     };
-    // Wide, sparse: copy the 64 index-list entries of tile (item, blk) into ring
-    // slot `slot` (entries past topk repeat the last one; they are padding).
+    // Wide: copy the index data of tile (item, blk) into ring slot `slot`.
+    // Sparse: its 64 index-list entries (entries past topk repeat the last one;
+    // they are padding).  Dense: its page id.
     auto idx_dma = [&](int item, int blk, int slot) __attribute__((always_inline)) {
-      const int sl = min(blk * kPage + lane, a.topk - 1);
-      copy_to_lds_4(a.indices + (int64_t)item * a.topk + sl, lds_addr(&idxbuf[slot & 3][wave][0]));
+      const int32_t* src;
+      if constexpr (sparse) src = a.indices + (int64_t)item * a.topk + min(blk * kPage + lane, a.topk - 1);
+      else src = a.block_table + (int64_t)item * a.max_blocks + blk;
+      copy_to_lds_4(src, lds_addr(&idxbuf[slot & 3][wave][0]));
     };
     auto idx_from_lds = [&](int blk, int slot, TileRaw& raw) __attribute__((always_inline)) {
+      if constexpr (sparse) {
 #pragma unroll
-      for (int r = 0; r < C::kLaneRows; ++r)
-        raw.v[r] = blk * kPage + cp_row[r] < a.topk ? idxbuf[slot & 3][wave][cp_row[r]] : -1;
+        for (int r = 0; r < C::kLaneRows; ++r)
+          raw.v[r] = blk * kPage + cp_row[r] < a.topk ? idxbuf[slot & 3][wave][cp_row[r]] : -1;
+      } else {
+        raw.v[0] = idxbuf[slot & 3][wave][0];
+      }
     };
 
     int64_t off[C::kLaneRows];   // cache byte offsets of the rows this lane copies for the next tile issued
@@ -491,23 +500,31 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
         mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
         mx = xor32_max(xor16_max(mx));
       } else {
-        // S^T (32 keys x 32 rows) = K Q^T over 36 k-steps of 16.
+        // S^T (32 keys x 32 rows) = K Q^T over 36 k-steps of 16.  The loop is
+        // written twice so that issuing the next tile's copy inside it costs
+        // no branch per k-step.
         floatx16 sacc = {};
-        constexpr int kPre = 6;
-        bf16x8 kf[kPre];
+        auto qk = [&](auto with_dma) __attribute__((always_inline)) {
+          constexpr int kPre = 6;
+          bf16x8 kf[kPre];
 #pragma unroll
-        for (int ks = 0; ks < kPre; ++ks)
-          kf[ks] = *reinterpret_cast<const bf16x8*>(stage + k_base + ((ks >> 2) << 10) + k_x[ks & 3]);
+          for (int ks = 0; ks < kPre; ++ks)
+            kf[ks] = *reinterpret_cast<const bf16x8*>(stage + k_base + ((ks >> 2) << 10) + k_x[ks & 3]);
 #pragma unroll
-        for (int ks = 0; ks < 36; ++ks) {
-          const bf16x8 kcur = kf[ks % kPre];
-          if (ks + kPre < 36)
-            kf[ks % kPre] = *reinterpret_cast<const bf16x8*>(stage + k_base + (((ks + kPre) >> 2) << 10) +
-                                                             k_x[(ks + kPre) & 3]);
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur, qf[ks], sacc, 0, 0, 0);
-          if ((ks & 1) == 0 && dma_stage != nullptr) issue_one(dma_stage, off, ks >> 1);
-          __builtin_amdgcn_sched_barrier(0);   // keep the reads kPre MFMAs ahead
-        }
+          for (int ks = 0; ks < 36; ++ks) {
+            const bf16x8 kcur = kf[ks % kPre];
+            if (ks + kPre < 36)
+              kf[ks % kPre] = *reinterpret_cast<const bf16x8*>(stage + k_base + (((ks + kPre) >> 2) << 10) +
+                                                               k_x[(ks + kPre) & 3]);
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur, qf[ks], sacc, 0, 0, 0);
+            if constexpr (decltype(with_dma)::value) {
+              if ((ks & 1) == 0) issue_one(dma_stage, off, ks >> 1);
+            }
+            __builtin_amdgcn_sched_barrier(0);   // keep the reads kPre MFMAs ahead
+          }
+        };
+        if (dma_stage != nullptr) qk(std::true_type{});
+        else qk(std::false_type{});
         // element r: key 32 half + 8 (r / 4) + 4 hl + r % 4.  Tiles whose keys
         // are all valid for every row of the wave skip the per-key mask.
         const bool full = !sparse && __builtin_amdgcn_ballot_w64(blk * kPage + 32 * half + 32 <= lim) ==
@@ -739,7 +756,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     tile_finish(cur_item, cur_blk, raw, off, kvalid[0]);
     issue(s0, off);
     if constexpr (kWide) {
-      if (sparse && nx_item >= 0) idx_dma(nx_item, nx_blk, 1);   // tile 1's offsets are made in step 0
+      if (nx_item >= 0) idx_dma(nx_item, nx_blk, 1);   // tile 1's offsets are made in step 0
     } else if (nx_item >= 0) {
       tile_fetch(nx_item, nx_blk, raw);
       if constexpr (sparse) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
@@ -757,14 +774,13 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
       if constexpr (kWide) {
         // Tile t was requested during the previous step's QK^T (and, sparse,
         // the index list of tile t + 1 before it): nothing else is in flight.
-        if (!sparse && has_next) tile_fetch(nx_item, nx_blk, raw);   // scalar loads
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         barrier_keep_loads();          // tile t in LDS for every wave; every wave is done with `nxt`
         if (has_next) {
-          if constexpr (sparse) idx_from_lds(nx_blk, t + 1, raw);
+          idx_from_lds(nx_blk, t + 1, raw);
           tile_finish(nx_item, nx_blk, raw, off, kvalid[(t + 1) & 3]);
         }
-        if (sparse && n2_item >= 0) idx_dma(n2_item, n2_blk, t + 2);
+        if (n2_item >= 0) idx_dma(n2_item, n2_blk, t + 2);
         const bool ends = !has_next || nx_item != cur_item;
         compute(cur, kvalid[t & 3], cur_blk, cur_lim, has_next ? nxt : nullptr);
         if (ends) {
