@@ -171,40 +171,52 @@ __device__ __forceinline__ void barrier_keep_loads() {
   asm volatile("s_barrier" ::: "memory");
 }
 
-// o = 0, lse = -inf for rows [r0, r0 + nr) of an item with no key.
-__device__ void write_empty(const DecodeArgs& a, int item, int r0, int nr, int tid, int nthreads) {
-  for (int e = tid; e < nr * 64; e += nthreads) {
-    const int64_t orow = (int64_t)item * a.M + r0 + e / 64;
-    *reinterpret_cast<uint4*>(a.o + orow * kDv + (e & 63) * 8) = uint4{0, 0, 0, 0};
-    if ((e & 63) == 0) a.lse[orow] = -INFINITY;
-  }
+// o = 0, lse = -inf for row r of an item with no key (one wave, 8 columns per lane).
+__device__ __forceinline__ void write_empty_row(const DecodeArgs& a, int item, int r, int lane) {
+  const int64_t orow = (int64_t)item * a.M + r;
+  *reinterpret_cast<uint4*>(a.o + orow * kDv + 8 * lane) = uint4{0, 0, 0, 0};
+  if (lane == 0) a.lse[orow] = -INFINITY;
 }
 
-// Log-sum-exp merge of the n partials of rows [r0, r0 + nr) of an item.
-__device__ void merge_rows(const DecodeArgs& a, int item, int slot0, int n, int r0, int nr, int tid,
-                           int nthreads) {
-  for (int e = tid; e < nr * 64; e += nthreads) {
-    const int r = r0 + e / 64;
-    const int c8 = (e & 63) * 8;
-    const int64_t orow = (int64_t)item * a.M + r;
+// Log-sum-exp merge of the n partials of row r of an item, one wave per row,
+// 8 columns per lane.  The partial LSEs are read lane-parallel for the max;
+// the weighted sum of the partial rows keeps 4 reads in flight.
+__device__ __forceinline__ void merge_row(const DecodeArgs& a, int item, int slot0, int n, int r, int lane) {
+  const int64_t orow = (int64_t)item * a.M + r;
+  if (n <= 8) {
+    // all reads in one go (one memory latency), then the arithmetic
+    float lk[8];
+    floatx4 v0[8], v1[8];
+    const int64_t stride = (int64_t)a.M * kDv;
+    const float* o_col = a.part_o + ((int64_t)slot0 * a.M + r) * kDv + 8 * lane;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (k < n) {
+        lk[k] = a.part_lse[(int64_t)(slot0 + k) * a.M + r];
+        const floatx4* src = reinterpret_cast<const floatx4*>(o_col + k * stride);
+        v0[k] = src[0];
+        v1[k] = src[1];
+      }
+    }
     float mx = -INFINITY;
-    for (int k = 0; k < n; ++k) mx = fmaxf(mx, a.part_lse[(int64_t)(slot0 + k) * a.M + r]);
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (k < n) mx = fmaxf(mx, lk[k]);
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
     float tot = 0.f;
     if (mx != -INFINITY) {
-      for (int k = 0; k < n; ++k) {
-        const int64_t prow = (int64_t)(slot0 + k) * a.M + r;
-        const float lk = a.part_lse[prow];
-        const float wk = lk == -INFINITY ? 0.f : expf(lk - mx);
-        tot += wk;
-        const floatx4* src = reinterpret_cast<const floatx4*>(a.part_o + prow * kDv + c8);
-        const floatx4 v0 = src[0], v1 = src[1];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[i] += wk * v0[i];
-          acc[4 + i] += wk * v1[i];
+      for (int k = 0; k < 8; ++k) {
+        if (k < n) {
+          const float wk = lk[k] == -INFINITY ? 0.f : expf(lk[k] - mx);
+          tot += wk;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[i] += wk * v0[k][i];
+            acc[4 + i] += wk * v1[k][i];
+          }
         }
       }
     }
@@ -212,9 +224,42 @@ __device__ void merge_rows(const DecodeArgs& a, int item, int slot0, int n, int 
     bf16x8 v;
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = (__bf16)(acc[i] * inv);
-    *reinterpret_cast<bf16x8*>(a.o + orow * kDv + c8) = v;
-    if ((e & 63) == 0) a.lse[orow] = tot > 0.f ? mx + logf(tot) : -INFINITY;
+    *reinterpret_cast<bf16x8*>(a.o + orow * kDv + 8 * lane) = v;
+    if (lane == 0) a.lse[orow] = tot > 0.f ? mx + logf(tot) : -INFINITY;
+    return;
   }
+  float mx = -INFINITY;
+  for (int k = lane; k < n; k += 64) mx = fmaxf(mx, a.part_lse[(int64_t)(slot0 + k) * a.M + r]);
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d, 64));
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  float tot = 0.f;
+  if (mx != -INFINITY) {
+    const float* lse_col = a.part_lse + (int64_t)slot0 * a.M + r;
+    const float* o_col = a.part_o + ((int64_t)slot0 * a.M + r) * kDv + 8 * lane;
+    const int64_t stride = (int64_t)a.M * kDv;
+#pragma unroll 4
+    for (int k = 0; k < n; ++k) {
+      const float lk = lse_col[(int64_t)k * a.M];
+      const float wk = lk == -INFINITY ? 0.f : expf(lk - mx);
+      tot += wk;
+      const floatx4* src = reinterpret_cast<const floatx4*>(o_col + k * stride);
+      const floatx4 v0 = src[0], v1 = src[1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[i] += wk * v0[i];
+        acc[4 + i] += wk * v1[i];
+      }
+    }
+  }
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  bf16x8 v;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (__bf16)(acc[i] * inv);
+  *reinterpret_cast<bf16x8*>(a.o + orow * kDv + 8 * lane) = v;
+  if (lane == 0) a.lse[orow] = tot > 0.f ? mx + logf(tot) : -INFINITY;
 }
 
 template <int V, bool SPARSE>
@@ -846,16 +891,16 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
 }
 
 // Merge of the partial results of items split over several workers, and the
-// empty result of items with no key (the unfused path).
+// empty result of items with no key (the unfused path).  One wave per row.
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   const int item = blockIdx.x;
   const int slot0 = a.num_splits[item];
   const int n = a.num_splits[item + 1] - slot0;
   if (n == 1) return;
-  for (int rr = blockIdx.y * 4; rr < a.M; rr += 4 * gridDim.y) {
-    const int nrr = min(4, a.M - rr);
-    if (n == 0) write_empty(a, item, rr, nrr, threadIdx.x, 256);
-    else merge_rows(a, item, slot0, n, rr, nrr, threadIdx.x, 256);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int r = blockIdx.y * 4 + wave; r < a.M; r += 4 * gridDim.y) {
+    if (n == 0) write_empty_row(a, item, r, lane);
+    else merge_row(a, item, slot0, n, r, lane);
   }
 }
 
