@@ -43,13 +43,15 @@ NCOPIES = 4
 
 
 def algorithmic_work(w):
-    """KV bytes (each key row once) and FLOPs (2 * (576 + 512) per query row and key)."""
+    """KV bytes (each key row of each latent head once) and FLOPs (2 * (576 + 512)
+    per query row and key)."""
     L = w.cache_seqlens.astype(np.int64)
+    h_kv = w.kv.shape[2]
     if w.indices is not None:
         ok = (w.indices >= 0) & (w.indices < L[:, None, None])
         keys = int(ok.sum())
-        return keys * KV_ROW_BYTES, keys * w.h_q * 2 * (576 + 512)
-    kv = int(L.sum()) * KV_ROW_BYTES
+        return keys * h_kv * KV_ROW_BYTES, keys * w.h_q * 2 * (576 + 512)
+    kv = int(L.sum()) * h_kv * KV_ROW_BYTES
     if w.causal:
         qk = sum(w.h_q * max(int(l) - w.s_q + s + 1, 0) for l in L for s in range(w.s_q))
     else:
@@ -82,20 +84,21 @@ def run_workload(torch, m, w, steps, warmup, ncopies=NCOPIES):
     idx = _to_dev(torch, w.indices.astype(np.int32)) if w.indices is not None else None
     qs = [q0] + [q0.clone() for _ in range(ncopies - 1)]
     kvs = [kv0] + [kv0.clone() for _ in range(ncopies - 1)]
-    rows = w.s_q * w.h_q
-    plan, ns = m.get_mla_metadata(sl, rows, 1, s_q=w.s_q, topk=w.topk)
+    h_kv = w.kv.shape[2]
+    rows = w.s_q * w.h_q // h_kv
+    plan, ns = m.get_mla_metadata(sl, rows, h_kv, s_q=w.s_q, topk=w.topk)
     W = plan.numel() // 8 - 1
     B = w.B
     o = torch.empty((B, w.s_q, w.h_q, 512), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((B, w.s_q, w.h_q), dtype=torch.float32, device="cuda")
-    ws_bytes = m.workspace_bytes(B, w.s_q, rows, 1, w.topk or 0, 512, W)
+    ws_bytes = m.workspace_bytes(B, w.s_q, rows, h_kv, w.topk or 0, 512, W)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
 
     def step(k, ev=None):
         c = k % ncopies
         if ev is not None:
             ev[0].record()
-        p, n = m.get_mla_metadata(sl, rows, 1, s_q=w.s_q, topk=w.topk)
+        p, n = m.get_mla_metadata(sl, rows, h_kv, s_q=w.s_q, topk=w.topk)
         if ev is not None:
             ev[1].record()
         m.mla_decode_with_kvcache(qs[c], kvs[c], bt, sl, 512, p, n, causal=w.causal, indices=idx,
@@ -197,10 +200,11 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="memory_bound",
-                    choices=["tiny", "memory_bound", "near_ridge", "mtp_causal", "sparse_topk"])
+                    choices=["tiny", "memory_bound", "near_ridge", "mtp_causal", "sparse_topk",
+                             "grouped_heads"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--secondary", action="store_true",
-                    help="also time the near-ridge, MTP-causal and sparse top-k workloads")
+                    help="also time the near-ridge, MTP-causal, sparse top-k and grouped-heads workloads")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run plain device copies of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -238,7 +242,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name, "batch": w.B, "s_q": w.s_q, "h_q": w.h_q, "h_kv": 1,
+        "config": {"workload": w.name, "batch": w.B, "s_q": w.s_q, "h_q": w.h_q, "h_kv": int(w.kv.shape[2]),
                    "d_qk": 576, "dv": 512, "page": 64, "causal": bool(w.causal),
                    "topk": w.topk, "kv_bytes": kv_bytes, "flops": flops,
                    "num_workers": r["num_workers"], "kv_copies_rotated": NCOPIES},
@@ -254,7 +258,7 @@ def main():
     }
     if args.secondary:
         sec = {}
-        for name in ("near_ridge", "mtp_causal", "sparse_topk"):
+        for name in ("near_ridge", "mtp_causal", "sparse_topk", "grouped_heads"):
             w2 = wl.NAMED[name]()
             kb, fl = algorithmic_work(w2)
             r2 = run_workload(torch, m, w2, max(10, args.steps // 2), 3)

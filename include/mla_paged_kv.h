@@ -35,7 +35,10 @@
  *   indices      [batch, s_q, topk]             int32, device (sparse mode only)
  *   o            [batch, s_q, h_q, dv]          bf16, device (output)
  *   lse          [batch, s_q, h_q]              fp32, device (output)
- * Supported: d_qk = 576, dv = 512, page size 64, h_kv = 1.
+ * Supported: d_qk = 576, dv = 512, page size 64, any h_kv dividing h_q.  With
+ * h_kv > 1 latent heads (grouped latent attention), query head h uses KV head
+ * h / (h_q / h_kv); row (page * 64 + slot) of head g sits at element offset
+ * ((page * 64 + slot) * h_kv + g) * d_qk of kvcache.
  */
 #ifndef MLA_PAGED_KV_H_
 #define MLA_PAGED_KV_H_
@@ -66,11 +69,12 @@ const char* mla_status_string(int status);
  * mla_plan_dims — host only; sizes the metadata call's outputs.
  *
  * The work of one decode call is a list of items.  Dense mode (topk <= 0):
- * one item per sequence, of length cache_seqlens[b], with num_q_rows =
- * s_q * h_q / h_kv query rows sharing it (the pages' second argument of the
- * metadata call).  Sparse mode (topk > 0): one item per query token
- * (batch * s_q items) whose keys are the topk entries of indices[b, s, :],
- * with num_q_rows / s_q rows each.
+ * one item per (sequence, KV head), item = b * h_kv + g, of length
+ * cache_seqlens[b], with num_q_rows = s_q * h_q / h_kv query rows sharing it
+ * (the pages' second argument of the metadata call).  Sparse mode (topk > 0):
+ * one item per (query token, KV head), item = (b * s_q + s) * h_kv + g, whose
+ * keys are the topk entries of indices[b, s, :], with num_q_rows / s_q rows
+ * each.
  *
  *   num_workers_request  0 = let the library choose (CU count and the decode
  *                        variant picked for this row count); > 0 forces it
@@ -102,7 +106,8 @@ int mla_plan_num_workers(int plan_words, int batch, int s_q, int num_q_rows, int
  *
  *   cache_seqlens  [batch] int32, device (read in sparse mode as well: index
  *                  entries outside [0, L_b) are padding)
- * Rule: item i has n_i = ceil(len_i / 64) blocks and costs overhead + n_i
+ * Rule: item i has n_i = ceil(len_i / 64) blocks (len_i = cache_seqlens[i / h_kv]
+ * dense, topk sparse) and costs overhead + n_i
  * units; items are laid end to end on a cost axis (total T); the first
  * W' = min(W, T) workers share it evenly, worker w owning the units
  * [floor(w T / W'), floor((w + 1) T / W')); block b of item i sits on unit

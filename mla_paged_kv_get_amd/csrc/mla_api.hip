@@ -41,15 +41,17 @@ struct Shape {
 
 int shape_of(int batch, int s_q, int num_q_rows, int h_kv, int topk, Shape* s) {
   if (batch < 0 || s_q < 1 || num_q_rows < 1 || h_kv < 1) return MLA_ERR_INVALID_ARGUMENT;
-  if (h_kv != 1) return MLA_ERR_UNSUPPORTED;
+  // Items: (sequence, KV head) in dense mode, (query token, KV head) in sparse mode.
   if (topk > 0) {
     if (num_q_rows % s_q) return MLA_ERR_INVALID_ARGUMENT;
-    const int64_t items = (int64_t)batch * s_q;
+    const int64_t items = (int64_t)batch * s_q * h_kv;
     if (items > (1 << 30)) return MLA_ERR_INVALID_ARGUMENT;
     s->items = (int)items;
     s->rows = num_q_rows / s_q;
   } else {
-    s->items = batch;
+    const int64_t items = (int64_t)batch * h_kv;
+    if (items > (1 << 30)) return MLA_ERR_INVALID_ARGUMENT;
+    s->items = (int)items;
     s->rows = num_q_rows;
   }
   s->variant = pick_variant(s->rows);
@@ -85,7 +87,7 @@ const char* mla_status_string(int status) {
   switch (status) {
     case MLA_OK: return "ok";
     case MLA_ERR_INVALID_ARGUMENT: return "invalid argument";
-    case MLA_ERR_UNSUPPORTED: return "unsupported shape (needs d_qk=576, dv=512, page 64, h_kv=1)";
+    case MLA_ERR_UNSUPPORTED: return "unsupported shape (needs d_qk=576, dv=512, page 64)";
     case MLA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case MLA_ERR_HIP: return "HIP runtime error";
     default: return "unknown status";
@@ -126,7 +128,7 @@ int mla_get_metadata(const int32_t* cache_seqlens, int batch, int s_q, int num_q
   if (st != MLA_OK) return st;
   if (s.items > mla::plan_max_items()) return MLA_ERR_UNSUPPORTED;
   const int overhead = variant_overhead(s.variant);
-  const hipError_t e = launch_plan(cache_seqlens, topk > 0 ? topk : 0, s.items, num_workers,
+  const hipError_t e = launch_plan(cache_seqlens, topk > 0 ? topk : 0, s.items, h_kv, num_workers,
                                    overhead, plan, num_splits,
                                    reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
@@ -152,7 +154,7 @@ int mla_decode_with_kvcache_phase(const void* q, const void* kvcache, int64_t nu
   if (batch < 0 || s_q < 1 || h_q < 1 || h_kv < 1 || max_blocks < 1 || num_pages < 1)
     return MLA_ERR_INVALID_ARGUMENT;
   if (h_q % h_kv) return MLA_ERR_INVALID_ARGUMENT;
-  if (page_size != kPage || d_qk != kDqk || dv != kDv || h_kv != 1) return MLA_ERR_UNSUPPORTED;
+  if (page_size != kPage || d_qk != kDqk || dv != kDv) return MLA_ERR_UNSUPPORTED;
   if (causal != 0 && causal != 1) return MLA_ERR_INVALID_ARGUMENT;
   if ((indices != nullptr) != (topk > 0)) return MLA_ERR_INVALID_ARGUMENT;
   if (indices && causal) return MLA_ERR_INVALID_ARGUMENT;
@@ -195,6 +197,8 @@ int mla_decode_with_kvcache_phase(const void* q, const void* kvcache, int64_t nu
   a.topk = topk > 0 ? topk : 0;
   a.causal = causal;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.h_kv = h_kv;
+  a.G = h_q / h_kv;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   if (phases & 1) {
     if (launch_decode(a, s.variant, hs) != hipSuccess) return MLA_ERR_HIP;

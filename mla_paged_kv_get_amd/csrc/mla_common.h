@@ -62,10 +62,26 @@ struct DecodeArgs {
   int topk;                   // 0 = dense
   int causal;
   float scale_log2;           // softmax_scale * log2(e)
+  int h_kv;                   // latent KV heads (items are (sequence or query token, KV head))
+  int G;                      // query heads per KV head, h_q / h_kv
 };
 
+// Row of q / o / lse ([batch * s_q * h_q] rows) holding query row `row` of
+// work item `item`.  Dense: item = b * h_kv + g, row = s * G + j -> token
+// (b, s), head g * G + j.  Sparse: item = (b * s_q + s) * h_kv + g, row = j.
+__device__ __forceinline__ int64_t q_row(const DecodeArgs& a, int item, int row) {
+  const int tok_or_b = item / a.h_kv, g = item - tok_or_b * a.h_kv;
+  if (a.topk > 0) return (int64_t)tok_or_b * (a.h_kv * a.G) + g * a.G + row;
+  const int s = row / a.G, j = row - s * a.G;
+  return ((int64_t)tok_or_b * a.s_q + s) * (a.h_kv * a.G) + g * a.G + j;
+}
+// Sequence (block-table row, length) of work item `item`.
+__device__ __forceinline__ int item_seq(const DecodeArgs& a, int item) {
+  return a.topk > 0 ? item / (a.h_kv * a.s_q) : item / a.h_kv;
+}
+
 // Launchers (defined next to their kernels).
-hipError_t launch_plan(const int32_t* seqlens, int topk, int num_items, int num_workers,
+hipError_t launch_plan(const int32_t* seqlens, int topk, int num_items, int item_div, int num_workers,
                        int overhead, int32_t* plan, int32_t* num_splits, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int variant, hipStream_t stream);
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream);

@@ -173,7 +173,7 @@ __device__ __forceinline__ void barrier_keep_loads() {
 
 // o = 0, lse = -inf for row r of an item with no key (one wave, 8 columns per lane).
 __device__ __forceinline__ void write_empty_row(const DecodeArgs& a, int item, int r, int lane) {
-  const int64_t orow = (int64_t)item * a.M + r;
+  const int64_t orow = q_row(a, item, r);
   *reinterpret_cast<uint4*>(a.o + orow * kDv + 8 * lane) = uint4{0, 0, 0, 0};
   if (lane == 0) a.lse[orow] = -INFINITY;
 }
@@ -182,7 +182,7 @@ __device__ __forceinline__ void write_empty_row(const DecodeArgs& a, int item, i
 // 8 columns per lane.  The partial LSEs are read lane-parallel for the max;
 // the weighted sum of the partial rows keeps 4 reads in flight.
 __device__ __forceinline__ void merge_row(const DecodeArgs& a, int item, int slot0, int n, int r, int lane) {
-  const int64_t orow = (int64_t)item * a.M + r;
+  const int64_t orow = q_row(a, item, r);
   if (n <= 8) {
     // all reads in one go (one memory latency), then the arithmetic
     float lk[8];
@@ -373,12 +373,12 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     int lens_v = 0;
     if (lane <= it_last - it_first) {
       const int x = it_first + lane;
-      lens_v = a.seqlens[sparse ? x / a.s_q : x];
+      lens_v = a.seqlens[item_seq(a, x)];
     }
     auto item_len = [&](int x) __attribute__((always_inline)) -> int {      // x is wave-uniform
       const int j = x - it_first;
       if (j < 64) return __builtin_amdgcn_readlane(lens_v, j);
-      return read_scalar(a.seqlens + (sparse ? x / a.s_q : x));
+      return read_scalar(a.seqlens + item_seq(a, x));
     };
     auto seg_hi = [&](int x) __attribute__((always_inline)) -> int {         // end block of this worker's run in item x
       if (x == it_last) return blk_end;
@@ -418,9 +418,9 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     };
     auto tile_fetch = [&](int item, int blk, TileRaw& raw) __attribute__((always_inline)) {
       if constexpr (!sparse) {
-        raw.v[0] = read_scalar(a.block_table + (int64_t)item * a.max_blocks + blk);   // not a vector load
+        raw.v[0] = read_scalar(a.block_table + (int64_t)item_seq(a, item) * a.max_blocks + blk);   // not a vector load
       } else {
-        const int32_t* idx_row = a.indices + (int64_t)item * a.topk;
+        const int32_t* idx_row = a.indices + (int64_t)(item / a.h_kv) * a.topk;
 #pragma unroll
         for (int r = 0; r < C::kLaneRows; ++r) {
           const int sl = blk * kPage + cp_row[r];
@@ -431,23 +431,24 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     auto tile_finish = [&](int item, int blk, const TileRaw& raw, int64_t (&off)[C::kLaneRows],
                            unsigned char* vslot) __attribute__((always_inline)) {
       const int L = item_len(item);
+      const int kvh = item % a.h_kv;      // latent KV head of the item
       if constexpr (!sparse) {
         const int64_t page = raw.v[0];
         const int nvalid = min(kPage, L - blk * kPage);
 #pragma unroll
         for (int r = 0; r < C::kLaneRows; ++r) {
           const int t = min(cp_row[r], nvalid - 1);
-          off[r] = (page * kPage + t) * (int64_t)kRowBytes;
+          off[r] = ((page * kPage + t) * a.h_kv + kvh) * (int64_t)kRowBytes;
         }
       } else {
-        const int32_t* bt_row = a.block_table + (int64_t)(item / a.s_q) * a.max_blocks;
+        const int32_t* bt_row = a.block_table + (int64_t)item_seq(a, item) * a.max_blocks;
 #pragma unroll
         for (int r = 0; r < C::kLaneRows; ++r) {
           const int idx = raw.v[r];
           const bool ok = sparse_key_valid(idx, L);
           // padding reads the sequence's first row (page 0 of the pool if it has none)
-          off[r] = ok ? cache_row(bt_row, idx) * (int64_t)kRowBytes
-                      : (L > 0 ? cache_row(bt_row, 0) * (int64_t)kRowBytes : 0);
+          const int64_t crow = ok ? cache_row(bt_row, idx) : (L > 0 ? cache_row(bt_row, 0) : 0);
+          off[r] = (crow * a.h_kv + kvh) * (int64_t)kRowBytes;
           if ((lane & 7) == 0) vslot[cp_row[r]] = ok ? 1 : 0;
         }
       }
@@ -468,8 +469,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     // they are padding).  Dense: its page id.
     auto idx_dma = [&](int item, int blk, int slot) __attribute__((always_inline)) {
       const int32_t* src;
-      if constexpr (sparse) src = a.indices + (int64_t)item * a.topk + min(blk * kPage + lane, a.topk - 1);
-      else src = a.block_table + (int64_t)item * a.max_blocks + blk;
+      if constexpr (sparse) src = a.indices + (int64_t)(item / a.h_kv) * a.topk + min(blk * kPage + lane, a.topk - 1);
+      else src = a.block_table + (int64_t)item_seq(a, item) * a.max_blocks + blk;
       copy_to_lds_4(src, lds_addr(&idxbuf[slot & 3][wave][0]));
     };
     auto idx_from_lds = [&](int blk, int slot, TileRaw& raw) __attribute__((always_inline)) {
@@ -494,7 +495,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     // Rows past M borrow row 0's values (their scores are masked to -inf), so
     // no select on the loaded data forces an early wait on the loads.
     auto load_q = [&](int item) __attribute__((always_inline)) {
-      const uint16_t* qrow = a.q + ((int64_t)item * a.M + (row_ok ? row : 0)) * kDqk;
+      const uint16_t* qrow = a.q + q_row(a, item, row_ok ? row : 0) * kDqk;
 #pragma unroll
       for (int ks = 0; ks < C::kQf; ++ks)
         qf[ks] = kWide ? *reinterpret_cast<const bf16x8*>(qrow + 16 * ks + 8 * hl)
@@ -503,7 +504,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     auto key_limit = [&](int item) __attribute__((always_inline)) -> int {   // dense: keys of this lane's row are < limit
       const int L = item_len(item);
       if (!row_ok) return 0;
-      return (!sparse && a.causal) ? L - a.s_q + row / a.h_q + 1 : L;
+      return (!sparse && a.causal) ? L - a.s_q + row / a.G + 1 : L;
     };
     auto rescale = [&](float m_new) __attribute__((always_inline)) {
       const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_ref - m_new);
@@ -723,7 +724,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
       const int slot0 = read_scalar(a.num_splits + item);
       const int nsplit = read_scalar(a.num_splits + item + 1) - slot0;
       const bool final_out = nsplit == 1;
-      const int64_t orow_base = final_out ? (int64_t)item * a.M : (int64_t)(slot0 + split) * a.M;
+      const int64_t part_base = (int64_t)(slot0 + split) * a.M;
       // row sums over the lanes and waves holding the row (same order everywhere)
       float l_tot = l_lane;
       if constexpr (!kWide) l_tot = xor16_sum(l_tot);
@@ -739,7 +740,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
       }
       if (row_ok) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        const int64_t orow = orow_base + row;
+        const int64_t orow = final_out ? q_row(a, item, row) : part_base + row;
         // element (d, i) of the lane: column c0 + 16 d + 4 g + i (rows16),
         // c0 + 32 d + 8 (i / 4) + 4 hl + i % 4 (wide)
         const int c0 = kWide ? 256 * half + 4 * hl : 128 * tg + 4 * g;
@@ -789,7 +790,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     // first copy is issued: a tracked load still pending behind a copy would
     // make its first use wait for the copy as well.
     TileRaw raw;
-    if constexpr (!sparse) raw.v[0] = a.block_table[(int64_t)cur_item * a.max_blocks + cur_blk];
+    if constexpr (!sparse) raw.v[0] = a.block_table[(int64_t)item_seq(a, cur_item) * a.max_blocks + cur_blk];
     else tile_fetch(cur_item, cur_blk, raw);
     load_q(cur_item);
     int cur_hi = seg_hi(cur_item);

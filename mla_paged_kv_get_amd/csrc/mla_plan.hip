@@ -44,13 +44,16 @@ __device__ int block_inclusive_scan(int v, int* wave_sums) {
   return v + before;
 }
 
-__device__ __forceinline__ int item_blocks(const int32_t* seqlens, int topk, int i) {
-  const int len = topk > 0 ? topk : seqlens[i];
+// Blocks of item i: topk keys (sparse) or the length of its sequence i / item_div
+// (dense; item_div = number of KV heads, items being (sequence, KV head)).
+__device__ __forceinline__ int item_blocks(const int32_t* seqlens, int topk, int item_div, int i) {
+  const int len = topk > 0 ? topk : seqlens[i / item_div];
   return len > 0 ? (len + kPage - 1) / kPage : 0;
 }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ seqlens,
-                                                            int topk, int num_items, int W, int c,
+                                                            int topk, int num_items, int item_div,
+                                                            int W, int c,
                                                             int32_t* __restrict__ plan,
                                                             int32_t* __restrict__ num_splits) {
   __shared__ int start[kPlanMaxItems + 1];
@@ -61,12 +64,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
 
   // Start of every item on the cost axis.
   int local = 0;
-  for (int i = i0; i < i1; ++i) local += c + item_blocks(seqlens, topk, i);
+  for (int i = i0; i < i1; ++i) local += c + item_blocks(seqlens, topk, item_div, i);
   const int incl = block_inclusive_scan(local, wave_sums);
   int run = incl - local;
   for (int i = i0; i < i1; ++i) {
     start[i] = run;
-    run += c + item_blocks(seqlens, topk, i);
+    run += c + item_blocks(seqlens, topk, item_div, i);
   }
   if (tid == kPlanThreads - 1) start[num_items] = incl;
   __syncthreads();
@@ -158,10 +161,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
 
 int plan_max_items() { return kPlanMaxItems; }
 
-hipError_t launch_plan(const int32_t* seqlens, int topk, int num_items, int num_workers,
+hipError_t launch_plan(const int32_t* seqlens, int topk, int num_items, int item_div, int num_workers,
                        int overhead, int32_t* plan, int32_t* num_splits, hipStream_t stream) {
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, seqlens, topk, num_items,
-                     num_workers, overhead, plan, num_splits);
+                     item_div, num_workers, overhead, plan, num_splits);
   return hipGetLastError();
 }
 

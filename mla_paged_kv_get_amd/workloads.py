@@ -166,10 +166,20 @@ def sparse_topk(poison: bool = False, B: int = 16) -> Workload:
                  num_pages=B * 1024, max_blocks=1024, topk=2048, poison=poison, rng=rng)
 
 
+def grouped_heads(poison: bool = False) -> Workload:
+    """b=32, s_q=1, h_q=128 over h_kv=8 latent heads (16 query heads each),
+    lengths uniform in [1, 4096], 1200-page pool."""
+    rng = np.random.default_rng(6)
+    lengths = rng.integers(1, 4097, size=32)
+    return build("grouped-heads b32 h128 hkv8 L~U[1,4096]", 6, lengths, B=32, s_q=1, h_q=128, h_kv=8,
+                 num_pages=1200, max_blocks=64, poison=poison, rng=rng)
+
+
 NAMED = {
     "tiny": tiny,
     "memory_bound": memory_bound,
     "near_ridge": near_ridge,
     "mtp_causal": mtp_causal,
     "sparse_topk": sparse_topk,
+    "grouped_heads": grouped_heads,
 }

@@ -287,11 +287,11 @@ def decode_by_plan(q_bits, kv_bits, block_table, cache_seqlens, dv, plan_words,
 # Work accounting used by the benchmark (algorithmic bytes and flops)
 # --------------------------------------------------------------------------
 def work(cache_seqlens, s_q: int, h_q: int, causal: bool, d_qk: int = D_QK, dv: int = D_V,
-         topk: int | None = None, indices=None):
+         topk: int | None = None, indices=None, h_kv: int = 1):
     """(KV bytes read once per key, FLOPs) of one decode call.
 
-    KV bytes count each (sequence, key) row once at 2 bytes per value; FLOPs
-    are 2 * (d_qk + dv) per (query row, key).
+    KV bytes count each (sequence, key, latent head) row once at 2 bytes per
+    value; FLOPs are 2 * (d_qk + dv) per (query row, key).
     """
     if indices is not None:
         idx = np.asarray(indices)
@@ -306,7 +306,7 @@ def work(cache_seqlens, s_q: int, h_q: int, causal: bool, d_qk: int = D_QK, dv: 
             kv_rows += L
             for s in range(s_q):
                 qk += h_q * (max(L - s_q + s + 1, 0) if causal else L)
-    return int(kv_rows) * d_qk * 2, int(qk) * 2 * (d_qk + dv)
+    return int(kv_rows) * h_kv * d_qk * 2, int(qk) * 2 * (d_qk + dv)
 
 
 def bf16_round_f64(x: np.ndarray) -> np.ndarray:

@@ -34,7 +34,9 @@ def run_gpu(d: Dev, num_workers=None, plan=None, softmax_scale=None):
     import mla_paged_kv_get_amd as m
     w = d.w
     if plan is None:
-        plan = m.get_mla_metadata(d.sl, w.s_q * w.h_q, 1, s_q=w.s_q, topk=w.topk, num_workers=num_workers)
+        h_kv = w.kv.shape[2]
+        plan = m.get_mla_metadata(d.sl, w.s_q * w.h_q // h_kv, h_kv, s_q=w.s_q, topk=w.topk,
+                                  num_workers=num_workers)
     o, lse = m.mla_decode_with_kvcache(d.q, d.kv, d.bt, d.sl, 512, plan[0], plan[1], causal=w.causal,
                                        softmax_scale=softmax_scale, indices=d.idx)
     torch.cuda.synchronize()

@@ -54,7 +54,8 @@ def test_plan_dims():
     assert _dims(64, 1, 16, 1, 0, 256) == (0, 256, 8 * 257, 64)
     assert _dims(16, 8, 8 * 128, 1, 2048, 100) == (0, 100, 8 * 101, 128)       # sparse: items = b * s_q
     assert _dims(32, 2, 256, 1, 0, 128) == (0, 128, 8 * 129, 32)
-    assert _dims(4, 1, 16, 2, 0, 8)[0] == _lib.MLA_ERR_UNSUPPORTED              # h_kv = 2
+    assert _dims(4, 1, 16, 2, 0, 8) == (0, 8, 8 * 9, 8)                         # h_kv = 2: items = b * h_kv
+    assert _dims(4, 2, 2 * 16, 4, 64, 8) == (0, 8, 8 * 9, 32)                  # sparse: items = b * s_q * h_kv
     assert _dims(4, 3, 16, 1, 64, 8)[0] == _lib.MLA_ERR_INVALID_ARGUMENT        # rows not a multiple of s_q
     assert _dims(-1, 1, 16, 1, 0, 8)[0] == _lib.MLA_ERR_INVALID_ARGUMENT
     assert _dims(4, 1, 16, 1, 0, -3)[0] == _lib.MLA_ERR_INVALID_ARGUMENT
@@ -65,6 +66,7 @@ def test_workspace_bytes():
     assert l.mla_workspace_bytes(64, 1, 16, 1, 0, 512, 256) == (64 + 256) * 16 * 513 * 4
     assert l.mla_workspace_bytes(16, 8, 1024, 1, 2048, 512, 256) == (128 + 256) * 128 * 513 * 4
     assert l.mla_workspace_bytes(64, 1, 16, 1, 0, 512, 0) == 0
+    assert l.mla_workspace_bytes(8, 1, 32, 4, 0, 512, 64) == (32 + 64) * 32 * 513 * 4   # h_kv = 4
 
 
 DUMMY = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails its host checks
@@ -82,7 +84,7 @@ def _decode(**kw):
     (dict(d=512), _lib.MLA_ERR_UNSUPPORTED),
     (dict(dv=256), _lib.MLA_ERR_UNSUPPORTED),
     (dict(page=32), _lib.MLA_ERR_UNSUPPORTED),
-    (dict(h_kv=2, h_q=16), _lib.MLA_ERR_UNSUPPORTED),
+    (dict(h_kv=2, h_q=16, ws_bytes=100), _lib.MLA_ERR_WORKSPACE_TOO_SMALL),    # h_kv = 2 is accepted
     (dict(h_q=15, h_kv=2), _lib.MLA_ERR_INVALID_ARGUMENT),
     (dict(q=None), _lib.MLA_ERR_INVALID_ARGUMENT),
     (dict(o=None), _lib.MLA_ERR_INVALID_ARGUMENT),
@@ -117,7 +119,8 @@ def test_metadata_rejects():
     l = _lib.lib()
     assert l.mla_get_metadata(DUMMY, 4, 1, 16, 1, 0, 8, None, DUMMY, None) == _lib.MLA_ERR_INVALID_ARGUMENT
     assert l.mla_get_metadata(DUMMY, 4, 1, 16, 1, 0, 0, DUMMY, DUMMY, None) == _lib.MLA_ERR_INVALID_ARGUMENT
-    assert l.mla_get_metadata(DUMMY, 4, 1, 16, 2, 0, 8, DUMMY, DUMMY, None) == _lib.MLA_ERR_UNSUPPORTED
+    assert l.mla_get_metadata(DUMMY, 4, 1, 16, 0, 0, 8, DUMMY, DUMMY, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert l.mla_get_metadata(DUMMY, 10000, 1, 16, 2, 0, 8, DUMMY, DUMMY, None) == _lib.MLA_ERR_UNSUPPORTED
     assert l.mla_get_metadata(None, 4, 1, 16, 1, 0, 8, DUMMY, DUMMY, None) == _lib.MLA_ERR_INVALID_ARGUMENT
     assert l.mla_get_metadata(DUMMY, 20000, 1, 16, 1, 0, 8, DUMMY, DUMMY, None) == _lib.MLA_ERR_UNSUPPORTED
 

@@ -160,6 +160,53 @@ def test_sparse_pads_and_empty():
     assert (o[1, 1].float().cpu().numpy() == 0).all()
 
 
+# ---------------------------------------------------------------------------
+# Several latent heads (h_kv > 1): query head h reads latent head h // (h_q / h_kv)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("h_kv,h_q,s_q,causal", [
+    (2, 16, 1, False),      # 8 rows per item: 16-row tiles
+    (4, 64, 2, True),       # 32 rows per item: 64-row tiles, causal
+    (2, 256, 1, False),     # 128 rows per item: two 64-row tiles
+    (8, 64, 4, True),       # 32 rows per item from four tokens of 8 heads
+])
+def test_grouped_latent_heads(h_kv, h_q, s_q, causal):
+    L = [1, 64, 65, 300, 0, 2049]
+    w = wl.build("grouped", 40 + h_kv, np.array(L), B=len(L), s_q=s_q, h_q=h_q, h_kv=h_kv,
+                 num_pages=60, causal=causal, poison=True)
+    o, lse, _ = run_gpu(Dev(w))
+    compare(w, o, lse, label=f"h_kv={h_kv} h_q={h_q} s_q={s_q} causal={causal}")
+    o2, lse2, _ = run_gpu(Dev(w), num_workers=3)
+    compare(w, o2, lse2, label=f"h_kv={h_kv} W=3")
+
+
+def test_grouped_heads_workload_full():
+    w = wl.grouped_heads()
+    o, lse, _ = run_gpu(Dev(w))
+    compare(w, o, lse, label="grouped-heads b32 h128 hkv8")
+
+
+@pytest.mark.parametrize("h_kv,h_q", [(2, 32), (4, 256)])
+def test_grouped_latent_heads_sparse(h_kv, h_q):
+    w = wl.build("grouped-sparse", 50 + h_kv, np.array([700, 129, 2000]), B=3, s_q=2, h_q=h_q,
+                 h_kv=h_kv, num_pages=60, poison=True, topk=128)
+    w.indices[1, 0, 5:9] = -1
+    o, lse, _ = run_gpu(Dev(w))
+    compare(w, o, lse, label=f"sparse h_kv={h_kv} h_q={h_q}")
+
+
+def test_grouped_plan_bit_exact():
+    m = _m()
+    lengths = [37, 130, 0, 5000, 64]
+    for h_kv, s_q, topk in [(2, 1, None), (4, 2, None), (2, 2, 256)]:
+        plan, ns = m.get_mla_metadata(i32_dev(np.array(lengths)), s_q * 16, h_kv, s_q=s_q, topk=topk,
+                                      num_workers=7)
+        torch.cuda.synchronize()
+        p = plan.cpu().numpy()
+        items = [topk] * (len(lengths) * s_q * h_kv) if topk else list(np.repeat(lengths, h_kv))
+        ref_p, ref_ns = orc.plan(items, int(p[0]), int(p[1]))
+        assert (p == ref_p).all() and (ns.cpu().numpy() == ref_ns).all(), (h_kv, s_q, topk)
+
+
 def test_softmax_scale():
     w = wl.tiny()
     o, lse, _ = run_gpu(Dev(w), softmax_scale=0.11)

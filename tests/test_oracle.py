@@ -19,13 +19,14 @@ from mla_paged_kv_get_amd import workloads as wl
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
-def _contiguous_cache(w, b):
-    """Sequence b's K rows in logical order, built page by page (independent of
-    the oracle's row arithmetic): concatenate whole pages in block-table order."""
+def _contiguous_cache(w, b, g=0):
+    """Sequence b's K rows of latent head g in logical order, built page by page
+    (independent of the oracle's row arithmetic): concatenate whole pages in
+    block-table order."""
     L = int(w.cache_seqlens[b])
     n = -(-L // 64)
     pages = [torch.from_numpy(w.kv[int(w.block_table[b, j])].astype(np.int32)) for j in range(n)]
-    rows = torch.cat(pages, dim=0)[:L, 0, :]               # [L, 576] int32 holding bf16 bits
+    rows = torch.cat(pages, dim=0)[:L, g, :]               # [L, 576] int32 holding bf16 bits
     return rows.to(torch.int16).view(torch.bfloat16).to(torch.float64)
 
 
@@ -33,11 +34,11 @@ def _q(w, b, s):
     return torch.from_numpy(w.q[b, s].astype(np.int32)).to(torch.int16).view(torch.bfloat16).double()
 
 
-def small(seed, lengths, s_q=1, h_q=16, causal=False, num_pages=None, poison=False, topk=None):
+def small(seed, lengths, s_q=1, h_q=16, causal=False, num_pages=None, poison=False, topk=None, h_kv=1):
     lengths = np.asarray(lengths)
     need = int(((lengths + 63) // 64).sum())
     return wl.build("t", seed, lengths, B=len(lengths), s_q=s_q, h_q=h_q,
-                    num_pages=num_pages or need + 3, causal=causal, poison=poison, topk=topk)
+                    num_pages=num_pages or need + 3, causal=causal, poison=poison, topk=topk, h_kv=h_kv)
 
 
 # ----------------------------------------------------------------------------
@@ -74,6 +75,34 @@ def test_decode_matches_torch_sdpa(lengths, h_q):
         ref = F.scaled_dot_product_attention(q[None, :, None, :], K[None, None].expand(1, h_q, -1, -1),
                                              K[None, None, :, :512].expand(1, h_q, -1, -1), scale=scale)
         np.testing.assert_allclose(O[b, 0], ref[0, :, 0].numpy(), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("h_kv,h_q", [(2, 16), (4, 8), (8, 8)])
+def test_grouped_latent_heads_match_sdpa(h_kv, h_q):
+    # query head h reads latent head h // (h_q / h_kv) (contiguous groups)
+    w = small(12, [70, 1, 129], h_q=h_q, h_kv=h_kv, s_q=2)
+    O, LSE = orc.decode(w.q, w.kv, w.block_table, w.cache_seqlens, 512)
+    group = h_q // h_kv
+    scale = 576 ** -0.5
+    for b in range(w.B):
+        Ks = torch.stack([_contiguous_cache(w, b, h // group) for h in range(h_q)])   # [h_q, L, 576]
+        for s in range(2):
+            q = _q(w, b, s)
+            ref = F.scaled_dot_product_attention(q[None, :, None, :], Ks[None], Ks[None, :, :, :512], scale=scale)
+            np.testing.assert_allclose(O[b, s], ref[0, :, 0].numpy(), rtol=0, atol=1e-12)
+            lse = torch.logsumexp(scale * torch.einsum("hd,hnd->hn", q, Ks), dim=1).numpy()
+            np.testing.assert_allclose(LSE[b, s], lse, rtol=0, atol=1e-12)
+
+
+def test_grouped_heads_equal_separate_single_head_caches():
+    # h_kv latent heads == h_kv independent single-head problems on the split cache
+    w = small(13, [200, 65], h_q=16, h_kv=4, causal=True, s_q=2)
+    O, LSE = orc.decode(w.q, w.kv, w.block_table, w.cache_seqlens, 512, causal=True)
+    for g in range(4):
+        Og, Lg = orc.decode(np.ascontiguousarray(w.q[:, :, 4 * g:4 * g + 4]),
+                            np.ascontiguousarray(w.kv[:, :, g:g + 1]), w.block_table, w.cache_seqlens,
+                            512, causal=True)
+        assert np.array_equal(O[:, :, 4 * g:4 * g + 4], Og) and np.array_equal(LSE[:, :, 4 * g:4 * g + 4], Lg)
 
 
 def test_causal_matches_sdpa_with_explicit_mask():
@@ -365,6 +394,8 @@ def test_work_closed_forms():
     idx = np.array([[[0, 5, -1, 99]]])
     b, f = orc.work([50], 1, 8, False, indices=idx)
     assert b == 2 * 1152 and f == 8 * 2 * 2176
+    b, f = orc.work([100, 7], 1, 32, False, h_kv=4)     # each key read once per latent head
+    assert b == 107 * 4 * 1152 and f == 32 * 107 * 2176
 
 
 def test_named_workload_recipes():
@@ -375,3 +406,5 @@ def test_named_workload_recipes():
     w = wl.memory_bound()
     assert w.cache_seqlens.min() >= 1 and w.cache_seqlens.max() <= 4096 and w.kv.shape[0] == 6000
     assert w.block_table.shape == (64, 64)
+    w = wl.grouped_heads()
+    assert w.kv.shape[2] == 8 and w.h_q == 128 and w.block_table.shape == (32, 64)
