@@ -15,6 +15,10 @@ a step from the previous one; the step reads its keys from HBM as a decode
 over a fresh layer would.  A GPU sleep queued ahead of the timed steps lets
 the host enqueue them all before the GPU reaches them, so the K steps run
 back to back and the HIP events measure GPU time, not Python launch time.
+Events sit only at the two ends of the timed region: an event between two
+launches costs several microseconds of GPU time.  The duration of each
+launch (plan, split decode, combine) comes from a second pass that enqueues
+K launches of that kernel alone, back to back, between two events.
 
 `roofline.traffic` is the HBM traffic of one decode launch measured with
 rocprofv3 counters (FETCH_SIZE and WRITE_SIZE, each calibrated against a plain
@@ -94,42 +98,44 @@ def run_workload(torch, m, w, steps, warmup, ncopies=NCOPIES):
     ws_bytes = m.workspace_bytes(B, w.s_q, rows, h_kv, w.topk or 0, 512, W)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
 
-    def step(k, ev=None):
+    def plan_call(k):
+        return m.get_mla_metadata(sl, rows, h_kv, s_q=w.s_q, topk=w.topk)
+
+    def decode_call(k, p, n, phases):
         c = k % ncopies
-        if ev is not None:
-            ev[0].record()
-        p, n = m.get_mla_metadata(sl, rows, h_kv, s_q=w.s_q, topk=w.topk)
-        if ev is not None:
-            ev[1].record()
         m.mla_decode_with_kvcache(qs[c], kvs[c], bt, sl, 512, p, n, causal=w.causal, indices=idx,
-                                  out=(o, lse), workspace=ws, phases=1)
-        if ev is not None:
-            ev[2].record()
-        m.mla_decode_with_kvcache(qs[c], kvs[c], bt, sl, 512, p, n, causal=w.causal, indices=idx,
-                                  out=(o, lse), workspace=ws, phases=2)
-        if ev is not None:
-            ev[3].record()
+                                  out=(o, lse), workspace=ws, phases=phases)
+
+    def step(k):
+        p, n = plan_call(k)
+        decode_call(k, p, n, 1)      # split decode kernel
+        decode_call(k, p, n, 2)      # merge of split items
+
+    def timed(fn, n):
+        """GPU time of n calls of fn enqueued back to back (events at the two ends only)."""
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        gpu_sleep_ms(torch, 2.0 + 0.25 * n)   # host enqueues all calls meanwhile
+        t0 = time.perf_counter()
+        start.record()
+        for k in range(n):
+            fn(k)
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end), time.perf_counter() - t0
 
     for k in range(warmup):
         step(k)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    gpu_sleep_ms(torch, 2.0 + 0.25 * steps)   # host enqueues all steps meanwhile
-    t0 = time.perf_counter()
-    start.record()
-    for k in range(steps):
-        step(k, evs[k])
-    end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    total_ms = start.elapsed_time(end)
-    plan_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    dec_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    comb_ms = [e[2].elapsed_time(e[3]) for e in evs]
-    return dict(ms_per_step=total_ms / steps, wall_s=wall, plan_ms=float(np.mean(plan_ms)),
-                decode_ms=float(np.mean(dec_ms)), decode_ms_med=float(np.median(dec_ms)),
-                combine_ms=float(np.mean(comb_ms)), num_workers=W, o=o, lse=lse)
+    # Timed region: K whole steps.
+    total_ms, wall = timed(step, steps)
+    # Each launch of the step on its own: K launches back to back on the
+    # stream the library launches on, so the average is the launch duration
+    # plus the gap between two launches.
+    plan_total, _ = timed(plan_call, steps)
+    dec_total, _ = timed(lambda k: decode_call(k, plan, ns, 1), steps)
+    comb_total, _ = timed(lambda k: decode_call(k, plan, ns, 2), steps)
+    return dict(ms_per_step=total_ms / steps, wall_s=wall, plan_ms=plan_total / steps,
+                decode_ms=dec_total / steps, combine_ms=comb_total / steps, num_workers=W, o=o, lse=lse)
 
 
 HERE = os.path.dirname(os.path.abspath(__file__))
