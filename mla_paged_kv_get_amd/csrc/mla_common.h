@@ -95,10 +95,10 @@ hipError_t launch_validate(const int32_t* block_table, int max_blocks, const int
 // Decode variants: how a workgroup covers an item's query rows.
 enum Variant : int {
   kVariantRows16 = 0,    // <= 16 rows: 4 waves split each 64-token tile 4 ways
-  kVariantRows64 = 1,    // > 16 rows: 4 waves x 16 rows = 64-row tiles
+  kVariantRows64 = 1,    // > 16 rows: 64-row tiles, two wave pairs of 32 rows
 };
 constexpr int variant_rows(int v) { return v == kVariantRows16 ? 16 : 64; }
-constexpr int variant_overhead(int v) { return v == kVariantRows16 ? 2 : 2; }
+constexpr int variant_overhead(int v) { return v == kVariantRows16 ? 1 : 2; }
 inline int pick_variant(int rows_per_item) { return rows_per_item <= 16 ? kVariantRows16 : kVariantRows64; }
 
 }  // namespace mla

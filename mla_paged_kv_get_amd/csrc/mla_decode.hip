@@ -501,6 +501,31 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
         qf[ks] = kWide ? *reinterpret_cast<const bf16x8*>(qrow + 16 * ks + 8 * hl)
                        : *reinterpret_cast<const bf16x8*>(qrow + 32 * ks + 8 * g);
     };
+    // Rows16, dense: the query rows of an item that starts mid-run come in
+    // through LDS.  Wave 0 copies them into rows 0..15 of the stage the next
+    // tile is headed for (its own share of that tile goes out later, from
+    // `off_late`), so no register load has to complete behind a tile copy and
+    // the copy of the next tile is not held back at the item boundary.
+    int64_t off_late[C::kLaneRows];
+    auto issue_q = [&](char* stage, int item) __attribute__((always_inline)) {
+      const char* q_bytes = reinterpret_cast<const char*>(a.q);
+#pragma unroll
+      for (int j = 0; j < C::kLoads; ++j) {
+        const int r = j / 9, cl = j % 9;
+        const int qr = cp_row[r] < a.M ? cp_row[r] : 0;     // rows past M borrow row 0
+        const char* src = q_bytes + q_row(a, item, qr) * (int64_t)kRowBytes + cl * 128 +
+                          (((lane & 7) ^ cp_swz[r]) << 4);
+        copy_to_lds_16(src, lds_addr(stage + j * 1024));
+      }
+    };
+    auto q_from_lds = [&](const char* stage) __attribute__((always_inline)) {
+      // row li, chunk 4 ks + g, in the tile layout
+      const int qb = ((li >> 3) * 9 << 10) + ((li & 7) << 7);
+      const int qx0 = (g ^ swz(li)) << 4, qx1 = ((4 + g) ^ swz(li)) << 4;
+#pragma unroll
+      for (int ks = 0; ks < C::kQf; ++ks)
+        qf[ks] = *reinterpret_cast<const bf16x8*>(stage + qb + ((ks >> 1) << 10) + ((ks & 1) ? qx1 : qx0));
+    };
     auto key_limit = [&](int item) __attribute__((always_inline)) -> int {   // dense: keys of this lane's row are < limit
       const int L = item_len(item);
       if (!row_ok) return 0;
@@ -635,6 +660,10 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
         if (lane == 0) red_need[wave] = need;
       }
       barrier_keep_loads();
+      if constexpr (!kWide) {
+        // every wave has read the query rows staged in `dma_stage`
+        if (dma_stage != nullptr) issue(dma_stage, off_late);
+      }
       float m_tile;
       bool move;
       if constexpr (!kWide) {
@@ -809,6 +838,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
       tile_finish(nx_item, nx_blk, raw, off, kvalid[1]);
     }
 
+    bool q_pending = false;   // rows16, dense: the query rows of tile t's item come through LDS
+
     // One step: tile t sits in `cur`; tile t + 1 goes into `nxt`.  Tile t + 1
     // is requested before waiting for tile t, so two tiles are in flight while
     // a wave waits; the wait below counts only this wave's copy of tile t + 1
@@ -848,7 +879,16 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
         return has_next;
       }
       barrier_keep_loads();                              // every wave is done with `nxt`
-      if (has_next) issue(nxt, off);
+      const bool q_lds = q_pending && wave == 0;         // wave-uniform
+      if (q_pending && wave == 0) issue_q(nxt, cur_item);
+      if (has_next) {
+        if (q_lds) {
+#pragma unroll
+          for (int r = 0; r < C::kLaneRows; ++r) off_late[r] = off[r];
+        } else {
+          issue(nxt, off);
+        }
+      }
       if (n2_item >= 0) tile_fetch(n2_item, n2_blk, raw);  // index data of tile t + 2
       // Vector-memory operations issued after tile t's copy: the copy of tile
       // t + 1 and, in sparse mode, the index loads of tile t + 2.  Waiting
@@ -856,25 +896,31 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
       // (loads complete in order).  The compiler barrier keeps the index loads
       // above the wait.
       asm volatile("" ::: "memory");
-      if (has_next) {
+      if (has_next && !q_lds) {
         if (sparse && n2_item >= 0) __builtin_amdgcn_s_waitcnt(kWaitKeepRawCopy);
         else __builtin_amdgcn_s_waitcnt(kWaitKeepCopy);
       } else {
-        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_s_waitcnt(0);     // wave 0 with staged query rows: tile t, then the rows
       }
       barrier_keep_loads();                              // tile t is in LDS for every wave
+      if (q_pending) q_from_lds(nxt);
       if (n2_item >= 0) tile_finish(n2_item, n2_blk, raw, off, kvalid[(t + 2) & 3]);
       const bool ends = !has_next || nx_item != cur_item;
-      compute(cur, kvalid[t & 3], cur_blk, cur_lim, nullptr);
+      compute(cur, kvalid[t & 3], cur_blk, cur_lim, q_lds && has_next ? nxt : nullptr);
+      q_pending = false;
       if (ends) {
         finish(cur_item, cur_split);
         if (has_next) {
           cur_lim = key_limit(nx_item);
           cur_split = 0;
-          // Query rows of the next item, completed before the next copy is
-          // issued (see the prologue).
-          load_q(nx_item);
-          __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+          if constexpr (sparse) {
+            // Query rows of the next item, completed before the next copy is
+            // issued (see the prologue).
+            load_q(nx_item);
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+          } else {
+            q_pending = true;          // staged through LDS in the next step
+          }
         }
       }
       cur_item = nx_item;
