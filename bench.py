@@ -207,10 +207,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="memory_bound",
                     choices=["tiny", "memory_bound", "near_ridge", "mtp_causal", "sparse_topk",
-                             "grouped_heads"])
+                             "grouped_heads", "sparse_prefill"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--secondary", action="store_true",
-                    help="also time the near-ridge, MTP-causal, sparse top-k and grouped-heads workloads")
+                    help="also time the near-ridge, MTP-causal, sparse top-k, grouped-heads and "
+                         "sparse-prefill workloads")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run plain device copies of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -264,7 +265,7 @@ def main():
     }
     if args.secondary:
         sec = {}
-        for name in ("near_ridge", "mtp_causal", "sparse_topk", "grouped_heads"):
+        for name in ("near_ridge", "mtp_causal", "sparse_topk", "grouped_heads", "sparse_prefill"):
             w2 = wl.NAMED[name]()
             kb, fl = algorithmic_work(w2)
             r2 = run_workload(torch, m, w2, max(10, args.steps // 2), 3)

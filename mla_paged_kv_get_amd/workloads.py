@@ -166,6 +166,16 @@ def sparse_topk(poison: bool = False, B: int = 16) -> Workload:
                  num_pages=B * 1024, max_blocks=1024, topk=2048, poison=poison, rng=rng)
 
 
+def sparse_prefill(poison: bool = False, T: int = 4096) -> Workload:
+    """Sparse prefill: one sequence of 4096 context tokens followed by T = 4096
+    new query tokens (s_q = T), h_q=128, top-k 2048 unique unsorted indices per
+    query token drawn from the keys it may see (positions 0 .. 4096 + t)."""
+    rng = np.random.default_rng(7)
+    lengths = np.array([4096 + T])
+    return build(f"sparse-prefill b1 T{T} h128 L{4096 + T} k2048", 7, lengths, B=1, s_q=T, h_q=128,
+                 num_pages=(4096 + T) // PAGE + 8, topk=2048, poison=poison, rng=rng)
+
+
 def grouped_heads(poison: bool = False) -> Workload:
     """b=32, s_q=1, h_q=128 over h_kv=8 latent heads (16 query heads each),
     lengths uniform in [1, 4096], 1200-page pool."""
@@ -182,4 +192,5 @@ NAMED = {
     "mtp_causal": mtp_causal,
     "sparse_topk": sparse_topk,
     "grouped_heads": grouped_heads,
+    "sparse_prefill": sparse_prefill,
 }

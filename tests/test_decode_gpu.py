@@ -179,6 +179,31 @@ def test_grouped_latent_heads(h_kv, h_q, s_q, causal):
     compare(w, o2, lse2, label=f"h_kv={h_kv} W=3")
 
 
+def test_sparse_prefill_sampled():
+    # 4096 query tokens of one sequence, each with 2048 of the keys it may see
+    w = wl.sparse_prefill()
+    o, lse, _ = run_gpu(Dev(w))
+    items = [(0, s) for s in (0, 1, 777, 2048, 3000, 4095)]
+    compare(w, o, lse, items=items, label="sparse-prefill")
+
+
+@pytest.mark.parametrize("h_q", [16, 128])
+def test_sparse_prefill_small_full(h_q):
+    # every query token checked: T = 200 new tokens after 100 of context, causal
+    # index lists with padding where a token sees fewer keys than top-k
+    T, ctx, k = 200, 100, 160
+    w = wl.build("prefill-small", 60, np.array([ctx + T]), B=1, s_q=T, h_q=h_q, num_pages=12,
+                 poison=True, topk=None)
+    rng = np.random.default_rng(61)
+    idx = np.full((1, T, k), -1, dtype=np.int32)
+    for t in range(T):
+        n = min(k, ctx + t + 1)
+        idx[0, t, :n] = rng.choice(ctx + t + 1, n, replace=False)
+    w.indices = idx
+    o, lse, _ = run_gpu(Dev(w))
+    compare(w, o, lse, label=f"prefill T={T} h_q={h_q}")
+
+
 def test_grouped_heads_workload_full():
     w = wl.grouped_heads()
     o, lse, _ = run_gpu(Dev(w))

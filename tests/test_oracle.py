@@ -408,3 +408,8 @@ def test_named_workload_recipes():
     assert w.block_table.shape == (64, 64)
     w = wl.grouped_heads()
     assert w.kv.shape[2] == 8 and w.h_q == 128 and w.block_table.shape == (32, 64)
+    w = wl.sparse_prefill(T=64)
+    assert w.indices.shape == (1, 64, 2048) and int(w.cache_seqlens[0]) == 4096 + 64
+    for t in range(64):     # causally valid, unique
+        row = w.indices[0, t]
+        assert row.min() >= 0 and row.max() <= 4096 + t and len(np.unique(row)) == 2048
