@@ -24,6 +24,11 @@ CFLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     # packed fp32 VALU forms are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: the register allocator then keeps the wide
+    # decode's output accumulators in place across the tile loop (in AGPRs it
+    # copied all 128 of them to VGPRs and back on every tile) and parks the
+    # query fragments, which only MFMAs read, in AGPRs
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
     "-Wall", "-Wno-unused-function",
 ]
