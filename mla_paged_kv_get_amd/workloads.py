@@ -12,6 +12,13 @@ handed out consecutively from the permutation, sequence by sequence.  Rows that
 no sequence references (unassigned pages, slots past a sequence's length in its
 last page) and the block-table padding page may be filled with NaN ("poison")
 so that any read of them shows up in the outputs.
+
+Packed FP8 caches (656 bytes per row: 512 OCP E4M3 codes, 4 float32 scales,
+64 bf16 RoPE values) are drawn in the same order: the latent values as float32
+N(0, 1), each block of 128 given the scale max|x| / 448 and cast to E4M3 by
+torch's float8_e4m3fn conversion (round to nearest even), then the RoPE values
+as bf16 N(0, 1).  Poisoned FP8 rows hold the NaN code 0x7F, NaN scales and
+NaN RoPE values.
 """
 from __future__ import annotations
 
@@ -23,6 +30,8 @@ PAGE = 64
 D_QK = 576
 D_V = 512
 BF16_NAN = 0x7FC0
+FP8_ROW_BYTES = 656
+E4M3_NAN = 0x7F
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -30,6 +39,33 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
     r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
     return r.astype(np.uint16)
+
+
+def packed_fp8_rows(rng: np.random.Generator, shape, chunk: int = 1 << 22) -> np.ndarray:
+    """Packed FP8 rows [*shape, 656] (uint8) of N(0, 1) latent values and bf16 RoPE values."""
+    import torch
+    n = int(np.prod(shape))
+    out = np.empty((n, FP8_ROW_BYTES), dtype=np.uint8)
+    for i in range(0, n, chunk):
+        m = min(chunk, n - i)
+        x = rng.standard_normal((m, 4, 128), dtype=np.float32)
+        scale = (np.abs(x).max(axis=2) / np.float32(448.0)).astype(np.float32)     # [m, 4]
+        scale[scale == 0] = 1.0
+        codes = torch.from_numpy(x / scale[:, :, None]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        out[i:i + m, :512] = codes.reshape(m, 512)
+        out[i:i + m, 512:528] = scale.astype("<f4").view(np.uint8).reshape(m, 16)
+    for i in range(0, n, chunk):
+        m = min(chunk, n - i)
+        rope = f32_to_bf16_bits(rng.standard_normal((m, 64), dtype=np.float32))
+        out[i:i + m, 528:656] = rope.astype("<u2").view(np.uint8).reshape(m, 128)
+    return out.reshape(*shape, FP8_ROW_BYTES)
+
+
+def poison_fp8_rows(rows: np.ndarray) -> None:
+    """Fill packed FP8 rows (last axis 656) with NaN codes, scales and RoPE values, in place."""
+    rows[..., :512] = E4M3_NAN
+    rows[..., 512:528] = np.full(4, np.nan, dtype="<f4").view(np.uint8)
+    rows[..., 528:656] = np.full(64, BF16_NAN, dtype="<u2").view(np.uint8)
 
 
 def normal_bf16(rng: np.random.Generator, shape, chunk: int = 1 << 24) -> np.ndarray:
@@ -77,7 +113,7 @@ def build(name: str, seed: int, lengths: np.ndarray | None, *, B: int, s_q: int,
           num_pages: int, causal: bool = False, max_blocks: int | None = None,
           poison: bool = False, h_kv: int = 1, topk: int | None = None,
           rng: np.random.Generator | None = None, pad_page: int | None = None,
-          dv: int = D_V) -> Workload:
+          dv: int = D_V, kv_format: str = "bf16") -> Workload:
     """Assemble a workload.  ``lengths`` may be drawn by the caller from ``rng``
     (the same generator is then used for the rest, keeping the draw order)."""
     rng = np.random.default_rng(seed) if rng is None else rng
@@ -101,7 +137,12 @@ def build(name: str, seed: int, lengths: np.ndarray | None, *, B: int, s_q: int,
         bt[b, :n] = perm[off:off + n]
         off += n
     q = normal_bf16(rng, (B, s_q, h_q, D_QK))
-    kv = normal_bf16(rng, (pool, PAGE, h_kv, D_QK))
+    if kv_format == "fp8":
+        kv = packed_fp8_rows(rng, (pool, PAGE, h_kv))
+    elif kv_format == "bf16":
+        kv = normal_bf16(rng, (pool, PAGE, h_kv, D_QK))
+    else:
+        raise ValueError(f"unknown kv_format {kv_format!r}")
     indices = None
     if topk is not None:
         indices = np.empty((B, s_q, topk), dtype=np.int32)
@@ -116,7 +157,12 @@ def build(name: str, seed: int, lengths: np.ndarray | None, *, B: int, s_q: int,
             for j in range(int(nblk[b])):
                 n_valid = min(PAGE, L - j * PAGE)
                 referenced[bt[b, j], :n_valid] = True
-        kv[~referenced] = BF16_NAN
+        if kv_format == "fp8":
+            bad = kv[~referenced]           # a copy: [rows, h_kv, 656]
+            poison_fp8_rows(bad)
+            kv[~referenced] = bad
+        else:
+            kv[~referenced] = BF16_NAN
     return Workload(name=name, q=q, kv=kv, block_table=bt,
                     cache_seqlens=lengths.astype(np.int32), causal=causal,
                     indices=indices, dv=dv,

@@ -28,6 +28,13 @@ float64 with NumPy (one library matmul per query token is the only "fast" step):
   query token (b, s) attends to the logical positions ``indices[b, s, :topk]``;
   an entry outside ``[0, L_b)`` (e.g. -1) is padding and is skipped.
 * Empty key set: O = 0, LSE = -inf.
+* FP8 cache ("FlashInfer, SM120 GPU를 위한 희소 MLA 커널", section "코드 분석",
+  item 5: a packed KV cache whose scale format is a parameter; "Blackwell을
+  위한 새로운 MLA 백엔드: TOKENSPEED_MLA 분석": FP8 KV caches).  The pages fix
+  no layout; the one read here packs each cached row into 656 bytes: the 512
+  latent values as OCP E4M3 codes, one float32 scale per block of 128 latent
+  values (4 scales), then the 64 RoPE values in bf16.  A latent value is its
+  code's value times its block's scale; K and V are then as above.
 * ``plan`` — the split-KV tile scheduler (``get_mla_metadata`` of topnet.top,
   step 2, returns ``tile_scheduler_metadata`` and ``num_splits``).  The pages do
   not say how work is split; :func:`plan` states the scheduler this library
@@ -45,6 +52,8 @@ import numpy as np
 PAGE = 64          # tokens per KV page (topnet.top, "FlashMLA의 주요 특성")
 D_QK = 576         # latent (512) + decoupled RoPE (64) values per cached row
 D_V = 512          # V = first 512 values of the row
+FP8_ROW_BYTES = 656    # packed FP8 row: 512 E4M3 codes, 4 float32 scales, 64 bf16 RoPE values
+FP8_BLOCK = 128        # latent values per scale
 
 
 # --------------------------------------------------------------------------
@@ -54,6 +63,37 @@ def bf16_to_f64(bits) -> np.ndarray:
     """Exact upcast of raw bf16 bit patterns (uint16) to float64."""
     u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
     return u.view(np.float32).astype(np.float64)
+
+
+def e4m3_to_f64(codes) -> np.ndarray:
+    """Value of OCP 8-bit floating-point E4M3 codes (exact in float64).
+
+    Bit 7 is the sign, bits 6..3 the exponent field e (bias 7), bits 2..0 the
+    mantissa m.  e = 0 encodes the subnormals m/8 * 2^-6; the code with e = 15
+    and m = 7 is NaN; there are no infinities (the largest value is 448).
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where((c >> 7) == 1, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return sign * mag
+
+
+def fp8_rows_to_f64(rows) -> np.ndarray:
+    """Packed FP8 rows [..., 656] (uint8) -> their 576 values in float64.
+
+    Bytes 0..511: E4M3 codes of the latent values; bytes 512..527: four
+    little-endian float32 scales, scale j for latent values 128 j .. 128 j + 127;
+    bytes 528..655: the 64 RoPE values as little-endian bf16.
+    """
+    r = np.array(rows, dtype=np.uint8, copy=True)
+    lat = e4m3_to_f64(r[..., :512])
+    scales = np.ascontiguousarray(r[..., 512:528]).view("<f4").astype(np.float64)
+    lat = lat * np.repeat(scales, FP8_BLOCK, axis=-1)
+    rope = bf16_to_f64(np.ascontiguousarray(r[..., 528:656]).view("<u2"))
+    return np.concatenate([lat, rope], axis=-1)
 
 
 # --------------------------------------------------------------------------
@@ -91,7 +131,8 @@ def decode(q_bits: np.ndarray, kv_bits: np.ndarray, block_table: np.ndarray,
     """float64 MLA decode.
 
     q_bits   uint16 [B, s_q, h_q, d]           (bf16 bit patterns)
-    kv_bits  uint16 [num_pages, 64, h_kv, d]   (bf16 bit patterns)
+    kv_bits  uint16 [num_pages, 64, h_kv, d]   (bf16 bit patterns), or
+             uint8  [num_pages, 64, h_kv, 656] (packed FP8 rows, see fp8_rows_to_f64)
     block_table int [B, max_blocks]; cache_seqlens int [B]
     indices  optional int [B, s_q, topk] logical positions (sparse mode)
     items    optional iterable of (b, s) pairs to compute (others stay NaN)
@@ -105,7 +146,11 @@ def decode(q_bits: np.ndarray, kv_bits: np.ndarray, block_table: np.ndarray,
     if indices is not None and causal:
         raise ValueError("causal and indices are exclusive")
     scale = d ** -0.5 if softmax_scale is None else float(softmax_scale)
-    rows = kv_bits.reshape(-1, h_kv, d)
+    fp8 = kv_bits.dtype == np.uint8
+    if fp8 and kv_bits.shape[-1] != FP8_ROW_BYTES:
+        raise ValueError("packed FP8 rows have 656 bytes")
+    rows = kv_bits.reshape(-1, h_kv, kv_bits.shape[-1])
+    row_values = fp8_rows_to_f64 if fp8 else bf16_to_f64
     group = h_q // h_kv
     out = np.full((B, s_q, h_q, dv), np.nan)
     lse = np.full((B, s_q, h_q), np.nan)
@@ -119,7 +164,7 @@ def decode(q_bits: np.ndarray, kv_bits: np.ndarray, block_table: np.ndarray,
             continue
         rid = physical_rows(block_table, b, pos)
         for g in range(h_kv):
-            K = bf16_to_f64(rows[rid, g, :])                 # [n, d]
+            K = row_values(rows[rid, g, :])                  # [n, d]
             V = K[:, :dv]                                    # [n, dv]
             Q = bf16_to_f64(q_bits[b, s, g * group:(g + 1) * group, :])  # [group, d]
             S = scale * (Q @ K.T)                            # [group, n]
@@ -318,6 +363,6 @@ def bf16_round_f64(x: np.ndarray) -> np.ndarray:
     return bf16_to_f64(r)
 
 
-__all__ = ["PAGE", "D_QK", "D_V", "bf16_to_f64", "physical_rows", "key_positions", "decode",
+__all__ = ["PAGE", "D_QK", "D_V", "FP8_ROW_BYTES", "FP8_BLOCK", "e4m3_to_f64", "fp8_rows_to_f64", "bf16_to_f64", "physical_rows", "key_positions", "decode",
            "merge_splits", "plan", "plan_runs", "decode_by_plan", "work", "bf16_round_f64",
            "PLAN_WORDS", "PLAN_VERSION"]

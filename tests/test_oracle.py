@@ -62,6 +62,88 @@ def test_generator_rounding_matches_torch():
 
 
 # ----------------------------------------------------------------------------
+# Packed FP8 rows
+# ----------------------------------------------------------------------------
+def test_e4m3_matches_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = orc.e4m3_to_f64(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ours[ok], ref[ok]) and np.array_equal(np.signbit(ours[ok]), np.signbit(ref[ok]))
+
+
+def test_e4m3_closed_forms():
+    # OCP E4M3: bias 7, 3 mantissa bits, e = 0 subnormal, S.1111.111 NaN, max 448
+    v = orc.e4m3_to_f64(np.array([0x38, 0x7E, 0x01, 0x08, 0x07, 0xB8, 0x00, 0x80, 0x7F, 0xFF, 0x3C],
+                                 dtype=np.uint8))
+    assert list(v[:8]) == [1.0, 448.0, 2.0 ** -9, 2.0 ** -6, 7 * 2.0 ** -9, -1.0, 0.0, -0.0]
+    assert np.isnan(v[8]) and np.isnan(v[9]) and v[10] == 1.5
+
+
+def _fp8_row(latent_codes, scales, rope_bits):
+    r = np.empty(656, dtype=np.uint8)
+    r[:512] = latent_codes
+    r[512:528] = np.asarray(scales, dtype="<f4").view(np.uint8)
+    r[528:] = np.asarray(rope_bits, dtype="<u2").view(np.uint8)
+    return r
+
+
+def test_fp8_row_layout():
+    codes = np.full(512, 0x38, dtype=np.uint8)          # 1.0
+    codes[130] = 0x40                                    # 2.0 in block 1
+    codes[511] = 0xC4                                    # -3.0 in block 3
+    rope = np.full(64, 0x3FC0, dtype=np.uint16)          # 1.5
+    rope[63] = 0xC000                                    # -2.0
+    v = orc.fp8_rows_to_f64(_fp8_row(codes, [0.5, 2.0, 4.0, -0.25], rope))
+    assert v.shape == (576,)
+    assert (v[:128] == 0.5).all() and v[128] == 2.0 and v[130] == 4.0 and (v[256:384] == 4.0).all()
+    assert v[384] == -0.25 and v[511] == 0.75
+    assert (v[512:575] == 1.5).all() and v[575] == -2.0
+
+
+def test_fp8_decode_equals_bf16_decode_on_exact_values():
+    # power-of-two scales: every dequantized value is a bf16, so the bf16 cache built from them
+    # (through torch's float8 and bfloat16 conversions) must give the very same float64 result
+    w = small(21, [70, 129], h_q=16, h_kv=2, causal=True, s_q=2)
+    rng = np.random.default_rng(5)
+    kv8 = wl.packed_fp8_rows(rng, w.kv.shape[:3])
+    sc = np.exp2(rng.integers(-8, 3, size=w.kv.shape[:3] + (4,))).astype("<f4")
+    kv8[..., 512:528] = sc.view(np.uint8)
+    lat = torch.from_numpy(kv8[..., :512].copy()).view(torch.float8_e4m3fn).to(torch.float32)
+    lat = lat * torch.from_numpy(np.repeat(sc, 128, axis=-1))
+    bf = np.empty(w.kv.shape, dtype=np.uint16)
+    bf[..., :512] = lat.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    bf[..., 512:] = kv8[..., 528:].copy().view("<u2")
+    O8, L8 = orc.decode(w.q, kv8, w.block_table, w.cache_seqlens, 512, causal=True)
+    Ob, Lb = orc.decode(w.q, bf, w.block_table, w.cache_seqlens, 512, causal=True)
+    assert np.array_equal(O8, Ob) and np.array_equal(L8, Lb)
+
+
+def test_fp8_decode_matches_sdpa():
+    w = wl.build("t8", 22, np.array([100, 1, 200]), B=3, s_q=1, h_q=16, num_pages=10, kv_format="fp8")
+    O, LSE = orc.decode(w.q, w.kv, w.block_table, w.cache_seqlens, 512)
+    for b in range(3):
+        L = int(w.cache_seqlens[b])
+        pages = [w.kv[int(w.block_table[b, j]), :, 0, :] for j in range(-(-L // 64))]
+        rows = np.concatenate(pages, axis=0)[:L]                       # [L, 656]
+        lat = torch.from_numpy(rows[:, :512].copy()).view(torch.float8_e4m3fn).to(torch.float64)
+        sc = torch.from_numpy(rows[:, 512:528].copy().view("<f4").astype(np.float64))
+        rope = torch.from_numpy(rows[:, 528:].copy().view("<u2").astype(np.int32)).to(torch.int16)
+        K = torch.cat([lat * sc.repeat_interleave(128, dim=1), rope.view(torch.bfloat16).double()], dim=1)
+        q = _q(w, b, 0)
+        ref = F.scaled_dot_product_attention(q[None, :, None, :], K[None, None].expand(1, 16, -1, -1),
+                                             K[None, None, :, :512].expand(1, 16, -1, -1), scale=576 ** -0.5)
+        np.testing.assert_allclose(O[b, 0], ref[0, :, 0].numpy(), rtol=0, atol=1e-12)
+
+
+def test_fp8_poison_rows_never_read():
+    w = wl.build("t8p", 23, np.array([65, 3]), B=2, s_q=1, h_q=16, num_pages=6, kv_format="fp8", poison=True)
+    O, LSE = orc.decode(w.q, w.kv, w.block_table, w.cache_seqlens, 512)
+    assert np.isfinite(O).all() and np.isfinite(LSE).all()
+
+
+# ----------------------------------------------------------------------------
 # Decode vs. a library routine (torch SDPA in float64 on the CPU)
 # ----------------------------------------------------------------------------
 @pytest.mark.parametrize("lengths,h_q", [([37, 130], 16), ([1, 64, 65, 200], 8), ([129], 32)])
