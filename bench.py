@@ -40,17 +40,17 @@ import time
 
 import numpy as np
 
-KV_ROW_BYTES = 576 * 2
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
 NCOPIES = 4
 
 
 def algorithmic_work(w):
-    """KV bytes (each key row of each latent head once) and FLOPs (2 * (576 + 512)
-    per query row and key)."""
+    """KV bytes (each key row of each latent head once, at its stored size: 1152
+    bytes bf16, 656 packed FP8) and FLOPs (2 * (576 + 512) per query row and key)."""
     L = w.cache_seqlens.astype(np.int64)
     h_kv = w.kv.shape[2]
+    KV_ROW_BYTES = w.kv.shape[3] * w.kv.itemsize
     if w.indices is not None:
         ok = (w.indices >= 0) & (w.indices < L[:, None, None])
         keys = int(ok.sum())
@@ -82,7 +82,7 @@ def _to_dev(torch, a, dtype=None):
 
 def run_workload(torch, m, w, steps, warmup, ncopies=NCOPIES):
     q0 = _to_dev(torch, w.q.view(np.int16), torch.bfloat16)
-    kv0 = _to_dev(torch, w.kv.view(np.int16), torch.bfloat16)
+    kv0 = _to_dev(torch, w.kv) if w.kv.dtype == np.uint8 else _to_dev(torch, w.kv.view(np.int16), torch.bfloat16)
     bt = _to_dev(torch, w.block_table.astype(np.int32))
     sl = _to_dev(torch, w.cache_seqlens.astype(np.int32))
     idx = _to_dev(torch, w.indices.astype(np.int32)) if w.indices is not None else None
@@ -207,11 +207,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="memory_bound",
                     choices=["tiny", "memory_bound", "near_ridge", "mtp_causal", "sparse_topk",
-                             "grouped_heads", "sparse_prefill"])
+                             "grouped_heads", "sparse_prefill", "memory_bound_fp8", "sparse_topk_fp8"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--secondary", action="store_true",
-                    help="also time the near-ridge, MTP-causal, sparse top-k, grouped-heads and "
-                         "sparse-prefill workloads")
+                    help="also time the near-ridge, MTP-causal, sparse top-k, grouped-heads, "
+                         "sparse-prefill and the two packed-FP8 workloads")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run plain device copies of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -265,7 +265,8 @@ def main():
     }
     if args.secondary:
         sec = {}
-        for name in ("near_ridge", "mtp_causal", "sparse_topk", "grouped_heads", "sparse_prefill"):
+        for name in ("near_ridge", "mtp_causal", "sparse_topk", "grouped_heads", "sparse_prefill",
+                     "memory_bound_fp8", "sparse_topk_fp8"):
             w2 = wl.NAMED[name]()
             kb, fl = algorithmic_work(w2)
             r2 = run_workload(torch, m, w2, max(10, args.steps // 2), 3)

@@ -191,6 +191,41 @@ int mla_decode_with_kvcache_phase(const void* q, const void* kvcache, int64_t nu
                                   size_t workspace_bytes, int phases, void* stream);
 
 /*
+ * mla_decode_with_kvcache_fp8 / mla_decode_with_kvcache_fp8_phase — the same
+ * decode over a packed FP8 cache (a packed KV cache with a per-block scale
+ * format: "FlashInfer, SM120 GPU를 위한 희소 MLA 커널", section "코드 분석",
+ * item 5; FP8 KV caches: "Blackwell을 위한 새로운 MLA 백엔드: TOKENSPEED_MLA
+ * 분석").  The pages fix no layout; this library's is:
+ *
+ *   kvcache  [num_pages, 64, h_kv, 656] bytes, device.  Row bytes 0..511: the
+ *            512 latent values as OCP E4M3 codes; bytes 512..527: four
+ *            little-endian float32 scales, scale j multiplying latent values
+ *            128 j .. 128 j + 127; bytes 528..655: the 64 RoPE values as bf16.
+ *
+ * K_j is the row's 576 values (latent code x its block's scale, then RoPE),
+ * V_j its first 512; d_qk must be 576 (the number of values, not bytes).  In
+ * the kernels each dequantized latent value is rounded to bf16 before the
+ * bf16 matrix products.  Every other argument, check, status and the phases
+ * argument are those of mla_decode_with_kvcache(_phase), with the same plan.
+ */
+int mla_decode_with_kvcache_fp8(const void* q, const void* kvcache, int64_t num_pages,
+                                int page_size, const int32_t* block_table, int max_blocks,
+                                const int32_t* cache_seqlens, int batch, int s_q, int h_q,
+                                int h_kv, int d_qk, int dv, const int32_t* plan,
+                                const int32_t* num_splits, int num_workers, int causal,
+                                float softmax_scale, const int32_t* indices, int topk,
+                                void* o, float* lse, void* workspace,
+                                size_t workspace_bytes, void* stream);
+int mla_decode_with_kvcache_fp8_phase(const void* q, const void* kvcache, int64_t num_pages,
+                                      int page_size, const int32_t* block_table, int max_blocks,
+                                      const int32_t* cache_seqlens, int batch, int s_q, int h_q,
+                                      int h_kv, int d_qk, int dv, const int32_t* plan,
+                                      const int32_t* num_splits, int num_workers, int causal,
+                                      float softmax_scale, const int32_t* indices, int topk,
+                                      void* o, float* lse, void* workspace,
+                                      size_t workspace_bytes, int phases, void* stream);
+
+/*
  * mla_debug_row_ids — indexing probe (test use).  Writes, through the same
  * device address function the decode kernels use, the physical cache row
  * (page * 64 + slot) of every key, or -1 where a key is not in the key set:

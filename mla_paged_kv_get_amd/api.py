@@ -13,6 +13,8 @@ import torch
 
 from . import _lib
 
+FP8_ROW_BYTES = 656   # packed FP8 cache row: 512 E4M3 codes, 4 float32 scales, 64 bf16 values
+
 D_QK = 576
 D_V = 512
 PAGE = 64
@@ -85,11 +87,20 @@ def mla_decode_with_kvcache(q: torch.Tensor, kvcache: torch.Tensor, block_table:
                             phases: int = 3):
     """Paged MLA decode; returns ``(o [b, s_q, h_q, dv] bf16, lse [b, s_q, h_q] fp32)``.
 
-    ``phases`` (1 = split kernel, 2 = merge kernel, 3 = both) lets a caller
-    launch the two kernels separately with the same arguments and buffers.
+    ``kvcache`` is bf16 ``[pages, 64, h_kv, 576]``, or uint8 ``[pages, 64, h_kv,
+    656]`` for packed FP8 rows (512 E4M3 latent codes, 4 float32 block scales,
+    64 bf16 RoPE values).  ``phases`` (1 = split kernel, 2 = merge kernel, 3 =
+    both) lets a caller launch the two kernels separately with the same
+    arguments and buffers.
     """
     _as_bits(q, "q")
-    _as_bits(kvcache, "kvcache")
+    fp8 = kvcache.dtype == torch.uint8
+    if fp8:
+        _need(kvcache.is_cuda and kvcache.is_contiguous(), "kvcache must be a contiguous CUDA tensor")
+        _need(kvcache.dim() == 4 and kvcache.shape[3] == FP8_ROW_BYTES,
+              "a packed FP8 kvcache is [pages, 64, h_kv, 656] uint8")
+    else:
+        _as_bits(kvcache, "kvcache")
     _i32(block_table, "block_table")
     _i32(cache_seqlens, "cache_seqlens")
     _i32(tile_scheduler_metadata, "tile_scheduler_metadata")
@@ -97,6 +108,8 @@ def mla_decode_with_kvcache(q: torch.Tensor, kvcache: torch.Tensor, block_table:
     _need(q.dim() == 4 and kvcache.dim() == 4, "q is [b, s_q, h_q, d], kvcache is [pages, 64, h_kv, d]")
     B, s_q, h_q, d = q.shape
     num_pages, page, h_kv, d2 = kvcache.shape
+    if fp8:
+        d2 = 576
     _need(d == d2, "q and kvcache disagree on d_qk")
     _need(block_table.dim() == 2 and block_table.shape[0] == B, "block_table is [b, max_blocks]")
     _need(cache_seqlens.numel() == B, "cache_seqlens is [b]")
@@ -120,7 +133,8 @@ def mla_decode_with_kvcache(q: torch.Tensor, kvcache: torch.Tensor, block_table:
     need = workspace_bytes(B, s_q, num_q_rows, h_kv, topk, dv, W) if dv > 0 else 0
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
-    _lib.check(_lib.lib().mla_decode_with_kvcache_phase(
+    entry = _lib.lib().mla_decode_with_kvcache_fp8_phase if fp8 else _lib.lib().mla_decode_with_kvcache_phase
+    _lib.check(entry(
         _ptr(q), _ptr(kvcache), num_pages, page, _ptr(block_table), block_table.shape[1],
         _ptr(cache_seqlens), B, s_q, h_q, h_kv, d, dv, _ptr(tile_scheduler_metadata),
         _ptr(num_splits), W, int(bool(causal)), ctypes.c_float(scale), _ptr(indices), topk,

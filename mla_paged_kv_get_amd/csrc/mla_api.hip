@@ -142,14 +142,17 @@ size_t mla_workspace_bytes(int batch, int s_q, int num_q_rows, int h_kv, int top
   return workspace_for(s, dv, num_workers);
 }
 
-int mla_decode_with_kvcache_phase(const void* q, const void* kvcache, int64_t num_pages,
-                                  int page_size, const int32_t* block_table, int max_blocks,
-                                  const int32_t* cache_seqlens, int batch, int s_q, int h_q,
-                                  int h_kv, int d_qk, int dv, const int32_t* plan,
-                                  const int32_t* num_splits, int num_workers, int causal,
-                                  float softmax_scale, const int32_t* indices, int topk, void* o,
-                                  float* lse, void* workspace, size_t workspace_bytes, int phases,
-                                  void* stream) {
+}  // extern "C"
+
+namespace {
+// The decode for both cache formats (kv_format 0: bf16 rows of d_qk values;
+// 1: packed FP8 rows of kRowBytes8 bytes holding d_qk values).
+int decode_impl(const void* q, const void* kvcache, int64_t num_pages, int page_size,
+                const int32_t* block_table, int max_blocks, const int32_t* cache_seqlens,
+                int batch, int s_q, int h_q, int h_kv, int d_qk, int dv, const int32_t* plan,
+                const int32_t* num_splits, int num_workers, int causal, float softmax_scale,
+                const int32_t* indices, int topk, void* o, float* lse, void* workspace,
+                size_t workspace_bytes, int kv_format, int phases, void* stream) {
   if (phases < 1 || phases > 3) return MLA_ERR_INVALID_ARGUMENT;
   if (batch < 0 || s_q < 1 || h_q < 1 || h_kv < 1 || max_blocks < 1 || num_pages < 1)
     return MLA_ERR_INVALID_ARGUMENT;
@@ -199,6 +202,7 @@ int mla_decode_with_kvcache_phase(const void* q, const void* kvcache, int64_t nu
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.h_kv = h_kv;
   a.G = h_q / h_kv;
+  a.kv_format = kv_format;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   if (phases & 1) {
     if (launch_decode(a, s.variant, hs) != hipSuccess) return MLA_ERR_HIP;
@@ -209,6 +213,24 @@ int mla_decode_with_kvcache_phase(const void* q, const void* kvcache, int64_t nu
   return MLA_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+int mla_decode_with_kvcache_phase(const void* q, const void* kvcache, int64_t num_pages,
+                                  int page_size, const int32_t* block_table, int max_blocks,
+                                  const int32_t* cache_seqlens, int batch, int s_q, int h_q,
+                                  int h_kv, int d_qk, int dv, const int32_t* plan,
+                                  const int32_t* num_splits, int num_workers, int causal,
+                                  float softmax_scale, const int32_t* indices, int topk, void* o,
+                                  float* lse, void* workspace, size_t workspace_bytes, int phases,
+                                  void* stream) {
+  return decode_impl(q, kvcache, num_pages, page_size, block_table, max_blocks, cache_seqlens,
+                     batch, s_q, h_q, h_kv, d_qk, dv, plan, num_splits, num_workers, causal,
+                     softmax_scale, indices, topk, o, lse, workspace, workspace_bytes, 0, phases,
+                     stream);
+}
+
 int mla_decode_with_kvcache(const void* q, const void* kvcache, int64_t num_pages, int page_size,
                             const int32_t* block_table, int max_blocks,
                             const int32_t* cache_seqlens, int batch, int s_q, int h_q, int h_kv,
@@ -216,10 +238,36 @@ int mla_decode_with_kvcache(const void* q, const void* kvcache, int64_t num_page
                             int num_workers, int causal, float softmax_scale,
                             const int32_t* indices, int topk, void* o, float* lse,
                             void* workspace, size_t workspace_bytes, void* stream) {
-  return mla_decode_with_kvcache_phase(q, kvcache, num_pages, page_size, block_table, max_blocks,
-                                       cache_seqlens, batch, s_q, h_q, h_kv, d_qk, dv, plan,
-                                       num_splits, num_workers, causal, softmax_scale, indices,
-                                       topk, o, lse, workspace, workspace_bytes, 3, stream);
+  return decode_impl(q, kvcache, num_pages, page_size, block_table, max_blocks, cache_seqlens,
+                     batch, s_q, h_q, h_kv, d_qk, dv, plan, num_splits, num_workers, causal,
+                     softmax_scale, indices, topk, o, lse, workspace, workspace_bytes, 0, 3, stream);
+}
+
+int mla_decode_with_kvcache_fp8_phase(const void* q, const void* kvcache, int64_t num_pages,
+                                      int page_size, const int32_t* block_table, int max_blocks,
+                                      const int32_t* cache_seqlens, int batch, int s_q, int h_q,
+                                      int h_kv, int d_qk, int dv, const int32_t* plan,
+                                      const int32_t* num_splits, int num_workers, int causal,
+                                      float softmax_scale, const int32_t* indices, int topk,
+                                      void* o, float* lse, void* workspace,
+                                      size_t workspace_bytes, int phases, void* stream) {
+  return decode_impl(q, kvcache, num_pages, page_size, block_table, max_blocks, cache_seqlens,
+                     batch, s_q, h_q, h_kv, d_qk, dv, plan, num_splits, num_workers, causal,
+                     softmax_scale, indices, topk, o, lse, workspace, workspace_bytes, 1, phases,
+                     stream);
+}
+
+int mla_decode_with_kvcache_fp8(const void* q, const void* kvcache, int64_t num_pages,
+                                int page_size, const int32_t* block_table, int max_blocks,
+                                const int32_t* cache_seqlens, int batch, int s_q, int h_q,
+                                int h_kv, int d_qk, int dv, const int32_t* plan,
+                                const int32_t* num_splits, int num_workers, int causal,
+                                float softmax_scale, const int32_t* indices, int topk, void* o,
+                                float* lse, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  return decode_impl(q, kvcache, num_pages, page_size, block_table, max_blocks, cache_seqlens,
+                     batch, s_q, h_q, h_kv, d_qk, dv, plan, num_splits, num_workers, causal,
+                     softmax_scale, indices, topk, o, lse, workspace, workspace_bytes, 1, 3, stream);
 }
 
 int mla_debug_row_ids(const int32_t* block_table, int max_blocks, const int32_t* cache_seqlens,

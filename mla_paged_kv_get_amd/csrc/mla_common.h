@@ -14,6 +14,11 @@ constexpr int kDv = 512;                  // V = first 512 values of the row
 constexpr int kRowBytes = kDqk * 2;       // 1152 B per cached row
 constexpr int kChunks = kRowBytes / 16;   // 72 chunks of 16 B per row
 constexpr int kTileBytes = kPage * kRowBytes;  // 73728 B per 64-row tile
+// Packed FP8 rows: 512 E4M3 latent codes, 4 float32 scales (one per 128
+// latent values), 64 bf16 RoPE values.
+constexpr int kRowBytes8 = 656;
+constexpr int kRaw8Bytes = kPage * kRowBytes8;     // 41984 B per 64-row tile as copied
+constexpr int kRaw8ScaleOff = kPage * 640;         // scales of a copied tile: [4 blocks][64 rows] float32
 constexpr int kPlanWords = 8;
 constexpr int kPlanVersion = 2;
 
@@ -64,6 +69,7 @@ struct DecodeArgs {
   float scale_log2;           // softmax_scale * log2(e)
   int h_kv;                   // latent KV heads (items are (sequence or query token, KV head))
   int G;                      // query heads per KV head, h_q / h_kv
+  int kv_format;              // 0: bf16 rows; 1: packed FP8 rows
 };
 
 // Row of q / o / lse ([batch * s_q * h_q] rows) holding query row `row` of

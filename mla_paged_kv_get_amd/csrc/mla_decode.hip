@@ -58,6 +58,12 @@ constexpr float kLazy = 8.f;   // log2 of the growth allowed before a rescale
 // the transposed reads.
 __device__ __forceinline__ int swz(int t) { return (((t & 3) << 1) | ((t >> 2) & 1)) ^ (((t >> 3) & 1) << 1); }
 
+// XOR pattern of the 16-byte chunks of segment sg of row t in a copied FP8
+// tile.  The expansion reads one segment per thread; with this pattern the 16
+// lanes (4 rows x 4 segments) of each quarter wave hit 16 distinct 16-byte
+// bank groups.
+__device__ __forceinline__ int raw8_swz(int t, int sg) { return ((sg & 3) << 1) | ((t >> 1) & 1); }
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Reductions over lane pairs (l, l ^ 32) and (l, l ^ 16) with the gfx950 lane
@@ -99,17 +105,31 @@ __device__ __forceinline__ bf16x4 read_tr(const char* p) {
 //    the probabilities with its partner through LDS.
 // In both, the waves sharing a row share its softmax reference, so no partial
 // outputs are merged when a run ends.
-template <int V>
+// With packed FP8 rows (KV8) the tiles are copied as they are stored (41 KB
+// per 64 rows) into the two stages, and each step first expands its tile into
+// a third buffer in the bf16 tile layout above: the E4M3 codes themselves
+// (every one is a bf16 value) and the RoPE values.  The block scales stay
+// out of the bf16 operands, so no dequantized value is rounded: QK^T keeps
+// one accumulation per 128-value block and adds them up with the keys'
+// scales, and PV takes each key's scale (for the output columns' block) into
+// its probability.
+template <int V, bool KV8>
 struct Cfg {
   static constexpr bool kWide = V == kVariantRows64;
   static constexpr int kWaves = 4;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int kRows = kWide ? 64 : 16;          // query rows per workgroup
-  static constexpr int kLoads = 72 / kWaves;             // 1 KB copy instructions per wave per tile
-  static constexpr int kLaneRows = (kLoads + 8) / 9;     // tile rows each lane copies
+  // Copy instructions per wave per tile.  bf16: the wave's 16 rows x 9
+  // chunk groups of 128 B.  FP8: its 16 rows x 5 segments of 128 B (latent
+  // bytes 0..511, RoPE bytes 528..655), plus four 4-byte copies that put the
+  // 16 rows' scales of each block into a [block][row] table.
+  static constexpr int kLoads = KV8 ? 14 : 18;
+  static constexpr int kLaneRows = 2;                    // tile rows each lane copies (8 lanes per row)
+  static constexpr int kOffs = KV8 ? 3 : 2;              // copy offsets per lane (FP8: + the scale row)
+  static constexpr int kRowB = KV8 ? kRowBytes8 : kRowBytes;   // bytes per cached row
+  static constexpr int kStageBytes = KV8 ? kRaw8Bytes : kTileBytes;
   static constexpr int kQf = kWide ? 36 : 18;            // bf16x8 B-operand fragments of Q per lane
   static constexpr int kRowsPerWave = kWide ? 32 : 16;   // rows of the softmax state a wave holds
-  static_assert(72 % kWaves == 0 && kLoads % 9 == 0, "tile copy must split evenly");
 };
 
 // s_waitcnt operand (gfx9 layout: vmcnt in bits 3:0 and 15:14, expcnt 6:4,
@@ -262,18 +282,20 @@ __device__ __forceinline__ void merge_row(const DecodeArgs& a, int item, int slo
   if (lane == 0) a.lse[orow] = tot > 0.f ? mx + logf(tot) : -INFINITY;
 }
 
-template <int V, bool SPARSE>
+template <int V, bool SPARSE, bool KV8>
 __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
-  using C = Cfg<V>;
+  using C = Cfg<V, KV8>;
   constexpr bool kWide = C::kWide;
   constexpr int kRw = C::kRowsPerWave;
   // vector-memory operations issued per wave for a tile: copy, sparse index loads
-  constexpr int kRaw = C::kLaneRows;
+  constexpr int kRaw = C::kOffs;
   constexpr int kWaitKeepCopy = waitcnt_vm(C::kLoads);
   constexpr int kWaitKeepRawCopy = waitcnt_vm(C::kLoads + kRaw);
   static_assert(C::kLoads + kRaw < 64, "vmcnt holds 6 bits");
-  __shared__ __attribute__((aligned(1024))) char s0[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char s1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char s0[C::kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char s1[C::kStageBytes];
+  // FP8: the current tile expanded to bf16 (the layout of a bf16 stage)
+  __shared__ __attribute__((aligned(1024))) char tbuf[KV8 ? kTileBytes : 16];
   __shared__ __attribute__((aligned(16))) unsigned char kvalid[4][64];   // sparse key validity, tile t -> t & 3
   __shared__ float red_m[4][kRw];     // per-wave row maxima of the tile
   __shared__ float red_l[4][kRw];     // per-wave row sums at the end of a run
@@ -281,7 +303,11 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
   // Probabilities of the tile in bf16.  Rows16: P^T [row][key pair block c][lane
   // group g][8], slot 4 h + i of (c, g) = key 16 (2 c + h) + 4 g + i.  Wide: the
   // B operands of the wave's two PV k-steps, [wave][k-step][lane][8].
-  __shared__ __attribute__((aligned(16))) char pbuf[kWide ? 4 * 2 * 64 * 16 : 16 * 128];
+  // (Wide FP8: in the copied stage of the tile being computed, which is free
+  // once it has been expanded; there is no room for it elsewhere.)
+  __shared__ __attribute__((aligned(16))) char pbuf_s[(kWide && KV8) ? 16 : (kWide ? 4 * 2 * 64 * 16 : 16 * 128)];
+  char* pbuf = pbuf_s;
+  const float* sc_tab = nullptr;   // FP8: scale table [block][row] of the tile being computed
   // Wide: index data of the next tiles (sparse: the 64 index-list entries;
   // dense: the page id, in every entry), copied in by each wave ([tile & 3]
   // [wave][64]) so that neither a register load left behind a tile copy nor a
@@ -358,12 +384,12 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
           v_x[e][b] = (((4 * b + 2 * (g & 1) + ((li & 3) >> 1)) ^ swz(tv + 8 * e)) << 4);
     }
 
-    // Tile rows this lane copies: t = 8 * (wave * kLoads / 9 + r) + lane / 8.
+    // Tile rows this lane copies: t = 8 * (2 wave + r) + lane / 8 (the wave's 16 rows).
     int cp_row[C::kLaneRows];
     int cp_swz[C::kLaneRows];
 #pragma unroll
     for (int r = 0; r < C::kLaneRows; ++r) {
-      cp_row[r] = 8 * (wave * C::kLoads / 9 + r) + (lane >> 3);
+      cp_row[r] = 8 * (2 * wave + r) + (lane >> 3);
       cp_swz[r] = swz(cp_row[r]);
     }
     const char* kv_bytes = reinterpret_cast<const char*>(a.kv);
@@ -414,8 +440,10 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     // tile_finish turns it into byte offsets (in the cache) of the rows this
     // lane copies, and the sparse key validity of the tile.
     struct TileRaw {
-      int v[C::kLaneRows];
+      int v[C::kOffs];
     };
+    // FP8: the row whose scales this lane copies (lanes 0..15 of the wave)
+    const int sc_row = 16 * wave + (lane & 15);
     auto tile_fetch = [&](int item, int blk, TileRaw& raw) __attribute__((always_inline)) {
       if constexpr (!sparse) {
         raw.v[0] = read_scalar(a.block_table + (int64_t)item_seq(a, item) * a.max_blocks + blk);   // not a vector load
@@ -426,9 +454,13 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
           const int sl = blk * kPage + cp_row[r];
           raw.v[r] = sl < a.topk ? idx_row[sl] : -1;
         }
+        if constexpr (KV8) {
+          const int sl = blk * kPage + sc_row;
+          raw.v[2] = sl < a.topk ? idx_row[sl] : -1;
+        }
       }
     };
-    auto tile_finish = [&](int item, int blk, const TileRaw& raw, int64_t (&off)[C::kLaneRows],
+    auto tile_finish = [&](int item, int blk, const TileRaw& raw, int64_t (&off)[C::kOffs],
                            unsigned char* vslot) __attribute__((always_inline)) {
       const int L = item_len(item);
       const int kvh = item % a.h_kv;      // latent KV head of the item
@@ -438,8 +470,9 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int r = 0; r < C::kLaneRows; ++r) {
           const int t = min(cp_row[r], nvalid - 1);
-          off[r] = ((page * kPage + t) * a.h_kv + kvh) * (int64_t)kRowBytes;
+          off[r] = ((page * kPage + t) * a.h_kv + kvh) * (int64_t)C::kRowB;
         }
+        if constexpr (KV8) off[2] = ((page * kPage + min(sc_row, nvalid - 1)) * a.h_kv + kvh) * (int64_t)C::kRowB;
       } else {
         const int32_t* bt_row = a.block_table + (int64_t)item_seq(a, item) * a.max_blocks;
 #pragma unroll
@@ -448,19 +481,37 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
           const bool ok = sparse_key_valid(idx, L);
           // padding reads the sequence's first row (page 0 of the pool if it has none)
           const int64_t crow = ok ? cache_row(bt_row, idx) : (L > 0 ? cache_row(bt_row, 0) : 0);
-          off[r] = (crow * a.h_kv + kvh) * (int64_t)kRowBytes;
+          off[r] = (crow * a.h_kv + kvh) * (int64_t)C::kRowB;
           if ((lane & 7) == 0) vslot[cp_row[r]] = ok ? 1 : 0;
+        }
+        if constexpr (KV8) {
+          const int idx = raw.v[2];
+          const int64_t crow = sparse_key_valid(idx, L) ? cache_row(bt_row, idx) : (L > 0 ? cache_row(bt_row, 0) : 0);
+          off[2] = (crow * a.h_kv + kvh) * (int64_t)C::kRowB;
         }
       }
     };
     // Copy instruction j (0 .. kLoads - 1) of this wave for a tile: 8 rows x 128 B.
-    auto issue_one = [&](char* stage, const int64_t (&off)[C::kLaneRows], int j) __attribute__((always_inline)) {
-      const int ii = wave * C::kLoads + j;
-      const int r = j / 9, cl = j % 9;
-      const char* src = kv_bytes + off[r] + cl * 128 + (((lane & 7) ^ cp_swz[r]) << 4);
-      copy_to_lds_16(src, lds_addr(stage + ii * 1024));
+    // FP8 stage layout: segment sg (0..3: latent bytes 128 sg .., 4: RoPE) of
+    // row t at ((t / 8) * 5 + sg) * 1024 + (t % 8) * 128, its 16-byte chunks
+    // XOR-swizzled by raw8_swz; scale b of row t at kRaw8ScaleOff + 4 (64 b + t).
+    auto issue_one = [&](char* stage, const int64_t (&off)[C::kOffs], int j) __attribute__((always_inline)) {
+      if constexpr (!KV8) {
+        const int ii = wave * C::kLoads + j;
+        const int r = j / 9, cl = j % 9;
+        const char* src = kv_bytes + off[r] + cl * 128 + (((lane & 7) ^ cp_swz[r]) << 4);
+        copy_to_lds_16(src, lds_addr(stage + ii * 1024));
+      } else if (j < 10) {
+        const int r = j / 5, sg = j % 5;
+        const char* src = kv_bytes + off[r] + (sg < 4 ? sg * 128 : 528) +
+                          (((lane & 7) ^ raw8_swz(cp_row[r], sg)) << 4);
+        copy_to_lds_16(src, lds_addr(stage + ((2 * wave + r) * 5 + sg) * 1024));
+      } else if (lane < 16) {
+        const int b = j - 10;
+        copy_to_lds_4(kv_bytes + off[2] + 512 + 4 * b, lds_addr(stage + kRaw8ScaleOff + 256 * b + 64 * wave));
+      }
     };
-    auto issue = [&](char* stage, const int64_t (&off)[C::kLaneRows]) __attribute__((always_inline)) {
+    auto issue = [&](char* stage, const int64_t (&off)[C::kOffs]) __attribute__((always_inline)) {
 #pragma unroll
       for (int j = 0; j < C::kLoads; ++j) issue_one(stage, off, j);
     };
@@ -478,12 +529,52 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int r = 0; r < C::kLaneRows; ++r)
           raw.v[r] = blk * kPage + cp_row[r] < a.topk ? idxbuf[slot & 3][wave][cp_row[r]] : -1;
+        if constexpr (KV8) raw.v[2] = blk * kPage + sc_row < a.topk ? idxbuf[slot & 3][wave][sc_row] : -1;
       } else {
         raw.v[0] = idxbuf[slot & 3][wave][0];
       }
     };
 
-    int64_t off[C::kLaneRows];   // cache byte offsets of the rows this lane copies for the next tile issued
+    int64_t off[C::kOffs];   // cache byte offsets of the rows this lane copies for the next tile issued
+
+    // FP8: expand the copied tile `raw` into the bf16 tile layout in `tb`.
+    // Thread (row t, latent block b) writes the 128 codes of block b of row t
+    // as bf16 (exact) and moves RoPE chunks 2b, 2b + 1 as they are.
+    auto expand_tile = [&](const char* raw, char* tb) __attribute__((always_inline)) {
+      const int t = threadIdx.x >> 2, b = threadIdx.x & 3;
+      const int tr = t & 7, rb = t >> 3, sw = swz(t);
+      const char* src = raw + ((rb * 5 + b) << 10) + (tr << 7);
+      char* dst = tb + ((rb * 9) << 10) + (tr << 7);
+      const int sz = raw8_swz(t, b);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int pc = (i + b) & 7;      // 16 codes: latent values 128 b + 16 pc .. + 15
+        const uint4 u = *reinterpret_cast<const uint4*>(src + ((pc ^ sz) << 4));
+        const unsigned w4[4] = {u.x, u.y, u.z, u.w};
+        bf16x8 h[2];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w4[k], false);   // codes 4k, 4k + 1
+          const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w4[k], true);    // codes 4k + 2, 4k + 3
+          h[k >> 1][4 * (k & 1) + 0] = (__bf16)lo[0];
+          h[k >> 1][4 * (k & 1) + 1] = (__bf16)lo[1];
+          h[k >> 1][4 * (k & 1) + 2] = (__bf16)hi[0];
+          h[k >> 1][4 * (k & 1) + 3] = (__bf16)hi[1];
+        }
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int c = 16 * b + 2 * pc + e;       // bf16 chunk: values 8 c .. 8 c + 7
+          *reinterpret_cast<bf16x8*>(dst + ((c >> 3) << 10) + (((c & 7) ^ sw) << 4)) = h[e];
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int c = 2 * b + e;                 // RoPE chunk c -> bf16 chunk 64 + c
+        const uint4 u = *reinterpret_cast<const uint4*>(raw + ((rb * 5 + 4) << 10) + (tr << 7) +
+                                                        ((c ^ raw8_swz(t, 4)) << 4));
+        *reinterpret_cast<uint4*>(dst + (8 << 10) + ((c ^ sw) << 4)) = u;
+      }
+    };
 
     // Per-run state of this wave.
     using Acc = typename std::conditional<kWide, floatx16, floatx4>::type;
@@ -506,7 +597,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     // tile is headed for (its own share of that tile goes out later, from
     // `off_late`), so no register load has to complete behind a tile copy and
     // the copy of the next tile is not held back at the item boundary.
-    int64_t off_late[C::kLaneRows];
+    int64_t off_late[C::kOffs];
     auto issue_q = [&](char* stage, int item) __attribute__((always_inline)) {
       const char* q_bytes = reinterpret_cast<const char*>(a.q);
 #pragma unroll
@@ -555,10 +646,29 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int ks = 0; ks < 18; ++ks)
           kf[ks] = *reinterpret_cast<const bf16x8*>(stage + k_base + ((ks >> 1) << 10) + k_x[ks & 1]);
-#pragma unroll
-        for (int ks = 0; ks < 18; ++ks) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[ks], sacc, 0, 0, 0);
         // element i: key 16 tg + 4 g + i
         const int t0 = 16 * tg + 4 * g;
+        if constexpr (!KV8) {
+#pragma unroll
+          for (int ks = 0; ks < 18; ++ks) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[ks], sacc, 0, 0, 0);
+        } else {
+          // one accumulation per 128-value latent block (4 k-steps each), then
+          // the keys' block scales; the RoPE k-steps 16, 17 are not scaled
+          floatx4 sb[4];
+#pragma unroll
+          for (int b = 0; b < 4; ++b) sb[b] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < 16; ++ks)
+            sb[ks >> 2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[ks], sb[ks >> 2], 0, 0, 0);
+#pragma unroll
+          for (int ks = 16; ks < 18; ++ks) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[ks], sacc, 0, 0, 0);
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const floatx4 sc = *reinterpret_cast<const floatx4*>(sc_tab + 64 * b + t0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sacc[i] = __builtin_fmaf(sc[i], sb[b][i], sacc[i]);
+          }
+        }
         unsigned vb = 0;
         if constexpr (sparse) vb = *reinterpret_cast<const unsigned*>(vslot + t0);
 #pragma unroll
@@ -575,6 +685,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
         // written twice so that issuing the next tile's copy inside it costs
         // no branch per k-step.
         floatx16 sacc = {};
+        floatx16 sblk[KV8 ? 4 : 1] = {};   // FP8: one accumulation per latent block
         auto qk = [&](auto with_dma) __attribute__((always_inline)) {
           constexpr int kPre = 6;
           bf16x8 kf[kPre];
@@ -587,15 +698,34 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
             if (ks + kPre < 36)
               kf[ks % kPre] = *reinterpret_cast<const bf16x8*>(stage + k_base + (((ks + kPre) >> 2) << 10) +
                                                                k_x[(ks + kPre) & 3]);
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur, qf[ks], sacc, 0, 0, 0);
+            // FP8: each latent block (k-steps 8 b .. 8 b + 7) accumulates on
+            // its own; the RoPE k-steps go into sacc
+            if constexpr (KV8) {
+              if (ks < 32) sblk[ks >> 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur, qf[ks], sblk[ks >> 3], 0, 0, 0);
+              else sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur, qf[ks], sacc, 0, 0, 0);
+            } else {
+              sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur, qf[ks], sacc, 0, 0, 0);
+            }
             if constexpr (decltype(with_dma)::value) {
-              if ((ks & 1) == 0) issue_one(dma_stage, off, ks >> 1);
+              // one copy every second k-step (kLoads <= 18)
+              static_assert(C::kLoads <= 18, "the copies must fit the 36 k-steps");
+              if (ks % 2 == 0 && ks / 2 < C::kLoads) issue_one(dma_stage, off, ks / 2);
             }
             __builtin_amdgcn_sched_barrier(0);   // keep the reads kPre MFMAs ahead
           }
         };
         if (dma_stage != nullptr) qk(std::true_type{});
         else qk(std::false_type{});
+        if constexpr (KV8) {
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              const floatx4 sc = *reinterpret_cast<const floatx4*>(sc_tab + 64 * b + 32 * half + 8 * q4 + 4 * hl);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) sacc[4 * q4 + i] = __builtin_fmaf(sc[i], sblk[b][4 * q4 + i], sacc[4 * q4 + i]);
+            }
+        }
         // element r: key 32 half + 8 (r / 4) + 4 hl + r % 4.  Tiles whose keys
         // are all valid for every row of the wave skip the per-key mask.
         const bool full = !sparse && __builtin_amdgcn_ballot_w64(blk * kPage + 32 * half + 32 <= lim) ==
@@ -691,6 +821,19 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
         bf16x8 pb[2];
 #pragma unroll
         for (int c = 0; c < 2; ++c) pb[c] = *reinterpret_cast<const bf16x8*>(pbuf + li * 128 + c * 64 + g * 16);
+        if constexpr (KV8) {
+          // the wave's output columns are latent block tg: each key's scale for it
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const floatx4 s0 = *reinterpret_cast<const floatx4*>(sc_tab + 64 * tg + 32 * c + 4 * g);
+            const floatx4 s1 = *reinterpret_cast<const floatx4*>(sc_tab + 64 * tg + 32 * c + 16 + 4 * g);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              pb[c][i] = (__bf16)((float)pb[c][i] * s0[i]);
+              pb[c][4 + i] = (__bf16)((float)pb[c][4 + i] * s1[i]);
+            }
+          }
+        }
         constexpr int kPv = 6;
         auto vaddr = [&](int n, int e) __attribute__((always_inline)) -> const char* {
           const int c = n >> 3, dt = n & 7;
@@ -734,6 +877,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
           vq0[n] = read_tr(vaddr(n, 0));
           vq1[n] = read_tr(vaddr(n, 1));
         }
+        bf16x8 pbs;   // FP8: scaled probabilities of the current (k-step, block)
 #pragma unroll
         for (int n = 0; n < 32; ++n) {
           const bf16x8 va = __builtin_shufflevector(vq0[n % kPv], vq1[n % kPv], 0, 1, 2, 3, 4, 5, 6, 7);
@@ -741,7 +885,23 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
             vq0[n % kPv] = read_tr(vaddr(n + kPv, 0));
             vq1[n % kPv] = read_tr(vaddr(n + kPv, 1));
           }
-          oacc[n & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[n >> 3], oacc[n & 7], 0, 0, 0);
+          bf16x8 pbn = pb[n >> 3];
+          if constexpr (KV8) {
+            // columns of oacc[db] lie in latent block 2 half + db / 4: the
+            // probabilities of k-step j times the keys' scales for that block
+            if ((n & 3) == 0) {
+              const float* st = sc_tab + 64 * (2 * half + ((n & 7) >> 2)) + 16 * (n >> 3) + 4 * hl;
+              const floatx4 s0 = *reinterpret_cast<const floatx4*>(st);
+              const floatx4 s1 = *reinterpret_cast<const floatx4*>(st + 8);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                pbs[i] = (__bf16)((float)pbn[i] * s0[i]);
+                pbs[4 + i] = (__bf16)((float)pbn[4 + i] * s1[i]);
+              }
+            }
+            pbn = pbs;
+          }
+          oacc[n & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pbn, oacc[n & 7], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);   // keep the reads kPv MFMAs ahead
         }
       }
@@ -853,13 +1013,19 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
         // the index list of tile t + 1 before it): nothing else is in flight.
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         barrier_keep_loads();          // tile t in LDS for every wave; every wave is done with `nxt`
+        if constexpr (KV8) {
+          expand_tile(cur, tbuf);
+          barrier_keep_loads();        // the bf16 tile is complete
+          pbuf = cur;                  // the copied codes are free until tile t + 2 is copied in
+          sc_tab = reinterpret_cast<const float*>(cur + kRaw8ScaleOff);
+        }
         if (has_next) {
           idx_from_lds(nx_blk, t + 1, raw);
           tile_finish(nx_item, nx_blk, raw, off, kvalid[(t + 1) & 3]);
         }
         if (n2_item >= 0) idx_dma(n2_item, n2_blk, t + 2);
         const bool ends = !has_next || nx_item != cur_item;
-        compute(cur, kvalid[t & 3], cur_blk, cur_lim, has_next ? nxt : nullptr);
+        compute(KV8 ? tbuf : cur, kvalid[t & 3], cur_blk, cur_lim, has_next ? nxt : nullptr);
         if (ends) {
           finish(cur_item, cur_split);
           if (has_next) {
@@ -884,7 +1050,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
       if (has_next) {
         if (q_lds) {
 #pragma unroll
-          for (int r = 0; r < C::kLaneRows; ++r) off_late[r] = off[r];
+          for (int r = 0; r < C::kOffs; ++r) off_late[r] = off[r];
         } else {
           issue(nxt, off);
         }
@@ -903,17 +1069,22 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
         __builtin_amdgcn_s_waitcnt(0);     // wave 0 with staged query rows: tile t, then the rows
       }
       barrier_keep_loads();                              // tile t is in LDS for every wave
+      if constexpr (KV8) {
+        expand_tile(cur, tbuf);
+        barrier_keep_loads();                            // the bf16 tile is complete
+        sc_tab = reinterpret_cast<const float*>(cur + kRaw8ScaleOff);
+      }
       if (q_pending) q_from_lds(nxt);
       if (n2_item >= 0) tile_finish(n2_item, n2_blk, raw, off, kvalid[(t + 2) & 3]);
       const bool ends = !has_next || nx_item != cur_item;
-      compute(cur, kvalid[t & 3], cur_blk, cur_lim, q_lds && has_next ? nxt : nullptr);
+      compute(KV8 ? tbuf : cur, kvalid[t & 3], cur_blk, cur_lim, q_lds && has_next ? nxt : nullptr);
       q_pending = false;
       if (ends) {
         finish(cur_item, cur_split);
         if (has_next) {
           cur_lim = key_limit(nx_item);
           cur_split = 0;
-          if constexpr (sparse) {
+          if constexpr (sparse || KV8) {
             // Query rows of the next item, completed before the next copy is
             // issued (see the prologue).
             load_q(nx_item);
@@ -951,22 +1122,26 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   }
 }
 
-template <int V>
+template <int V, bool KV8>
 hipError_t launch_variant(const DecodeArgs& a, hipStream_t stream) {
   const int groups = (a.num_workers + 7) / 8;
   const int grid = a.m_tiles == 1 ? a.num_workers : groups * 8 * a.m_tiles;
   if (a.topk > 0)
-    hipLaunchKernelGGL((decode_kernel<V, true>), dim3(grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<V, true, KV8>), dim3(grid), dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((decode_kernel<V, false>), dim3(grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<V, false, KV8>), dim3(grid), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, int variant, hipStream_t stream) {
-  if (variant == kVariantRows16) return launch_variant<kVariantRows16>(a, stream);
-  return launch_variant<kVariantRows64>(a, stream);
+  if (a.kv_format == 1) {
+    if (variant == kVariantRows16) return launch_variant<kVariantRows16, true>(a, stream);
+    return launch_variant<kVariantRows64, true>(a, stream);
+  }
+  if (variant == kVariantRows16) return launch_variant<kVariantRows16, false>(a, stream);
+  return launch_variant<kVariantRows64, false>(a, stream);
 }
 
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream) {

@@ -231,6 +231,23 @@ def grouped_heads(poison: bool = False) -> Workload:
                  num_pages=1200, max_blocks=64, poison=poison, rng=rng)
 
 
+def memory_bound_fp8(poison: bool = False) -> Workload:
+    """The memory-bound decode shape over a packed FP8 cache (656-byte rows)."""
+    rng = np.random.default_rng(8)
+    lengths = rng.integers(1, 4097, size=64)
+    return build("memory-bound fp8 b64 h16 L~U[1,4096]", 8, lengths, B=64, s_q=1, h_q=16,
+                 num_pages=6000, max_blocks=64, poison=poison, rng=rng, kv_format="fp8")
+
+
+def sparse_topk_fp8(poison: bool = False, B: int = 16) -> Workload:
+    """The sparse top-k shape over a packed FP8 cache."""
+    rng = np.random.default_rng(9)
+    lengths = np.full(B, 65536)
+    return build(f"sparse-topk fp8 b{B} sq8 h128 L65536 k2048", 9, lengths, B=B, s_q=8, h_q=128,
+                 num_pages=B * 1024, max_blocks=1024, topk=2048, poison=poison, rng=rng,
+                 kv_format="fp8")
+
+
 NAMED = {
     "tiny": tiny,
     "memory_bound": memory_bound,
@@ -239,4 +256,6 @@ NAMED = {
     "sparse_topk": sparse_topk,
     "grouped_heads": grouped_heads,
     "sparse_prefill": sparse_prefill,
+    "memory_bound_fp8": memory_bound_fp8,
+    "sparse_topk_fp8": sparse_topk_fp8,
 }

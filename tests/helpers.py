@@ -14,6 +14,13 @@ def bits_to_dev(a: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
 
 
+def kv_to_dev(a: np.ndarray) -> torch.Tensor:
+    """bf16 cache (uint16 bit patterns) or packed FP8 cache (uint8 rows) to the GPU."""
+    if a.dtype == np.uint8:
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    return bits_to_dev(a)
+
+
 def i32_dev(a: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
 
@@ -24,7 +31,7 @@ class Dev:
     def __init__(self, w):
         self.w = w
         self.q = bits_to_dev(w.q)
-        self.kv = bits_to_dev(w.kv)
+        self.kv = kv_to_dev(w.kv)
         self.bt = i32_dev(w.block_table)
         self.sl = i32_dev(w.cache_seqlens)
         self.idx = i32_dev(w.indices) if w.indices is not None else None

@@ -115,6 +115,19 @@ def test_phase_argument_checked():
     assert l.mla_decode_with_kvcache_phase(*args, 4, None) == _lib.MLA_ERR_INVALID_ARGUMENT
 
 
+def test_fp8_entries_reject():
+    l = _lib.lib()
+    args = [DUMMY, DUMMY, 10, 64, DUMMY, 4, DUMMY, 2, 1, 16, 1, 576, 512, DUMMY, DUMMY, 8, 0,
+            ctypes.c_float(0.05), None, 0, DUMMY, DUMMY, DUMMY, 1 << 40]
+    assert l.mla_decode_with_kvcache_fp8_phase(*args, 0, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    bad_d = list(args)
+    bad_d[11] = 656                      # d_qk counts values, not bytes
+    assert l.mla_decode_with_kvcache_fp8(*bad_d, None) == _lib.MLA_ERR_UNSUPPORTED
+    bad_scale = list(args)
+    bad_scale[17] = ctypes.c_float(-1.0)
+    assert l.mla_decode_with_kvcache_fp8(*bad_scale, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+
+
 def test_metadata_rejects():
     l = _lib.lib()
     assert l.mla_get_metadata(DUMMY, 4, 1, 16, 1, 0, 8, None, DUMMY, None) == _lib.MLA_ERR_INVALID_ARGUMENT
