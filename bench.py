@@ -51,16 +51,20 @@ def algorithmic_work(w):
     L = w.cache_seqlens.astype(np.int64)
     h_kv = w.kv.shape[2]
     KV_ROW_BYTES = w.kv.shape[3] * w.kv.itemsize
+    d_qk = w.q.shape[3]
     if w.indices is not None:
         ok = (w.indices >= 0) & (w.indices < L[:, None, None])
         keys = int(ok.sum())
-        return keys * h_kv * KV_ROW_BYTES, keys * w.h_q * 2 * (576 + 512)
+        if w.aux is not None:      # dual cache: the auxiliary keys join each token's key set
+            idx2, L2 = w.aux[3], w.aux[2].astype(np.int64)
+            keys += int(((idx2 >= 0) & (idx2 < L2[:, None, None])).sum())
+        return keys * h_kv * KV_ROW_BYTES, keys * w.h_q * 2 * (d_qk + 512)
     kv = int(L.sum()) * h_kv * KV_ROW_BYTES
     if w.causal:
         qk = sum(w.h_q * max(int(l) - w.s_q + s + 1, 0) for l in L for s in range(w.s_q))
     else:
         qk = int(L.sum()) * w.s_q * w.h_q
-    return kv, qk * 2 * (576 + 512)
+    return kv, qk * 2 * (d_qk + 512)
 
 
 def gpu_sleep_ms(torch, ms):
@@ -90,7 +94,14 @@ def run_workload(torch, m, w, steps, warmup, ncopies=NCOPIES):
     kvs = [kv0] + [kv0.clone() for _ in range(ncopies - 1)]
     h_kv = w.kv.shape[2]
     rows = w.s_q * w.h_q // h_kv
-    plan, ns = m.get_mla_metadata(sl, rows, h_kv, s_q=w.s_q, topk=w.topk)
+    aux = None
+    topk2 = 0
+    if w.aux is not None:
+        kv2, bt2, sl2, idx2 = w.aux
+        aux = (_to_dev(torch, kv2.view(np.int16), torch.bfloat16), _to_dev(torch, bt2.astype(np.int32)),
+               _to_dev(torch, sl2.astype(np.int32)), _to_dev(torch, idx2.astype(np.int32)))
+        topk2 = idx2.shape[2]
+    plan, ns = m.get_mla_metadata(sl, rows, h_kv, s_q=w.s_q, topk=w.topk, topk2=topk2)
     W = plan.numel() // 8 - 1
     B = w.B
     o = torch.empty((B, w.s_q, w.h_q, 512), dtype=torch.bfloat16, device="cuda")
@@ -99,12 +110,12 @@ def run_workload(torch, m, w, steps, warmup, ncopies=NCOPIES):
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
 
     def plan_call(k):
-        return m.get_mla_metadata(sl, rows, h_kv, s_q=w.s_q, topk=w.topk)
+        return m.get_mla_metadata(sl, rows, h_kv, s_q=w.s_q, topk=w.topk, topk2=topk2)
 
     def decode_call(k, p, n, phases):
         c = k % ncopies
         m.mla_decode_with_kvcache(qs[c], kvs[c], bt, sl, 512, p, n, causal=w.causal, indices=idx,
-                                  out=(o, lse), workspace=ws, phases=phases)
+                                  out=(o, lse), workspace=ws, phases=phases, aux=aux)
 
     def step(k):
         p, n = plan_call(k)
@@ -207,11 +218,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="memory_bound",
                     choices=["tiny", "memory_bound", "near_ridge", "mtp_causal", "sparse_topk",
-                             "grouped_heads", "sparse_prefill", "memory_bound_fp8", "sparse_topk_fp8"])
+                             "grouped_heads", "sparse_prefill", "memory_bound_fp8", "sparse_topk_fp8",
+                             "dual_cache"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--secondary", action="store_true",
                     help="also time the near-ridge, MTP-causal, sparse top-k, grouped-heads, "
-                         "sparse-prefill and the two packed-FP8 workloads")
+                         "sparse-prefill, the two packed-FP8 and the dual-cache workloads")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run plain device copies of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -250,7 +262,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "s_q": w.s_q, "h_q": w.h_q, "h_kv": int(w.kv.shape[2]),
-                   "d_qk": 576, "dv": 512, "page": 64, "causal": bool(w.causal),
+                   "d_qk": int(w.q.shape[3]), "dv": 512, "page": 64, "causal": bool(w.causal),
                    "topk": w.topk, "kv_bytes": kv_bytes, "flops": flops,
                    "num_workers": r["num_workers"], "kv_copies_rotated": NCOPIES},
         "tflops": round(flops / step_s / 1e12, 3),
@@ -266,7 +278,7 @@ def main():
     if args.secondary:
         sec = {}
         for name in ("near_ridge", "mtp_causal", "sparse_topk", "grouped_heads", "sparse_prefill",
-                     "memory_bound_fp8", "sparse_topk_fp8"):
+                     "memory_bound_fp8", "sparse_topk_fp8", "dual_cache"):
             w2 = wl.NAMED[name]()
             kb, fl = algorithmic_work(w2)
             r2 = run_workload(torch, m, w2, max(10, args.steps // 2), 3)

@@ -35,7 +35,8 @@
  *   indices      [batch, s_q, topk]             int32, device (sparse mode only)
  *   o            [batch, s_q, h_q, dv]          bf16, device (output)
  *   lse          [batch, s_q, h_q]              fp32, device (output)
- * Supported: d_qk = 576, dv = 512, page size 64, any h_kv dividing h_q.  With
+ * Supported: d_qk = 576 or 512 (bf16 caches; packed FP8 caches hold 576
+ * values), dv = 512, page size 64, any h_kv dividing h_q.  With
  * h_kv > 1 latent heads (grouped latent attention), query head h uses KV head
  * h / (h_q / h_kv); row (page * 64 + slot) of head g sits at element offset
  * ((page * 64 + slot) * h_kv + g) * d_qk of kvcache.
@@ -154,6 +155,10 @@ size_t mla_workspace_bytes(int batch, int s_q, int num_q_rows, int h_kv, int top
  *   num_pages       pages in kvcache (used to check the plan's bounds only on
  *                   the validation call; not read by the kernels)
  *   page_size       must be 64
+ *   d_qk, dv        d_qk = 576 (512 latent + 64 RoPE values per row; V = the
+ *                   first 512) or 512 (the d_qk = 512 rows named by "FlashInfer,
+ *                   SM120 GPU를 위한 희소 MLA 커널", 들어가며; V = the whole row);
+ *                   dv = 512
  *   max_blocks      columns of block_table
  *   plan, num_splits, num_workers   from mla_get_metadata with the same
  *                   lengths / batch / s_q / topk and num_q_rows = s_q*h_q/h_kv
@@ -224,6 +229,34 @@ int mla_decode_with_kvcache_fp8_phase(const void* q, const void* kvcache, int64_
                                       float softmax_scale, const int32_t* indices, int topk,
                                       void* o, float* lse, void* workspace,
                                       size_t workspace_bytes, int phases, void* stream);
+
+/*
+ * mla_decode_with_kvcache_dual — sparse decode over two caches at once (the
+ * dual-cache scenario, a main and an auxiliary cache used together:
+ * "FlashInfer, SM120 GPU를 위한 희소 MLA 커널", section "코드 분석", item 1).
+ * Query token (b, s) attends to the union of its main-list keys
+ * (indices[b, s, :topk] into the main cache, valid below cache_seqlens[b])
+ * and its auxiliary-list keys (indices2[b, s, :topk2] into the auxiliary
+ * cache, valid below cache_seqlens2[b]), with one softmax over both; entries
+ * outside [0, L) of their list are padding.  Both caches are bf16 [pages, 64,
+ * h_kv, d_qk] with their own block tables; d_qk is 576 or 512 (the same rows
+ * as mla_decode_with_kvcache).  The plan comes from mla_get_metadata with
+ * topk = 64 * (ceil(topk / 64) + ceil(topk2 / 64)): every item has that many
+ * 64-key tiles, the main list's first.  topk2 may be 0 (indices2 NULL).
+ * causal is not an argument (sparse mode); the other arguments, checks and
+ * phases are those of mla_decode_with_kvcache_phase.
+ */
+int mla_decode_with_kvcache_dual(const void* q, const void* kvcache, int64_t num_pages,
+                                 const int32_t* block_table, int max_blocks,
+                                 const int32_t* cache_seqlens, const int32_t* indices, int topk,
+                                 const void* kvcache2, int64_t num_pages2,
+                                 const int32_t* block_table2, int max_blocks2,
+                                 const int32_t* cache_seqlens2, const int32_t* indices2, int topk2,
+                                 int page_size, int batch, int s_q, int h_q, int h_kv, int d_qk,
+                                 int dv, const int32_t* plan, const int32_t* num_splits,
+                                 int num_workers, float softmax_scale, void* o, float* lse,
+                                 void* workspace, size_t workspace_bytes, int phases,
+                                 void* stream);
 
 /*
  * mla_debug_row_ids — indexing probe (test use).  Writes, through the same

@@ -58,17 +58,21 @@ def workspace_bytes(batch, s_q, num_q_rows, h_kv, topk, dv, num_workers) -> int:
 
 
 def get_mla_metadata(cache_seqlens: torch.Tensor, num_q_rows: int, h_kv: int, *, s_q: int = 1,
-                     topk: int | None = None, num_workers: int | None = None):
+                     topk: int | None = None, num_workers: int | None = None, topk2: int = 0):
     """Split-KV plan: returns ``(tile_scheduler_metadata, num_splits)`` (int32, device).
 
     ``num_q_rows`` is s_q * h_q / h_kv as in the pages' call.  In sparse mode
     (``topk`` given) every query token is an item of ``topk`` keys and ``s_q``
-    must be passed.
+    must be passed; with an auxiliary cache (dual-cache decode) ``topk2`` is
+    the length of its index lists.
     """
     _i32(cache_seqlens, "cache_seqlens")
     _need(cache_seqlens.is_cuda, "cache_seqlens must be on the GPU")
     batch = cache_seqlens.numel()
     tk = int(topk or 0)
+    if topk2:
+        _need(tk > 0, "topk2 needs topk (dual-cache decode is sparse)")
+        tk = 64 * (-(-tk // 64) + -(-int(topk2) // 64))
     W, words, items = plan_dims(batch, s_q, num_q_rows, h_kv, tk, int(num_workers or 0))
     dev = cache_seqlens.device
     plan = torch.empty(words, dtype=torch.int32, device=dev)
@@ -84,14 +88,17 @@ def mla_decode_with_kvcache(q: torch.Tensor, kvcache: torch.Tensor, block_table:
                             num_splits: torch.Tensor, causal: bool = False,
                             softmax_scale: float | None = None, indices: torch.Tensor | None = None,
                             out: tuple | None = None, workspace: torch.Tensor | None = None,
-                            phases: int = 3):
+                            phases: int = 3, aux: tuple | None = None):
     """Paged MLA decode; returns ``(o [b, s_q, h_q, dv] bf16, lse [b, s_q, h_q] fp32)``.
 
     ``kvcache`` is bf16 ``[pages, 64, h_kv, 576]``, or uint8 ``[pages, 64, h_kv,
     656]`` for packed FP8 rows (512 E4M3 latent codes, 4 float32 block scales,
     64 bf16 RoPE values).  ``phases`` (1 = split kernel, 2 = merge kernel, 3 =
     both) lets a caller launch the two kernels separately with the same
-    arguments and buffers.
+    arguments and buffers.  ``aux = (kvcache2, block_table2, cache_seqlens2,
+    indices2)`` adds an auxiliary bf16 cache (sparse mode): each query token
+    attends to the union of its keys in both caches; the plan then comes from
+    ``get_mla_metadata(..., topk=topk, topk2=indices2.shape[2])``.
     """
     _as_bits(q, "q")
     fp8 = kvcache.dtype == torch.uint8
@@ -133,6 +140,25 @@ def mla_decode_with_kvcache(q: torch.Tensor, kvcache: torch.Tensor, block_table:
     need = workspace_bytes(B, s_q, num_q_rows, h_kv, topk, dv, W) if dv > 0 else 0
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    if aux is not None:
+        kv2, bt2, sl2, idx2 = aux
+        _need(indices is not None and not fp8, "an auxiliary cache needs sparse mode and bf16 caches")
+        _as_bits(kv2, "kvcache2")
+        _i32(bt2, "block_table2")
+        _i32(sl2, "cache_seqlens2")
+        _i32(idx2, "indices2")
+        _need(kv2.dim() == 4 and kv2.shape[1] == page and kv2.shape[2] == h_kv and kv2.shape[3] == d,
+              "kvcache2 is [pages2, 64, h_kv, d_qk]")
+        _need(bt2.dim() == 2 and bt2.shape[0] == B and sl2.numel() == B, "block_table2 / cache_seqlens2 per sequence")
+        _need(idx2.dim() == 3 and tuple(idx2.shape[:2]) == (B, s_q), "indices2 is [b, s_q, topk2]")
+        _lib.check(_lib.lib().mla_decode_with_kvcache_dual(
+            _ptr(q), _ptr(kvcache), num_pages, _ptr(block_table), block_table.shape[1], _ptr(cache_seqlens),
+            _ptr(indices), topk, _ptr(kv2), kv2.shape[0], _ptr(bt2), bt2.shape[1], _ptr(sl2),
+            _ptr(idx2) if idx2.shape[2] > 0 else None, idx2.shape[2], page, B, s_q, h_q, h_kv, d, dv,
+            _ptr(tile_scheduler_metadata), _ptr(num_splits), W, ctypes.c_float(scale), _ptr(o), _ptr(lse),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), int(phases), _stream(dev)),
+            "mla_decode_with_kvcache_dual")
+        return o, lse
     entry = _lib.lib().mla_decode_with_kvcache_fp8_phase if fp8 else _lib.lib().mla_decode_with_kvcache_phase
     _lib.check(entry(
         _ptr(q), _ptr(kvcache), num_pages, page, _ptr(block_table), block_table.shape[1],

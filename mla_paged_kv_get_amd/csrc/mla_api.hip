@@ -145,19 +145,40 @@ size_t mla_workspace_bytes(int batch, int s_q, int num_q_rows, int h_kv, int top
 }  // extern "C"
 
 namespace {
+// The auxiliary cache of the dual-cache sparse decode.
+struct AuxCache {
+  const void* kv;
+  int64_t num_pages;
+  const int32_t* block_table;
+  int max_blocks;
+  const int32_t* seqlens;
+  const int32_t* indices;
+  int topk;
+};
+
 // The decode for both cache formats (kv_format 0: bf16 rows of d_qk values;
-// 1: packed FP8 rows of kRowBytes8 bytes holding d_qk values).
+// 1: packed FP8 rows of kRowBytes8 bytes holding d_qk values), with an
+// optional auxiliary cache (sparse mode only).
 int decode_impl(const void* q, const void* kvcache, int64_t num_pages, int page_size,
                 const int32_t* block_table, int max_blocks, const int32_t* cache_seqlens,
                 int batch, int s_q, int h_q, int h_kv, int d_qk, int dv, const int32_t* plan,
                 const int32_t* num_splits, int num_workers, int causal, float softmax_scale,
                 const int32_t* indices, int topk, void* o, float* lse, void* workspace,
-                size_t workspace_bytes, int kv_format, int phases, void* stream) {
+                size_t workspace_bytes, int kv_format, const AuxCache* aux, int phases,
+                void* stream) {
   if (phases < 1 || phases > 3) return MLA_ERR_INVALID_ARGUMENT;
   if (batch < 0 || s_q < 1 || h_q < 1 || h_kv < 1 || max_blocks < 1 || num_pages < 1)
     return MLA_ERR_INVALID_ARGUMENT;
   if (h_q % h_kv) return MLA_ERR_INVALID_ARGUMENT;
-  if (page_size != kPage || d_qk != kDqk || dv != kDv) return MLA_ERR_UNSUPPORTED;
+  if (page_size != kPage || dv != kDv) return MLA_ERR_UNSUPPORTED;
+  if (d_qk != kDqk && !(d_qk == 512 && kv_format == 0)) return MLA_ERR_UNSUPPORTED;
+  if (aux) {
+    if (topk <= 0 || aux->topk < 0 || aux->num_pages < 1 || aux->max_blocks < 1 || !aux->kv ||
+        !aux->block_table || !aux->seqlens || (aux->topk > 0) != (aux->indices != nullptr))
+      return MLA_ERR_INVALID_ARGUMENT;
+    if ((int64_t)aux->max_blocks * kPage > (int64_t)0x7fffffff) return MLA_ERR_INVALID_ARGUMENT;
+    if (aux->num_pages > ((int64_t)1 << 31) / kPage) return MLA_ERR_UNSUPPORTED;
+  }
   if (causal != 0 && causal != 1) return MLA_ERR_INVALID_ARGUMENT;
   if ((indices != nullptr) != (topk > 0)) return MLA_ERR_INVALID_ARGUMENT;
   if (indices && causal) return MLA_ERR_INVALID_ARGUMENT;
@@ -203,6 +224,24 @@ int decode_impl(const void* q, const void* kvcache, int64_t num_pages, int page_
   a.h_kv = h_kv;
   a.G = h_q / h_kv;
   a.kv_format = kv_format;
+  a.d_qk = d_qk;
+  a.nb1 = topk > 0 ? (topk + kPage - 1) / kPage : 0;
+  a.nb_sparse = a.nb1;
+  a.kv2 = nullptr;
+  a.block_table2 = nullptr;
+  a.seqlens2 = nullptr;
+  a.indices2 = nullptr;
+  a.max_blocks2 = 0;
+  a.topk2 = 0;
+  if (aux && aux->topk > 0) {
+    a.kv2 = static_cast<const uint16_t*>(aux->kv);
+    a.block_table2 = aux->block_table;
+    a.seqlens2 = aux->seqlens;
+    a.indices2 = aux->indices;
+    a.max_blocks2 = aux->max_blocks;
+    a.topk2 = aux->topk;
+    a.nb_sparse += (aux->topk + kPage - 1) / kPage;
+  }
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   if (phases & 1) {
     if (launch_decode(a, s.variant, hs) != hipSuccess) return MLA_ERR_HIP;
@@ -227,8 +266,8 @@ int mla_decode_with_kvcache_phase(const void* q, const void* kvcache, int64_t nu
                                   void* stream) {
   return decode_impl(q, kvcache, num_pages, page_size, block_table, max_blocks, cache_seqlens,
                      batch, s_q, h_q, h_kv, d_qk, dv, plan, num_splits, num_workers, causal,
-                     softmax_scale, indices, topk, o, lse, workspace, workspace_bytes, 0, phases,
-                     stream);
+                     softmax_scale, indices, topk, o, lse, workspace, workspace_bytes, 0, nullptr,
+                     phases, stream);
 }
 
 int mla_decode_with_kvcache(const void* q, const void* kvcache, int64_t num_pages, int page_size,
@@ -240,7 +279,8 @@ int mla_decode_with_kvcache(const void* q, const void* kvcache, int64_t num_page
                             void* workspace, size_t workspace_bytes, void* stream) {
   return decode_impl(q, kvcache, num_pages, page_size, block_table, max_blocks, cache_seqlens,
                      batch, s_q, h_q, h_kv, d_qk, dv, plan, num_splits, num_workers, causal,
-                     softmax_scale, indices, topk, o, lse, workspace, workspace_bytes, 0, 3, stream);
+                     softmax_scale, indices, topk, o, lse, workspace, workspace_bytes, 0, nullptr, 3,
+                     stream);
 }
 
 int mla_decode_with_kvcache_fp8_phase(const void* q, const void* kvcache, int64_t num_pages,
@@ -253,8 +293,8 @@ int mla_decode_with_kvcache_fp8_phase(const void* q, const void* kvcache, int64_
                                       size_t workspace_bytes, int phases, void* stream) {
   return decode_impl(q, kvcache, num_pages, page_size, block_table, max_blocks, cache_seqlens,
                      batch, s_q, h_q, h_kv, d_qk, dv, plan, num_splits, num_workers, causal,
-                     softmax_scale, indices, topk, o, lse, workspace, workspace_bytes, 1, phases,
-                     stream);
+                     softmax_scale, indices, topk, o, lse, workspace, workspace_bytes, 1, nullptr,
+                     phases, stream);
 }
 
 int mla_decode_with_kvcache_fp8(const void* q, const void* kvcache, int64_t num_pages,
@@ -267,7 +307,27 @@ int mla_decode_with_kvcache_fp8(const void* q, const void* kvcache, int64_t num_
                                 void* stream) {
   return decode_impl(q, kvcache, num_pages, page_size, block_table, max_blocks, cache_seqlens,
                      batch, s_q, h_q, h_kv, d_qk, dv, plan, num_splits, num_workers, causal,
-                     softmax_scale, indices, topk, o, lse, workspace, workspace_bytes, 1, 3, stream);
+                     softmax_scale, indices, topk, o, lse, workspace, workspace_bytes, 1, nullptr, 3,
+                     stream);
+}
+
+int mla_decode_with_kvcache_dual(const void* q, const void* kvcache, int64_t num_pages,
+                                 const int32_t* block_table, int max_blocks,
+                                 const int32_t* cache_seqlens, const int32_t* indices, int topk,
+                                 const void* kvcache2, int64_t num_pages2,
+                                 const int32_t* block_table2, int max_blocks2,
+                                 const int32_t* cache_seqlens2, const int32_t* indices2, int topk2,
+                                 int page_size, int batch, int s_q, int h_q, int h_kv, int d_qk,
+                                 int dv, const int32_t* plan, const int32_t* num_splits,
+                                 int num_workers, float softmax_scale, void* o, float* lse,
+                                 void* workspace, size_t workspace_bytes, int phases,
+                                 void* stream) {
+  if (!indices || topk <= 0) return MLA_ERR_INVALID_ARGUMENT;
+  const AuxCache aux{kvcache2, num_pages2, block_table2, max_blocks2, cache_seqlens2, indices2, topk2};
+  return decode_impl(q, kvcache, num_pages, page_size, block_table, max_blocks, cache_seqlens,
+                     batch, s_q, h_q, h_kv, d_qk, dv, plan, num_splits, num_workers, 0,
+                     softmax_scale, indices, topk, o, lse, workspace, workspace_bytes, 0, &aux,
+                     phases, stream);
 }
 
 int mla_debug_row_ids(const int32_t* block_table, int max_blocks, const int32_t* cache_seqlens,

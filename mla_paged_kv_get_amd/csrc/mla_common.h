@@ -70,6 +70,18 @@ struct DecodeArgs {
   int h_kv;                   // latent KV heads (items are (sequence or query token, KV head))
   int G;                      // query heads per KV head, h_q / h_kv
   int kv_format;              // 0: bf16 rows; 1: packed FP8 rows
+  int d_qk;                   // values per cached row: 576 (512 latent + 64 RoPE) or 512
+  // Sparse mode with a second (auxiliary) cache: item keys are the main
+  // list's tiles (nb1 = ceil(topk / 64) of them) followed by the auxiliary
+  // list's; kv2 == nullptr when there is none.
+  const uint16_t* kv2;
+  const int32_t* block_table2;
+  const int32_t* seqlens2;
+  const int32_t* indices2;
+  int max_blocks2;
+  int topk2;
+  int nb1;                    // tiles of the main list of a sparse item
+  int nb_sparse;              // tiles of a sparse item (both lists)
 };
 
 // Row of q / o / lse ([batch * s_q * h_q] rows) holding query row `row` of

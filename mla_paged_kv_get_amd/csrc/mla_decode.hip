@@ -113,9 +113,12 @@ __device__ __forceinline__ bf16x4 read_tr(const char* p) {
 // one accumulation per 128-value block and adds them up with the keys'
 // scales, and PV takes each key's scale (for the output columns' block) into
 // its probability.
-template <int V, bool KV8>
+template <int V, bool KV8, int D>
 struct Cfg {
+  static_assert(D == 576 || D == 512, "latent rows of 576 (512 + 64 RoPE) or 512 values");
+  static_assert(!KV8 || D == 576, "packed FP8 rows hold 576 values");
   static constexpr bool kWide = V == kVariantRows64;
+  static constexpr int kCG = D / 64;                     // 128-byte chunk groups of a bf16 row
   static constexpr int kWaves = 4;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int kRows = kWide ? 64 : 16;          // query rows per workgroup
@@ -123,12 +126,13 @@ struct Cfg {
   // chunk groups of 128 B.  FP8: its 16 rows x 5 segments of 128 B (latent
   // bytes 0..511, RoPE bytes 528..655), plus four 4-byte copies that put the
   // 16 rows' scales of each block into a [block][row] table.
-  static constexpr int kLoads = KV8 ? 14 : 18;
+  static constexpr int kLoads = KV8 ? 14 : 2 * kCG;
   static constexpr int kLaneRows = 2;                    // tile rows each lane copies (8 lanes per row)
   static constexpr int kOffs = KV8 ? 3 : 2;              // copy offsets per lane (FP8: + the scale row)
-  static constexpr int kRowB = KV8 ? kRowBytes8 : kRowBytes;   // bytes per cached row
-  static constexpr int kStageBytes = KV8 ? kRaw8Bytes : kTileBytes;
-  static constexpr int kQf = kWide ? 36 : 18;            // bf16x8 B-operand fragments of Q per lane
+  static constexpr int kRowB = KV8 ? kRowBytes8 : 2 * D;      // bytes per cached row
+  static constexpr int kTileB = kPage * 2 * D;                 // bytes of a tile in the bf16 layout
+  static constexpr int kStageBytes = KV8 ? kRaw8Bytes : kTileB;
+  static constexpr int kQf = kWide ? D / 16 : D / 32;    // bf16x8 B-operand fragments of Q per lane
   static constexpr int kRowsPerWave = kWide ? 32 : 16;   // rows of the softmax state a wave holds
 };
 
@@ -282,9 +286,9 @@ __device__ __forceinline__ void merge_row(const DecodeArgs& a, int item, int slo
   if (lane == 0) a.lse[orow] = tot > 0.f ? mx + logf(tot) : -INFINITY;
 }
 
-template <int V, bool SPARSE, bool KV8>
+template <int V, bool SPARSE, bool KV8, int D>
 __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
-  using C = Cfg<V, KV8>;
+  using C = Cfg<V, KV8, D>;
   constexpr bool kWide = C::kWide;
   constexpr int kRw = C::kRowsPerWave;
   // vector-memory operations issued per wave for a tile: copy, sparse index loads
@@ -295,7 +299,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) char s0[C::kStageBytes];
   __shared__ __attribute__((aligned(1024))) char s1[C::kStageBytes];
   // FP8: the current tile expanded to bf16 (the layout of a bf16 stage)
-  __shared__ __attribute__((aligned(1024))) char tbuf[KV8 ? kTileBytes : 16];
+  __shared__ __attribute__((aligned(1024))) char tbuf[KV8 ? C::kTileB : 16];
   __shared__ __attribute__((aligned(16))) unsigned char kvalid[4][64];   // sparse key validity, tile t -> t & 3
   __shared__ float red_m[4][kRw];     // per-wave row maxima of the tile
   __shared__ float red_l[4][kRw];     // per-wave row sums at the end of a run
@@ -349,26 +353,27 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
 
   if (it_first >= 0) {
     // LDS read offsets of this lane.  Byte offset of chunk c of tile row t:
-    // ((t / 8) * 9 + c / 8) * 1024 + (t % 8) * 128 + ((c % 8) ^ swz(t)) * 16.
+    // ((t / 8) * kCG + c / 8) * 1024 + (t % 8) * 128 + ((c % 8) ^ swz(t)) * 16
+    // (kCG = 9 chunk groups of 128 B for 576-value rows, 8 for 512).
     int k_base, v_base;
     int k_x[4];       // rows16: [0] even ks, [1] odd ks; wide: by ks & 3
     int v_x[2][4];    // rows16: [0][dt & 3]; wide: [second 4 keys][db & 1]
     if constexpr (!kWide) {
       //  K: key row t = 16 tg + li, chunk 4 ks + g.
       const int tk = 16 * tg + li;
-      k_base = ((tk >> 3) * 9 << 10) + ((tk & 7) << 7);
+      k_base = ((tk >> 3) * C::kCG << 10) + ((tk & 7) << 7);
       k_x[0] = ((g ^ swz(tk)) << 4);
       k_x[1] = (((4 + g) ^ swz(tk)) << 4);
       //  V^T: source row t = 16 s + 4 g + li / 4 of key subtile s, columns
       //  128 tg + 16 dt + 4 (li & 3) .. + 3: chunk 16 tg + 2 dt + (li & 3) / 2, half li & 1.
       const int tv = 4 * g + (li >> 2);
-      v_base = ((tv >> 3) * 9 << 10) + ((tv & 7) << 7) + ((li & 1) << 3) + ((2 * tg) << 10);
+      v_base = ((tv >> 3) * C::kCG << 10) + ((tv & 7) << 7) + ((li & 1) << 3) + ((2 * tg) << 10);
 #pragma unroll
       for (int d = 0; d < 4; ++d) v_x[0][d] = (((2 * d + ((li & 3) >> 1)) ^ swz(tv)) << 4);
     } else {
       //  K: key row t = 32 half + lrow, chunk 2 ks + hl.
       const int tk = 32 * half + lrow;
-      k_base = ((tk >> 3) * 9 << 10) + ((tk & 7) << 7);
+      k_base = ((tk >> 3) * C::kCG << 10) + ((tk & 7) << 7);
 #pragma unroll
       for (int b = 0; b < 4; ++b) k_x[b] = (((2 * b + hl) ^ swz(tk)) << 4);
       //  V^T for PV k-step j (keys 16 j .. 16 j + 15 in the order of the score
@@ -408,8 +413,22 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     };
     auto seg_hi = [&](int x) __attribute__((always_inline)) -> int {         // end block of this worker's run in item x
       if (x == it_last) return blk_end;
-      const int len = sparse ? a.topk : item_len(x);
+      if constexpr (sparse) return a.nb_sparse;
+      const int len = item_len(x);
       return len > 0 ? (len + kPage - 1) / kPage : 0;
+    };
+    // Sparse tile blk of an item: its index list (main, or the auxiliary
+    // cache's after the main list's nb1 tiles), that list's length, and the
+    // tile's first entry.
+    struct SparseList {
+      const int32_t* list;
+      int n, e0;
+      bool aux;
+    };
+    auto sparse_list = [&](int item, int blk) __attribute__((always_inline)) -> SparseList {
+      const int64_t tok = item / a.h_kv;
+      if (blk < a.nb1) return {a.indices + tok * a.topk, a.topk, blk * kPage, false};
+      return {a.indices2 + tok * a.topk2, a.topk2, (blk - a.nb1) * kPage, true};
     };
     // Tile after (item, blk) in this worker's runs (hi = end block of the run
     // in `item`); ni = -1 at the end.
@@ -448,15 +467,15 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
       if constexpr (!sparse) {
         raw.v[0] = read_scalar(a.block_table + (int64_t)item_seq(a, item) * a.max_blocks + blk);   // not a vector load
       } else {
-        const int32_t* idx_row = a.indices + (int64_t)(item / a.h_kv) * a.topk;
+        const SparseList sl = sparse_list(item, blk);
 #pragma unroll
         for (int r = 0; r < C::kLaneRows; ++r) {
-          const int sl = blk * kPage + cp_row[r];
-          raw.v[r] = sl < a.topk ? idx_row[sl] : -1;
+          const int e = sl.e0 + cp_row[r];
+          raw.v[r] = e < sl.n ? sl.list[e] : -1;
         }
         if constexpr (KV8) {
-          const int sl = blk * kPage + sc_row;
-          raw.v[2] = sl < a.topk ? idx_row[sl] : -1;
+          const int e = sl.e0 + sc_row;
+          raw.v[2] = e < sl.n ? sl.list[e] : -1;
         }
       }
     };
@@ -474,20 +493,27 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
         }
         if constexpr (KV8) off[2] = ((page * kPage + min(sc_row, nvalid - 1)) * a.h_kv + kvh) * (int64_t)C::kRowB;
       } else {
-        const int32_t* bt_row = a.block_table + (int64_t)item_seq(a, item) * a.max_blocks;
+        // auxiliary-cache tiles: its block table, lengths and rows (offsets
+        // taken from the main cache's base)
+        const bool aux = blk >= a.nb1;
+        const int b = item_seq(a, item);
+        const int32_t* bt_row = aux ? a.block_table2 + (int64_t)b * a.max_blocks2
+                                    : a.block_table + (int64_t)b * a.max_blocks;
+        const int Ls = aux ? read_scalar(a.seqlens2 + b) : L;
+        const int64_t base = aux ? (int64_t)(reinterpret_cast<const char*>(a.kv2) - kv_bytes) : 0;
 #pragma unroll
         for (int r = 0; r < C::kLaneRows; ++r) {
           const int idx = raw.v[r];
-          const bool ok = sparse_key_valid(idx, L);
+          const bool ok = sparse_key_valid(idx, Ls);
           // padding reads the sequence's first row (page 0 of the pool if it has none)
-          const int64_t crow = ok ? cache_row(bt_row, idx) : (L > 0 ? cache_row(bt_row, 0) : 0);
-          off[r] = (crow * a.h_kv + kvh) * (int64_t)C::kRowB;
+          const int64_t crow = ok ? cache_row(bt_row, idx) : (Ls > 0 ? cache_row(bt_row, 0) : 0);
+          off[r] = base + (crow * a.h_kv + kvh) * (int64_t)C::kRowB;
           if ((lane & 7) == 0) vslot[cp_row[r]] = ok ? 1 : 0;
         }
         if constexpr (KV8) {
           const int idx = raw.v[2];
-          const int64_t crow = sparse_key_valid(idx, L) ? cache_row(bt_row, idx) : (L > 0 ? cache_row(bt_row, 0) : 0);
-          off[2] = (crow * a.h_kv + kvh) * (int64_t)C::kRowB;
+          const int64_t crow = sparse_key_valid(idx, Ls) ? cache_row(bt_row, idx) : (Ls > 0 ? cache_row(bt_row, 0) : 0);
+          off[2] = base + (crow * a.h_kv + kvh) * (int64_t)C::kRowB;
         }
       }
     };
@@ -498,7 +524,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     auto issue_one = [&](char* stage, const int64_t (&off)[C::kOffs], int j) __attribute__((always_inline)) {
       if constexpr (!KV8) {
         const int ii = wave * C::kLoads + j;
-        const int r = j / 9, cl = j % 9;
+        const int r = j / C::kCG, cl = j % C::kCG;
         const char* src = kv_bytes + off[r] + cl * 128 + (((lane & 7) ^ cp_swz[r]) << 4);
         copy_to_lds_16(src, lds_addr(stage + ii * 1024));
       } else if (j < 10) {
@@ -520,16 +546,21 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     // they are padding).  Dense: its page id.
     auto idx_dma = [&](int item, int blk, int slot) __attribute__((always_inline)) {
       const int32_t* src;
-      if constexpr (sparse) src = a.indices + (int64_t)(item / a.h_kv) * a.topk + min(blk * kPage + lane, a.topk - 1);
-      else src = a.block_table + (int64_t)item_seq(a, item) * a.max_blocks + blk;
+      if constexpr (sparse) {
+        const SparseList sl = sparse_list(item, blk);
+        src = sl.list + min(sl.e0 + lane, sl.n - 1);
+      } else {
+        src = a.block_table + (int64_t)item_seq(a, item) * a.max_blocks + blk;
+      }
       copy_to_lds_4(src, lds_addr(&idxbuf[slot & 3][wave][0]));
     };
-    auto idx_from_lds = [&](int blk, int slot, TileRaw& raw) __attribute__((always_inline)) {
+    auto idx_from_lds = [&](int item, int blk, int slot, TileRaw& raw) __attribute__((always_inline)) {
       if constexpr (sparse) {
+        const SparseList sl = sparse_list(item, blk);
 #pragma unroll
         for (int r = 0; r < C::kLaneRows; ++r)
-          raw.v[r] = blk * kPage + cp_row[r] < a.topk ? idxbuf[slot & 3][wave][cp_row[r]] : -1;
-        if constexpr (KV8) raw.v[2] = blk * kPage + sc_row < a.topk ? idxbuf[slot & 3][wave][sc_row] : -1;
+          raw.v[r] = sl.e0 + cp_row[r] < sl.n ? idxbuf[slot & 3][wave][cp_row[r]] : -1;
+        if constexpr (KV8) raw.v[2] = sl.e0 + sc_row < sl.n ? idxbuf[slot & 3][wave][sc_row] : -1;
       } else {
         raw.v[0] = idxbuf[slot & 3][wave][0];
       }
@@ -544,7 +575,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
       const int t = threadIdx.x >> 2, b = threadIdx.x & 3;
       const int tr = t & 7, rb = t >> 3, sw = swz(t);
       const char* src = raw + ((rb * 5 + b) << 10) + (tr << 7);
-      char* dst = tb + ((rb * 9) << 10) + (tr << 7);
+      char* dst = tb + ((rb * C::kCG) << 10) + (tr << 7);
       const int sz = raw8_swz(t, b);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -576,6 +607,22 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
       }
     };
 
+    // Sparse: a tile without a single valid key adds nothing, but its rows
+    // need not hold finite values (a sequence with no row at all in a cache
+    // has its padding read the pool's first row), and 0 * NaN would reach O
+    // through PV.  Such a tile is cleared before it is computed (the test is
+    // the same in every wave).
+    auto clear_if_empty = [&](char* tile, const unsigned char* vslot) __attribute__((always_inline)) {
+      if constexpr (sparse) {
+        if (__builtin_amdgcn_ballot_w64(vslot[lane] != 0) == 0) {
+          for (int i = threadIdx.x; i < C::kTileB / 16; i += C::kThreads)
+            reinterpret_cast<uint4*>(tile)[i] = uint4{0, 0, 0, 0};
+          if constexpr (KV8) reinterpret_cast<float*>(const_cast<float*>(sc_tab))[threadIdx.x] = 0.f;
+          barrier_keep_loads();
+        }
+      }
+    };
+
     // Per-run state of this wave.
     using Acc = typename std::conditional<kWide, floatx16, floatx4>::type;
     bf16x8 qf[C::kQf];    // B operand of S^T, 8 values of row `row` per fragment
@@ -586,7 +633,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     // Rows past M borrow row 0's values (their scores are masked to -inf), so
     // no select on the loaded data forces an early wait on the loads.
     auto load_q = [&](int item) __attribute__((always_inline)) {
-      const uint16_t* qrow = a.q + q_row(a, item, row_ok ? row : 0) * kDqk;
+      const uint16_t* qrow = a.q + q_row(a, item, row_ok ? row : 0) * D;
 #pragma unroll
       for (int ks = 0; ks < C::kQf; ++ks)
         qf[ks] = kWide ? *reinterpret_cast<const bf16x8*>(qrow + 16 * ks + 8 * hl)
@@ -602,16 +649,16 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
       const char* q_bytes = reinterpret_cast<const char*>(a.q);
 #pragma unroll
       for (int j = 0; j < C::kLoads; ++j) {
-        const int r = j / 9, cl = j % 9;
+        const int r = j / C::kCG, cl = j % C::kCG;
         const int qr = cp_row[r] < a.M ? cp_row[r] : 0;     // rows past M borrow row 0
-        const char* src = q_bytes + q_row(a, item, qr) * (int64_t)kRowBytes + cl * 128 +
+        const char* src = q_bytes + q_row(a, item, qr) * (int64_t)(2 * D) + cl * 128 +
                           (((lane & 7) ^ cp_swz[r]) << 4);
         copy_to_lds_16(src, lds_addr(stage + j * 1024));
       }
     };
     auto q_from_lds = [&](const char* stage) __attribute__((always_inline)) {
       // row li, chunk 4 ks + g, in the tile layout
-      const int qb = ((li >> 3) * 9 << 10) + ((li & 7) << 7);
+      const int qb = ((li >> 3) * C::kCG << 10) + ((li & 7) << 7);
       const int qx0 = (g ^ swz(li)) << 4, qx1 = ((4 + g) ^ swz(li)) << 4;
 #pragma unroll
       for (int ks = 0; ks < C::kQf; ++ks)
@@ -640,17 +687,17 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
       float x[kX];                           // raw scores of the lane's keys, -inf where masked
       float mx;                              // raw row max over this wave's keys
       if constexpr (!kWide) {
-        // S^T (16 keys x 16 rows): all 18 K fragments first, one LDS latency for the chain.
+        // S^T (16 keys x 16 rows): all kQf K fragments first, one LDS latency for the chain.
         floatx4 sacc = floatx4{0.f, 0.f, 0.f, 0.f};
-        bf16x8 kf[18];
+        bf16x8 kf[C::kQf];
 #pragma unroll
-        for (int ks = 0; ks < 18; ++ks)
+        for (int ks = 0; ks < C::kQf; ++ks)
           kf[ks] = *reinterpret_cast<const bf16x8*>(stage + k_base + ((ks >> 1) << 10) + k_x[ks & 1]);
         // element i: key 16 tg + 4 g + i
         const int t0 = 16 * tg + 4 * g;
         if constexpr (!KV8) {
 #pragma unroll
-          for (int ks = 0; ks < 18; ++ks) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[ks], sacc, 0, 0, 0);
+          for (int ks = 0; ks < C::kQf; ++ks) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[ks], sacc, 0, 0, 0);
         } else {
           // one accumulation per 128-value latent block (4 k-steps each), then
           // the keys' block scales; the RoPE k-steps 16, 17 are not scaled
@@ -681,7 +728,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
         mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
         mx = xor32_max(xor16_max(mx));
       } else {
-        // S^T (32 keys x 32 rows) = K Q^T over 36 k-steps of 16.  The loop is
+        // S^T (32 keys x 32 rows) = K Q^T over kQf k-steps of 16.  The loop is
         // written twice so that issuing the next tile's copy inside it costs
         // no branch per k-step.
         floatx16 sacc = {};
@@ -693,9 +740,9 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
           for (int ks = 0; ks < kPre; ++ks)
             kf[ks] = *reinterpret_cast<const bf16x8*>(stage + k_base + ((ks >> 2) << 10) + k_x[ks & 3]);
 #pragma unroll
-          for (int ks = 0; ks < 36; ++ks) {
+          for (int ks = 0; ks < C::kQf; ++ks) {
             const bf16x8 kcur = kf[ks % kPre];
-            if (ks + kPre < 36)
+            if (ks + kPre < C::kQf)
               kf[ks % kPre] = *reinterpret_cast<const bf16x8*>(stage + k_base + (((ks + kPre) >> 2) << 10) +
                                                                k_x[(ks + kPre) & 3]);
             // FP8: each latent block (k-steps 8 b .. 8 b + 7) accumulates on
@@ -707,8 +754,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
               sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur, qf[ks], sacc, 0, 0, 0);
             }
             if constexpr (decltype(with_dma)::value) {
-              // one copy every second k-step (kLoads <= 18)
-              static_assert(C::kLoads <= 18, "the copies must fit the 36 k-steps");
+              // one copy every second k-step
+              static_assert(2 * C::kLoads <= C::kQf, "the copies must fit the k-steps");
               if (ks % 2 == 0 && ks / 2 < C::kLoads) issue_one(dma_stage, off, ks / 2);
             }
             __builtin_amdgcn_sched_barrier(0);   // keep the reads kPre MFMAs ahead
@@ -837,7 +884,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
         constexpr int kPv = 6;
         auto vaddr = [&](int n, int e) __attribute__((always_inline)) -> const char* {
           const int c = n >> 3, dt = n & 7;
-          return stage + v_base + (2 * c + e) * (2 * 9 * 1024) + ((dt >> 2) << 10) + v_x[0][dt & 3];
+          return stage + v_base + (2 * c + e) * (2 * C::kCG * 1024) + ((dt >> 2) << 10) + v_x[0][dt & 3];
         };
         bf16x4 vq0[kPv], vq1[kPv];
 #pragma unroll
@@ -869,7 +916,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
         constexpr int kPv = 6;
         auto vaddr = [&](int n, int e) __attribute__((always_inline)) -> const char* {
           const int j = n >> 3, db = n & 7;
-          return stage + v_base + (2 * j + e) * (9 * 1024) + ((db >> 1) << 10) + v_x[e][db & 1];
+          return stage + v_base + (2 * j + e) * (C::kCG * 1024) + ((db >> 1) << 10) + v_x[e][db & 1];
         };
         bf16x4 vq0[kPv], vq1[kPv];
 #pragma unroll
@@ -1020,11 +1067,12 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
           sc_tab = reinterpret_cast<const float*>(cur + kRaw8ScaleOff);
         }
         if (has_next) {
-          idx_from_lds(nx_blk, t + 1, raw);
+          idx_from_lds(nx_item, nx_blk, t + 1, raw);
           tile_finish(nx_item, nx_blk, raw, off, kvalid[(t + 1) & 3]);
         }
         if (n2_item >= 0) idx_dma(n2_item, n2_blk, t + 2);
         const bool ends = !has_next || nx_item != cur_item;
+        clear_if_empty(KV8 ? tbuf : cur, kvalid[t & 3]);
         compute(KV8 ? tbuf : cur, kvalid[t & 3], cur_blk, cur_lim, has_next ? nxt : nullptr);
         if (ends) {
           finish(cur_item, cur_split);
@@ -1077,6 +1125,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
       if (q_pending) q_from_lds(nxt);
       if (n2_item >= 0) tile_finish(n2_item, n2_blk, raw, off, kvalid[(t + 2) & 3]);
       const bool ends = !has_next || nx_item != cur_item;
+      clear_if_empty(KV8 ? tbuf : cur, kvalid[t & 3]);
       compute(KV8 ? tbuf : cur, kvalid[t & 3], cur_blk, cur_lim, q_lds && has_next ? nxt : nullptr);
       q_pending = false;
       if (ends) {
@@ -1122,26 +1171,29 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   }
 }
 
-template <int V, bool KV8>
+template <int V, bool KV8, int D>
 hipError_t launch_variant(const DecodeArgs& a, hipStream_t stream) {
   const int groups = (a.num_workers + 7) / 8;
   const int grid = a.m_tiles == 1 ? a.num_workers : groups * 8 * a.m_tiles;
   if (a.topk > 0)
-    hipLaunchKernelGGL((decode_kernel<V, true, KV8>), dim3(grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<V, true, KV8, D>), dim3(grid), dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((decode_kernel<V, false, KV8>), dim3(grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<V, false, KV8, D>), dim3(grid), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, int variant, hipStream_t stream) {
-  if (a.kv_format == 1) {
-    if (variant == kVariantRows16) return launch_variant<kVariantRows16, true>(a, stream);
-    return launch_variant<kVariantRows64, true>(a, stream);
-  }
-  if (variant == kVariantRows16) return launch_variant<kVariantRows16, false>(a, stream);
-  return launch_variant<kVariantRows64, false>(a, stream);
+  const bool r16 = variant == kVariantRows16;
+  if (a.kv_format == 1)
+    return r16 ? launch_variant<kVariantRows16, true, 576>(a, stream)
+               : launch_variant<kVariantRows64, true, 576>(a, stream);
+  if (a.d_qk == 512)
+    return r16 ? launch_variant<kVariantRows16, false, 512>(a, stream)
+               : launch_variant<kVariantRows64, false, 512>(a, stream);
+  return r16 ? launch_variant<kVariantRows16, false, 576>(a, stream)
+             : launch_variant<kVariantRows64, false, 576>(a, stream);
 }
 
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream) {

@@ -82,8 +82,8 @@ def normal_bf16(rng: np.random.Generator, shape, chunk: int = 1 << 24) -> np.nda
 class Workload:
     """One decode call's inputs (host arrays)."""
     name: str
-    q: np.ndarray              # uint16 [B, s_q, h_q, 576]
-    kv: np.ndarray             # uint16 [num_pages, 64, h_kv, 576]
+    q: np.ndarray              # uint16 [B, s_q, h_q, d_qk]  (d_qk = 576 or 512)
+    kv: np.ndarray             # uint16 [num_pages, 64, h_kv, d_qk] (or uint8 [.., 656] packed FP8)
     block_table: np.ndarray    # int32 [B, max_blocks]
     cache_seqlens: np.ndarray  # int32 [B]
     causal: bool = False
@@ -91,6 +91,8 @@ class Workload:
     dv: int = D_V
     softmax_scale: float | None = None
     meta: dict = field(default_factory=dict)
+    # dual-cache sparse decode: (kv2, block_table2, cache_seqlens2, indices2)
+    aux: tuple | None = None
 
     @property
     def B(self):
@@ -113,7 +115,7 @@ def build(name: str, seed: int, lengths: np.ndarray | None, *, B: int, s_q: int,
           num_pages: int, causal: bool = False, max_blocks: int | None = None,
           poison: bool = False, h_kv: int = 1, topk: int | None = None,
           rng: np.random.Generator | None = None, pad_page: int | None = None,
-          dv: int = D_V, kv_format: str = "bf16") -> Workload:
+          dv: int = D_V, kv_format: str = "bf16", d_qk: int = D_QK) -> Workload:
     """Assemble a workload.  ``lengths`` may be drawn by the caller from ``rng``
     (the same generator is then used for the rest, keeping the draw order)."""
     rng = np.random.default_rng(seed) if rng is None else rng
@@ -136,11 +138,11 @@ def build(name: str, seed: int, lengths: np.ndarray | None, *, B: int, s_q: int,
         n = int(nblk[b])
         bt[b, :n] = perm[off:off + n]
         off += n
-    q = normal_bf16(rng, (B, s_q, h_q, D_QK))
+    q = normal_bf16(rng, (B, s_q, h_q, d_qk))
     if kv_format == "fp8":
         kv = packed_fp8_rows(rng, (pool, PAGE, h_kv))
     elif kv_format == "bf16":
-        kv = normal_bf16(rng, (pool, PAGE, h_kv, D_QK))
+        kv = normal_bf16(rng, (pool, PAGE, h_kv, d_qk))
     else:
         raise ValueError(f"unknown kv_format {kv_format!r}")
     indices = None
@@ -222,6 +224,52 @@ def sparse_prefill(poison: bool = False, T: int = 4096) -> Workload:
                  num_pages=(4096 + T) // PAGE + 8, topk=2048, poison=poison, rng=rng)
 
 
+def add_aux_cache(w: Workload, rng: np.random.Generator, lengths2, topk2: int, num_pages2: int,
+                  poison: bool = False) -> Workload:
+    """Give a sparse workload an auxiliary cache (dual-cache decode), drawn after
+    everything else: its page permutation, its rows, then per query token topk2
+    unique unsorted positions below its sequence's auxiliary length (-1 past it)."""
+    lengths2 = np.asarray(lengths2, dtype=np.int64)
+    B, s_q, h_kv, d = w.B, w.s_q, w.kv.shape[2], w.kv.shape[3]
+    nblk = (lengths2 + PAGE - 1) // PAGE
+    mb = int(max(1, nblk.max()))
+    need = int(nblk.sum())
+    pool = max(num_pages2, need + 1)
+    perm = rng.permutation(pool)
+    bt = np.full((B, mb), int(perm[need]), dtype=np.int32)
+    off = 0
+    for b in range(B):
+        n = int(nblk[b])
+        bt[b, :n] = perm[off:off + n]
+        off += n
+    kv2 = normal_bf16(rng, (pool, PAGE, h_kv, d))
+    idx2 = np.full((B, s_q, topk2), -1, dtype=np.int32)
+    for b in range(B):
+        for s in range(s_q):
+            n = min(topk2, int(lengths2[b]))
+            if n:
+                idx2[b, s, :n] = rng.choice(int(lengths2[b]), size=n, replace=False)
+    if poison:
+        referenced = np.zeros((pool, PAGE), dtype=bool)
+        for b in range(B):
+            for j in range(int(nblk[b])):
+                referenced[bt[b, j], :min(PAGE, int(lengths2[b]) - j * PAGE)] = True
+        kv2[~referenced] = BF16_NAN
+    w.aux = (kv2, bt, lengths2.astype(np.int32), idx2)
+    return w
+
+
+def dual_cache(poison: bool = False, B: int = 16) -> Workload:
+    """Dual-cache sparse decode over 512-value rows: b=16, s_q=2, h_q=128;
+    main cache length 32768 with top-k 2048, auxiliary cache of 1024 tokens
+    of which each query token takes 512."""
+    rng = np.random.default_rng(10)
+    lengths = np.full(B, 32768)
+    w = build(f"dual-cache d512 b{B} sq2 h128 L32768 k2048 + L1024 k512", 10, lengths, B=B, s_q=2,
+              h_q=128, num_pages=B * 512, max_blocks=512, topk=2048, poison=poison, rng=rng, d_qk=512)
+    return add_aux_cache(w, rng, np.full(B, 1024), 512, B * 16 + 1, poison=poison)
+
+
 def grouped_heads(poison: bool = False) -> Workload:
     """b=32, s_q=1, h_q=128 over h_kv=8 latent heads (16 query heads each),
     lengths uniform in [1, 4096], 1200-page pool."""
@@ -258,4 +306,5 @@ NAMED = {
     "sparse_prefill": sparse_prefill,
     "memory_bound_fp8": memory_bound_fp8,
     "sparse_topk_fp8": sparse_topk_fp8,
+    "dual_cache": dual_cache,
 }

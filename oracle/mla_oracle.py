@@ -28,6 +28,14 @@ float64 with NumPy (one library matmul per query token is the only "fast" step):
   query token (b, s) attends to the logical positions ``indices[b, s, :topk]``;
   an entry outside ``[0, L_b)`` (e.g. -1) is padding and is skipped.
 * Empty key set: O = 0, LSE = -inf.
+* Rows of 512 values ("FlashInfer, SM120 GPU를 위한 희소 MLA 커널", 들어가며:
+  models with d_qk = 512 beside d_qk = 576): K is the whole row and V, with
+  dv = 512, the whole row too.
+* Dual cache (the same page, section "코드 분석", item 1: a main and an
+  auxiliary cache used together): in sparse mode a query token attends to the
+  union of its keys in the main cache (``indices`` through ``block_table``)
+  and in the auxiliary cache (``indices2`` through ``block_table2``, valid
+  below ``cache_seqlens2``), with one softmax over both sets.
 * FP8 cache ("FlashInfer, SM120 GPU를 위한 희소 MLA 커널", section "코드 분석",
   item 5: a packed KV cache whose scale format is a parameter; "Blackwell을
   위한 새로운 MLA 백엔드: TOKENSPEED_MLA 분석": FP8 KV caches).  The pages fix
@@ -127,7 +135,7 @@ def key_positions(b: int, s: int, seqlen: int, s_q: int, causal: bool,
 def decode(q_bits: np.ndarray, kv_bits: np.ndarray, block_table: np.ndarray,
            cache_seqlens: np.ndarray, dv: int = D_V, causal: bool = False,
            softmax_scale: float | None = None, indices: np.ndarray | None = None,
-           topk: int | None = None, items=None):
+           topk: int | None = None, items=None, aux=None):
     """float64 MLA decode.
 
     q_bits   uint16 [B, s_q, h_q, d]           (bf16 bit patterns)
@@ -136,6 +144,9 @@ def decode(q_bits: np.ndarray, kv_bits: np.ndarray, block_table: np.ndarray,
     block_table int [B, max_blocks]; cache_seqlens int [B]
     indices  optional int [B, s_q, topk] logical positions (sparse mode)
     items    optional iterable of (b, s) pairs to compute (others stay NaN)
+    aux      optional auxiliary cache (kv2_bits, block_table2, cache_seqlens2,
+             indices2) of the dual-cache sparse decode; its keys join each
+             query token's key set
 
     Returns (O float64 [B, s_q, h_q, dv], LSE float64 [B, s_q, h_q]).
     """
@@ -155,16 +166,27 @@ def decode(q_bits: np.ndarray, kv_bits: np.ndarray, block_table: np.ndarray,
     out = np.full((B, s_q, h_q, dv), np.nan)
     lse = np.full((B, s_q, h_q), np.nan)
     todo = items if items is not None else [(b, s) for b in range(B) for s in range(s_q)]
+    if aux is not None:
+        if indices is None:
+            raise ValueError("the auxiliary cache needs sparse mode")
+        kv2, bt2, sl2, idx2 = aux
+        rows2 = kv2.reshape(-1, h_kv, kv2.shape[-1])
     for b, s in todo:
         L = int(cache_seqlens[b])
         pos = key_positions(b, s, L, s_q, causal, indices, topk)
-        if pos.size == 0:
+        rid = physical_rows(block_table, b, pos)
+        rid2 = np.zeros(0, dtype=np.int64)
+        if aux is not None:
+            pos2 = key_positions(b, s, int(sl2[b]), s_q, False, idx2, None)
+            rid2 = physical_rows(bt2, b, pos2)
+        if rid.size + rid2.size == 0:
             out[b, s] = 0.0
             lse[b, s] = -np.inf
             continue
-        rid = physical_rows(block_table, b, pos)
         for g in range(h_kv):
             K = row_values(rows[rid, g, :])                  # [n, d]
+            if aux is not None:
+                K = np.concatenate([K, row_values(rows2[rid2, g, :])], axis=0)
             V = K[:, :dv]                                    # [n, dv]
             Q = bf16_to_f64(q_bits[b, s, g * group:(g + 1) * group, :])  # [group, d]
             S = scale * (Q @ K.T)                            # [group, n]

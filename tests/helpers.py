@@ -35,6 +35,10 @@ class Dev:
         self.bt = i32_dev(w.block_table)
         self.sl = i32_dev(w.cache_seqlens)
         self.idx = i32_dev(w.indices) if w.indices is not None else None
+        self.aux = None
+        if w.aux is not None:
+            kv2, bt2, sl2, idx2 = w.aux
+            self.aux = (kv_to_dev(kv2), i32_dev(bt2), i32_dev(sl2), i32_dev(idx2))
 
 
 def run_gpu(d: Dev, num_workers=None, plan=None, softmax_scale=None):
@@ -42,10 +46,11 @@ def run_gpu(d: Dev, num_workers=None, plan=None, softmax_scale=None):
     w = d.w
     if plan is None:
         h_kv = w.kv.shape[2]
+        topk2 = w.aux[3].shape[2] if d.aux is not None else 0
         plan = m.get_mla_metadata(d.sl, w.s_q * w.h_q // h_kv, h_kv, s_q=w.s_q, topk=w.topk,
-                                  num_workers=num_workers)
+                                  num_workers=num_workers, topk2=topk2)
     o, lse = m.mla_decode_with_kvcache(d.q, d.kv, d.bt, d.sl, 512, plan[0], plan[1], causal=w.causal,
-                                       softmax_scale=softmax_scale, indices=d.idx)
+                                       softmax_scale=softmax_scale, indices=d.idx, aux=d.aux)
     torch.cuda.synchronize()
     return o, lse, plan
 
@@ -57,7 +62,7 @@ def o_to_f64(o: torch.Tensor) -> np.ndarray:
 def compare(w, o, lse, items=None, softmax_scale=None, label=""):
     """Compare GPU outputs with the oracle on the given (b, s) items (all by default)."""
     O_ref, L_ref = orc.decode(w.q, w.kv, w.block_table, w.cache_seqlens, 512, causal=w.causal,
-                              softmax_scale=softmax_scale, indices=w.indices, items=items)
+                              softmax_scale=softmax_scale, indices=w.indices, items=items, aux=w.aux)
     og = o_to_f64(o)
     lg = lse.cpu().numpy().astype(np.float64)
     todo = items if items is not None else [(b, s) for b in range(w.B) for s in range(w.s_q)]

@@ -81,7 +81,8 @@ def _decode(**kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(d=512), _lib.MLA_ERR_UNSUPPORTED),
+    (dict(d=448), _lib.MLA_ERR_UNSUPPORTED),
+    (dict(d=512, ws_bytes=100), _lib.MLA_ERR_WORKSPACE_TOO_SMALL),           # d_qk = 512 is accepted
     (dict(dv=256), _lib.MLA_ERR_UNSUPPORTED),
     (dict(page=32), _lib.MLA_ERR_UNSUPPORTED),
     (dict(h_kv=2, h_q=16, ws_bytes=100), _lib.MLA_ERR_WORKSPACE_TOO_SMALL),    # h_kv = 2 is accepted
@@ -126,6 +127,32 @@ def test_fp8_entries_reject():
     bad_scale = list(args)
     bad_scale[17] = ctypes.c_float(-1.0)
     assert l.mla_decode_with_kvcache_fp8(*bad_scale, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+
+
+def _dual(**kw):
+    a = dict(q=DUMMY, kv=DUMMY, num_pages=10, bt=DUMMY, mb=4, sl=DUMMY, idx=DUMMY, topk=64,
+             kv2=DUMMY, num_pages2=10, bt2=DUMMY, mb2=4, sl2=DUMMY, idx2=DUMMY, topk2=32,
+             page=64, batch=2, s_q=1, h_q=16, h_kv=1, d=512, dv=512, plan=DUMMY, ns=DUMMY, W=8,
+             scale=ctypes.c_float(0.05), o=DUMMY, lse=DUMMY, ws=DUMMY, ws_bytes=1 << 40, phases=3,
+             stream=None)
+    a.update(kw)
+    return _lib.lib().mla_decode_with_kvcache_dual(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(idx=None), _lib.MLA_ERR_INVALID_ARGUMENT),           # the main list is required
+    (dict(topk=0), _lib.MLA_ERR_INVALID_ARGUMENT),
+    (dict(idx2=None), _lib.MLA_ERR_INVALID_ARGUMENT),          # topk2 > 0 needs its list
+    (dict(kv2=None), _lib.MLA_ERR_INVALID_ARGUMENT),
+    (dict(num_pages2=0), _lib.MLA_ERR_INVALID_ARGUMENT),
+    (dict(mb2=0), _lib.MLA_ERR_INVALID_ARGUMENT),
+    (dict(d=448), _lib.MLA_ERR_UNSUPPORTED),
+    (dict(phases=0), _lib.MLA_ERR_INVALID_ARGUMENT),
+    (dict(ws_bytes=100), _lib.MLA_ERR_WORKSPACE_TOO_SMALL),
+    (dict(idx2=None, topk2=0, ws_bytes=100), _lib.MLA_ERR_WORKSPACE_TOO_SMALL),   # no auxiliary keys: accepted
+])
+def test_dual_rejects(kw, code):
+    assert _dual(**kw) == code
 
 
 def test_metadata_rejects():

@@ -187,6 +187,79 @@ def test_grouped_heads_equal_separate_single_head_caches():
         assert np.array_equal(O[:, :, 4 * g:4 * g + 4], Og) and np.array_equal(LSE[:, :, 4 * g:4 * g + 4], Lg)
 
 
+def test_d512_rows_match_sdpa():
+    # 512-value rows: K = V = the whole row, default scale 512^-0.5
+    w = wl.build("t512", 24, np.array([70, 1, 129]), B=3, s_q=2, h_q=16, num_pages=8, d_qk=512,
+                 causal=True)
+    O, LSE = orc.decode(w.q, w.kv, w.block_table, w.cache_seqlens, 512, causal=True)
+    for b in range(3):
+        K = _contiguous_cache(w, b)                              # [L, 512]
+        L = K.shape[0]
+        for s in range(2):
+            n = L - 2 + s + 1
+            q = _q(w, b, s)
+            ref = F.scaled_dot_product_attention(q[None, :, None, :], K[None, None, :n].expand(1, 16, -1, -1),
+                                                 K[None, None, :n].expand(1, 16, -1, -1), scale=512 ** -0.5)
+            np.testing.assert_allclose(O[b, s], ref[0, :, 0].numpy(), rtol=0, atol=1e-12)
+
+
+def _dual_small(seed, d_qk=576, topk2=40, lengths2=(100, 0, 65)):
+    lengths = np.array([300, 90, 129])
+    w = wl.build("dual", seed, lengths, B=3, s_q=2, h_q=16, num_pages=12, poison=True, topk=64, d_qk=d_qk)
+    w.indices[1, 0, 10:20] = -1
+    rng = np.random.default_rng(seed + 1)
+    return wl.add_aux_cache(w, rng, np.array(lengths2), topk2, 6, poison=True)
+
+
+@pytest.mark.parametrize("d_qk", [576, 512])
+def test_dual_equals_one_cache_holding_both(d_qk):
+    # the union over two caches == one sparse call over a single cache that holds the
+    # auxiliary pages after the main ones, each sequence's auxiliary blocks appended to
+    # its block table and its auxiliary positions shifted past its main blocks
+    w = _dual_small(25, d_qk)
+    kv2, bt2, sl2, idx2 = w.aux
+    pool1 = w.kv.shape[0]
+    kv = np.concatenate([w.kv, kv2], axis=0)
+    nb1 = -(-w.cache_seqlens.astype(np.int64) // 64)
+    mb = int((nb1 + bt2.shape[1]).max())
+    bt = np.zeros((w.B, mb), dtype=np.int32)
+    lens = np.zeros(w.B, dtype=np.int32)
+    idx = np.full((w.B, w.s_q, w.indices.shape[2] + idx2.shape[2]), -1, dtype=np.int32)
+    for b in range(w.B):
+        n1 = int(nb1[b])
+        bt[b, :n1] = w.block_table[b, :n1]
+        bt[b, n1:n1 + bt2.shape[1]] = bt2[b] + pool1
+        lens[b] = n1 * 64 + int(sl2[b])
+        for s in range(w.s_q):
+            m1 = w.indices[b, s]
+            m1 = np.where((m1 >= 0) & (m1 < w.cache_seqlens[b]), m1, -1)
+            m2 = idx2[b, s]
+            m2 = np.where((m2 >= 0) & (m2 < sl2[b]), m2 + n1 * 64, -1)
+            idx[b, s] = np.concatenate([m1, m2])
+    O2, L2 = orc.decode(w.q, w.kv, w.block_table, w.cache_seqlens, 512, indices=w.indices, aux=w.aux)
+    O1, L1 = orc.decode(w.q, kv, bt, lens, 512, indices=idx)
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+
+
+def test_dual_matches_sdpa_on_gathered_keys():
+    w = _dual_small(26, 512, topk2=30)
+    kv2, bt2, sl2, idx2 = w.aux
+    O, LSE = orc.decode(w.q, w.kv, w.block_table, w.cache_seqlens, 512, indices=w.indices, aux=w.aux)
+    for b, s in [(0, 0), (1, 1), (2, 0)]:
+        rows = []
+        for cache, table, L, ix in ((w.kv, w.block_table, w.cache_seqlens[b], w.indices[b, s]),
+                                    (kv2, bt2, sl2[b], idx2[b, s])):
+            for j in ix[(ix >= 0) & (ix < L)]:
+                rows.append(cache[int(table[b, j // 64]), j % 64, 0].astype(np.int32))
+        K = torch.from_numpy(np.stack(rows)).to(torch.int16).view(torch.bfloat16).double()
+        q = _q(w, b, s)
+        ref = F.scaled_dot_product_attention(q[None, :, None, :], K[None, None].expand(1, 16, -1, -1),
+                                             K[None, None].expand(1, 16, -1, -1), scale=512 ** -0.5)
+        np.testing.assert_allclose(O[b, s], ref[0, :, 0].numpy(), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(LSE[b, s], torch.logsumexp(512 ** -0.5 * (K @ q.T), dim=0).numpy(),
+                                   rtol=0, atol=1e-12)
+
+
 def test_causal_matches_sdpa_with_explicit_mask():
     # bottom-right alignment: token s of s_q sees keys 0 .. L - s_q + s
     w = small(12, [70, 5, 130], s_q=3, h_q=8, causal=True)
