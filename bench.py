@@ -102,7 +102,7 @@ def run_workload(torch, m, w, steps, warmup, ncopies=NCOPIES):
                _to_dev(torch, sl2.astype(np.int32)), _to_dev(torch, idx2.astype(np.int32)))
         topk2 = idx2.shape[2]
     plan, ns = m.get_mla_metadata(sl, rows, h_kv, s_q=w.s_q, topk=w.topk, topk2=topk2)
-    W = plan.numel() // 8 - 1
+    W = int(plan[0].item())                   # header word 0
     B = w.B
     o = torch.empty((B, w.s_q, w.h_q, 512), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((B, w.s_q, w.h_q), dtype=torch.float32, device="cuda")
@@ -122,6 +122,10 @@ def run_workload(torch, m, w, steps, warmup, ncopies=NCOPIES):
         decode_call(k, p, n, 1)      # split decode kernel
         decode_call(k, p, n, 2)      # merge of split items
 
+    def step_single(k):
+        p, n = plan_call(k)
+        decode_call(k, p, n, 4)      # split decode that merges split items itself
+
     def timed(fn, n):
         """GPU time of n calls of fn enqueued back to back (events at the two ends only)."""
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -139,13 +143,16 @@ def run_workload(torch, m, w, steps, warmup, ncopies=NCOPIES):
     torch.cuda.synchronize()
     # Timed region: K whole steps.
     total_ms, wall = timed(step, steps)
+    single_ms, _ = timed(step_single, steps)
     # Each launch of the step on its own: K launches back to back on the
     # stream the library launches on, so the average is the launch duration
     # plus the gap between two launches.
     plan_total, _ = timed(plan_call, steps)
     dec_total, _ = timed(lambda k: decode_call(k, plan, ns, 1), steps)
     comb_total, _ = timed(lambda k: decode_call(k, plan, ns, 2), steps)
-    return dict(ms_per_step=total_ms / steps, wall_s=wall, plan_ms=plan_total / steps,
+    fused_total, _ = timed(lambda k: decode_call(k, plan, ns, 4), steps)
+    return dict(ms_per_step=total_ms / steps, ms_per_step_single=single_ms / steps,
+                decode_single_ms=fused_total / steps, wall_s=wall, plan_ms=plan_total / steps,
                 decode_ms=dec_total / steps, combine_ms=comb_total / steps, num_workers=W, o=o, lse=lse)
 
 
@@ -267,7 +274,9 @@ def main():
                    "num_workers": r["num_workers"], "kv_copies_rotated": NCOPIES},
         "tflops": round(flops / step_s / 1e12, 3),
         "step_breakdown_ms": {"plan": round(r["plan_ms"], 5), "decode": round(r["decode_ms"], 5),
-                              "combine": round(r["combine_ms"], 5)},
+                              "combine": round(r["combine_ms"], 5),
+                              "single_launch_decode": round(r["decode_single_ms"], 5),
+                              "single_launch_step": round(r["ms_per_step_single"], 5)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(w.name),

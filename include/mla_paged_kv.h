@@ -131,7 +131,9 @@ int mla_get_metadata(const int32_t* cache_seqlens, int batch, int s_q,
 
 /*
  * mla_workspace_bytes — host only; bytes of the decode scratch buffer:
- * (items + W) partial results of num_q_rows x (dv + 1) fp32 values each.
+ * (items + W) partial results of num_q_rows x (dv + 1) fp32 values each, then
+ * one int32 arrival counter per item and row tile (the single-launch mode of
+ * mla_decode_with_kvcache_phase).
  */
 size_t mla_workspace_bytes(int batch, int s_q, int num_q_rows, int h_kv, int topk,
                            int dv, int num_workers);
@@ -182,9 +184,18 @@ int mla_decode_with_kvcache(const void* q, const void* kvcache, int64_t num_page
  * kernel only (items covered by one worker get their final o / lse, the others
  * get fp32 partials in `workspace`); phases = 2 runs the merge of the partials
  * only (it must follow phase 1 on the same stream with the same arguments);
- * phases = 3 runs both and is mla_decode_with_kvcache.  Any other value
- * returns MLA_ERR_INVALID_ARGUMENT.  Same arguments, checks and ownership rules as
- * mla_decode_with_kvcache.
+ * phases = 3 runs both and is mla_decode_with_kvcache.  phases = 4 is the
+ * single-launch decode (a fixed launch overhead matters: "Blackwell을 위한
+ * 새로운 MLA 백엔드: TOKENSPEED_MLA 분석", section "왜 이게 좋은 최적화인가?",
+ * item 3): one kernel, in
+ * which the last run of each split item to finish merges the item's partials
+ * and items without a key are written as well.  Its runs exchange partials
+ * through memory at agent scope and count arrivals in the last
+ * items * ceil(rows / tile rows) ints of `workspace`, which must be zero
+ * before the first phases = 4 call on a workspace; every completed call
+ * leaves them zero (calls sharing one workspace must not overlap).  Any other
+ * value returns MLA_ERR_INVALID_ARGUMENT.  Same arguments, checks and
+ * ownership rules as mla_decode_with_kvcache.
  */
 int mla_decode_with_kvcache_phase(const void* q, const void* kvcache, int64_t num_pages,
                                   int page_size, const int32_t* block_table, int max_blocks,

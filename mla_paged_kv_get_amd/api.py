@@ -95,7 +95,10 @@ def mla_decode_with_kvcache(q: torch.Tensor, kvcache: torch.Tensor, block_table:
     656]`` for packed FP8 rows (512 E4M3 latent codes, 4 float32 block scales,
     64 bf16 RoPE values).  ``phases`` (1 = split kernel, 2 = merge kernel, 3 =
     both) lets a caller launch the two kernels separately with the same
-    arguments and buffers.  ``aux = (kvcache2, block_table2, cache_seqlens2,
+    arguments and buffers; ``phases=4`` is the single-launch decode, whose
+    kernel merges split items itself, counting finished runs in counters that
+    the plan carries (zeroed by get_mla_metadata, left zero by every completed
+    call: single-launch calls that share a plan must not overlap).  ``aux = (kvcache2, block_table2, cache_seqlens2,
     indices2)`` adds an auxiliary bf16 cache (sparse mode): each query token
     attends to the union of its keys in both caches; the plan then comes from
     ``get_mla_metadata(..., topk=topk, topk2=indices2.shape[2])``.

@@ -79,6 +79,10 @@ size_t workspace_for(const Shape& s, int dv, int W) {
   return slots * (size_t)s.rows * ((size_t)dv + 1) * sizeof(float);
 }
 
+// Arrival counters of the single-launch mode, after the plan's rows: one per
+// item and row tile.
+int64_t plan_counters(const Shape& s) { return (int64_t)s.items * s.m_tiles; }
+
 }  // namespace
 
 extern "C" {
@@ -105,8 +109,10 @@ int mla_plan_dims(int batch, int s_q, int num_q_rows, int h_kv, int topk, int nu
   int W = 0;
   st = workers_for(s, num_workers_request, &W);
   if (st != MLA_OK) return st;
+  const int64_t words = (int64_t)kPlanWords * (W + 1) + plan_counters(s);
+  if (words > 0x7fffffff) return MLA_ERR_UNSUPPORTED;
   *out_num_workers = W;
-  *out_plan_words = kPlanWords * (W + 1);
+  *out_plan_words = (int)words;
   *out_num_items = s.items;
   return MLA_OK;
 }
@@ -114,8 +120,9 @@ int mla_plan_dims(int batch, int s_q, int num_q_rows, int h_kv, int topk, int nu
 int mla_plan_num_workers(int plan_words, int batch, int s_q, int num_q_rows, int h_kv, int topk) {
   Shape s;
   if (shape_of(batch, s_q, num_q_rows, h_kv, topk, &s) != MLA_OK) return -1;
-  if (plan_words < 2 * kPlanWords || plan_words % kPlanWords) return -1;
-  return plan_words / kPlanWords - 1;
+  const int64_t rows_words = (int64_t)plan_words - plan_counters(s);
+  if (rows_words < 2 * kPlanWords || rows_words % kPlanWords) return -1;
+  return (int)(rows_words / kPlanWords - 1);
 }
 
 int mla_get_metadata(const int32_t* cache_seqlens, int batch, int s_q, int num_q_rows, int h_kv,
@@ -130,7 +137,8 @@ int mla_get_metadata(const int32_t* cache_seqlens, int batch, int s_q, int num_q
   const int overhead = variant_overhead(s.variant);
   const hipError_t e = launch_plan(cache_seqlens, topk > 0 ? topk : 0, s.items, h_kv, num_workers,
                                    overhead, plan, num_splits,
-                                   reinterpret_cast<hipStream_t>(stream));
+                                   plan + (int64_t)kPlanWords * (num_workers + 1),
+                                   (int)plan_counters(s), reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
@@ -166,7 +174,7 @@ int decode_impl(const void* q, const void* kvcache, int64_t num_pages, int page_
                 const int32_t* indices, int topk, void* o, float* lse, void* workspace,
                 size_t workspace_bytes, int kv_format, const AuxCache* aux, int phases,
                 void* stream) {
-  if (phases < 1 || phases > 3) return MLA_ERR_INVALID_ARGUMENT;
+  if (phases < 1 || phases > 4) return MLA_ERR_INVALID_ARGUMENT;
   if (batch < 0 || s_q < 1 || h_q < 1 || h_kv < 1 || max_blocks < 1 || num_pages < 1)
     return MLA_ERR_INVALID_ARGUMENT;
   if (h_q % h_kv) return MLA_ERR_INVALID_ARGUMENT;
@@ -210,6 +218,9 @@ int decode_impl(const void* q, const void* kvcache, int64_t num_pages, int page_
   const size_t slots = (size_t)s.items + (size_t)num_workers;
   a.part_o = static_cast<float*>(workspace);
   a.part_lse = a.part_o + slots * (size_t)s.rows * kDv;
+  // the plan carries the arrival counters (zeroed by mla_get_metadata)
+  a.arrivals = const_cast<int32_t*>(plan) + (int64_t)kPlanWords * (num_workers + 1);
+  a.fused = phases == 4;
   a.max_blocks = max_blocks;
   a.batch = batch;
   a.s_q = s_q;
@@ -243,6 +254,10 @@ int decode_impl(const void* q, const void* kvcache, int64_t num_pages, int page_
     a.nb_sparse += (aux->topk + kPage - 1) / kPage;
   }
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (phases == 4) {
+    if (launch_decode(a, s.variant, hs) != hipSuccess) return MLA_ERR_HIP;
+    return MLA_OK;
+  }
   if (phases & 1) {
     if (launch_decode(a, s.variant, hs) != hipSuccess) return MLA_ERR_HIP;
   }

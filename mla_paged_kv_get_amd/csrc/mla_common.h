@@ -82,6 +82,13 @@ struct DecodeArgs {
   int topk2;
   int nb1;                    // tiles of the main list of a sparse item
   int nb_sparse;              // tiles of a sparse item (both lists)
+  // Single-launch mode: the decode kernel merges the partials of split items
+  // itself (the last run of an item and row tile to finish does it) and
+  // writes the items without keys; arrivals[item * m_tiles + row tile] (in
+  // the plan, after its rows) counts finished runs and is zero outside a
+  // launch.
+  int fused;
+  int* arrivals;
 };
 
 // Row of q / o / lse ([batch * s_q * h_q] rows) holding query row `row` of
@@ -100,7 +107,8 @@ __device__ __forceinline__ int item_seq(const DecodeArgs& a, int item) {
 
 // Launchers (defined next to their kernels).
 hipError_t launch_plan(const int32_t* seqlens, int topk, int num_items, int item_div, int num_workers,
-                       int overhead, int32_t* plan, int32_t* num_splits, hipStream_t stream);
+                       int overhead, int32_t* plan, int32_t* num_splits, int32_t* counters,
+                       int num_counters, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int variant, hipStream_t stream);
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_row_ids(const int32_t* block_table, int max_blocks, const int32_t* seqlens,

@@ -195,6 +195,47 @@ __device__ __forceinline__ void barrier_keep_loads() {
   asm volatile("s_barrier" ::: "memory");
 }
 
+// Partials of split items.  In the single-launch mode the runs of an item,
+// which may sit on different XCDs (each with its own L2, not coherent with the
+// others), exchange them through memory: stores and loads at agent scope
+// (sc1), so no L2 write-back or invalidate is needed.
+template <bool kAgent>
+__device__ __forceinline__ floatx4 load_part4(const float* p) {
+  if constexpr (!kAgent) {
+    return *reinterpret_cast<const floatx4*>(p);
+  } else {
+    uint64_t* q = reinterpret_cast<uint64_t*>(const_cast<float*>(p));
+    const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    floatx4 v;
+    v[0] = __uint_as_float((unsigned)lo);
+    v[1] = __uint_as_float((unsigned)(lo >> 32));
+    v[2] = __uint_as_float((unsigned)hi);
+    v[3] = __uint_as_float((unsigned)(hi >> 32));
+    return v;
+  }
+}
+template <bool kAgent>
+__device__ __forceinline__ float load_part1(const float* p) {
+  if constexpr (!kAgent) {
+    return *p;
+  } else {
+    unsigned* q = reinterpret_cast<unsigned*>(const_cast<float*>(p));
+    return __uint_as_float(__hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  }
+}
+__device__ __forceinline__ void store_part4_agent(float* p, floatx4 v) {
+  uint64_t* q = reinterpret_cast<uint64_t*>(p);
+  const uint64_t lo = (uint64_t)__float_as_uint(v[0]) | ((uint64_t)__float_as_uint(v[1]) << 32);
+  const uint64_t hi = (uint64_t)__float_as_uint(v[2]) | ((uint64_t)__float_as_uint(v[3]) << 32);
+  __hip_atomic_store(q, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(q + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_part1_agent(float* p, float v) {
+  __hip_atomic_store(reinterpret_cast<unsigned*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // o = 0, lse = -inf for row r of an item with no key (one wave, 8 columns per lane).
 __device__ __forceinline__ void write_empty_row(const DecodeArgs& a, int item, int r, int lane) {
   const int64_t orow = q_row(a, item, r);
@@ -205,6 +246,7 @@ __device__ __forceinline__ void write_empty_row(const DecodeArgs& a, int item, i
 // Log-sum-exp merge of the n partials of row r of an item, one wave per row,
 // 8 columns per lane.  The partial LSEs are read lane-parallel for the max;
 // the weighted sum of the partial rows keeps 4 reads in flight.
+template <bool kAgent>
 __device__ __forceinline__ void merge_row(const DecodeArgs& a, int item, int slot0, int n, int r, int lane) {
   const int64_t orow = q_row(a, item, r);
   if (n <= 8) {
@@ -216,10 +258,9 @@ __device__ __forceinline__ void merge_row(const DecodeArgs& a, int item, int slo
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       if (k < n) {
-        lk[k] = a.part_lse[(int64_t)(slot0 + k) * a.M + r];
-        const floatx4* src = reinterpret_cast<const floatx4*>(o_col + k * stride);
-        v0[k] = src[0];
-        v1[k] = src[1];
+        lk[k] = load_part1<kAgent>(a.part_lse + (int64_t)(slot0 + k) * a.M + r);
+        v0[k] = load_part4<kAgent>(o_col + k * stride);
+        v1[k] = load_part4<kAgent>(o_col + k * stride + 4);
       }
     }
     float mx = -INFINITY;
@@ -253,7 +294,7 @@ __device__ __forceinline__ void merge_row(const DecodeArgs& a, int item, int slo
     return;
   }
   float mx = -INFINITY;
-  for (int k = lane; k < n; k += 64) mx = fmaxf(mx, a.part_lse[(int64_t)(slot0 + k) * a.M + r]);
+  for (int k = lane; k < n; k += 64) mx = fmaxf(mx, load_part1<kAgent>(a.part_lse + (int64_t)(slot0 + k) * a.M + r));
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d, 64));
   float acc[8];
@@ -266,11 +307,10 @@ __device__ __forceinline__ void merge_row(const DecodeArgs& a, int item, int slo
     const int64_t stride = (int64_t)a.M * kDv;
 #pragma unroll 4
     for (int k = 0; k < n; ++k) {
-      const float lk = lse_col[(int64_t)k * a.M];
+      const float lk = load_part1<kAgent>(lse_col + (int64_t)k * a.M);
       const float wk = lk == -INFINITY ? 0.f : expf(lk - mx);
       tot += wk;
-      const floatx4* src = reinterpret_cast<const floatx4*>(o_col + k * stride);
-      const floatx4 v0 = src[0], v1 = src[1];
+      const floatx4 v0 = load_part4<kAgent>(o_col + k * stride), v1 = load_part4<kAgent>(o_col + k * stride + 4);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         acc[i] += wk * v0[i];
@@ -286,7 +326,7 @@ __device__ __forceinline__ void merge_row(const DecodeArgs& a, int item, int slo
   if (lane == 0) a.lse[orow] = tot > 0.f ? mx + logf(tot) : -INFINITY;
 }
 
-template <int V, bool SPARSE, bool KV8, int D>
+template <int V, bool SPARSE, bool KV8, int D, bool FUSED>
 __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
   using C = Cfg<V, KV8, D>;
   constexpr bool kWide = C::kWide;
@@ -956,6 +996,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
 
     // Finish the run of `item`: write O/LSE, or the fp32 partial when the item
     // is split over several runs.
+    int merge_item[2] = {-1, -1};   // single launch: split items whose partials this workgroup merges
+    int n_merge = 0;
     auto finish = [&](int item, int split) __attribute__((always_inline)) {
       const int slot0 = read_scalar(a.num_splits + item);
       const int nsplit = read_scalar(a.num_splits + item + 1) - slot0;
@@ -1000,14 +1042,36 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
               floatx4 v;
 #pragma unroll
               for (int i = 0; i < 4; ++i) v[i] = oacc[d][4 * q4 + i] * inv;
-              *reinterpret_cast<floatx4*>(orp + (kWide ? 32 * d + 8 * q4 : 16 * d)) = v;
+              float* dst = orp + (kWide ? 32 * d + 8 * q4 : 16 * d);
+              if constexpr (FUSED) store_part4_agent(dst, v);
+              else *reinterpret_cast<floatx4*>(dst) = v;
             }
         }
         const bool lse_lane = kWide ? (half == 0 && hl == 0) : (tg == 0 && g == 0);
         if (lse_lane) {
           const float lse = l_tot > 0.f ? m_ref * kLn2 + logf(l_tot) : -INFINITY;
-          if (final_out) a.lse[orow] = lse; else a.part_lse[orow] = lse;
+          if (final_out) a.lse[orow] = lse;
+          else if (FUSED) store_part1_agent(a.part_lse + orow, lse);
+          else a.part_lse[orow] = lse;
         }
+      }
+      if (FUSED && !final_out) {
+        // Single launch: count this run in.  The last run of the item (and
+        // row tile) to arrive merges the partials once its own tile stream is
+        // done (a worker has at most two split runs: its first and its last
+        // item).  Every wave's partial stores are complete before the count
+        // is raised.
+        __builtin_amdgcn_s_waitcnt(0);
+        barrier_keep_loads();
+        if (threadIdx.x == 0)
+          red_need[0] = __hip_atomic_fetch_add(a.arrivals + (int64_t)item * a.m_tiles + mt, 1,
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        barrier_keep_loads();
+        if (red_need[0] == nsplit - 1) {
+          merge_item[n_merge] = item;
+          ++n_merge;
+        }
+        barrier_keep_loads();   // red_need is reused by the next tile's softmax
       }
       // reset for the next run
 #pragma unroll
@@ -1154,6 +1218,28 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     };
     while (step(s0, s1) && step(s1, s0)) {
     }
+    if constexpr (FUSED) {
+      // merge the split items whose last run this was, and clear their counts
+      for (int k = 0; k < n_merge; ++k) {
+        const int item = merge_item[k];
+        const int slot0 = a.num_splits[item];
+        const int nsplit = a.num_splits[item + 1] - slot0;
+        for (int r = wave; r < C::kRows; r += C::kWaves)
+          if (row0 + r < a.M) merge_row<true>(a, item, slot0, nsplit, row0 + r, lane);
+        if (threadIdx.x == 0)
+          __hip_atomic_store(a.arrivals + (int64_t)item * a.m_tiles + mt, 0, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+  if constexpr (FUSED) {
+    // Single launch: items without a key get o = 0, lse = -inf (all their
+    // rows), item i from participating workgroup i mod (workers x row tiles).
+    const int wid = w * a.m_tiles + mt, nwg = a.num_workers * a.m_tiles;
+    for (int i = wid; i < a.num_items; i += nwg) {
+      if (a.num_splits[i + 1] == a.num_splits[i])
+        for (int r = wave; r < a.M; r += C::kWaves) write_empty_row(a, i, r, lane);
+    }
   }
 }
 
@@ -1167,7 +1253,7 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int r = blockIdx.y * 4 + wave; r < a.M; r += 4 * gridDim.y) {
     if (n == 0) write_empty_row(a, item, r, lane);
-    else merge_row(a, item, slot0, n, r, lane);
+    else merge_row<false>(a, item, slot0, n, r, lane);
   }
 }
 
@@ -1175,10 +1261,16 @@ template <int V, bool KV8, int D>
 hipError_t launch_variant(const DecodeArgs& a, hipStream_t stream) {
   const int groups = (a.num_workers + 7) / 8;
   const int grid = a.m_tiles == 1 ? a.num_workers : groups * 8 * a.m_tiles;
-  if (a.topk > 0)
-    hipLaunchKernelGGL((decode_kernel<V, true, KV8, D>), dim3(grid), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((decode_kernel<V, false, KV8, D>), dim3(grid), dim3(256), 0, stream, a);
+  if (a.fused) {
+    if (a.topk > 0)
+      hipLaunchKernelGGL((decode_kernel<V, true, KV8, D, true>), dim3(grid), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_kernel<V, false, KV8, D, true>), dim3(grid), dim3(256), 0, stream, a);
+  } else if (a.topk > 0) {
+    hipLaunchKernelGGL((decode_kernel<V, true, KV8, D, false>), dim3(grid), dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((decode_kernel<V, false, KV8, D, false>), dim3(grid), dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

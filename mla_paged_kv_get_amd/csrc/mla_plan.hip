@@ -55,7 +55,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
                                                             int topk, int num_items, int item_div,
                                                             int W, int c,
                                                             int32_t* __restrict__ plan,
-                                                            int32_t* __restrict__ num_splits) {
+                                                            int32_t* __restrict__ num_splits,
+                                                            int32_t* __restrict__ counters,
+                                                            int num_counters) {
   __shared__ int start[kPlanMaxItems + 1];
   __shared__ int wave_sums[kPlanThreads / 64];
   const int tid = threadIdx.x;
@@ -145,6 +147,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     row[6] = 0;
     row[7] = 0;
   }
+  // arrival counters of the single-launch decode start at zero
+  for (int i = tid; i < num_counters; i += kPlanThreads) counters[i] = 0;
   if (tid == 0) {
     plan[0] = W;
     plan[1] = c;
@@ -162,9 +166,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
 int plan_max_items() { return kPlanMaxItems; }
 
 hipError_t launch_plan(const int32_t* seqlens, int topk, int num_items, int item_div, int num_workers,
-                       int overhead, int32_t* plan, int32_t* num_splits, hipStream_t stream) {
+                       int overhead, int32_t* plan, int32_t* num_splits, int32_t* counters,
+                       int num_counters, hipStream_t stream) {
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, seqlens, topk, num_items,
-                     item_div, num_workers, overhead, plan, num_splits);
+                     item_div, num_workers, overhead, plan, num_splits, counters, num_counters);
   return hipGetLastError();
 }
 

@@ -51,11 +51,12 @@ def _dims(*a):
 
 
 def test_plan_dims():
-    assert _dims(64, 1, 16, 1, 0, 256) == (0, 256, 8 * 257, 64)
-    assert _dims(16, 8, 8 * 128, 1, 2048, 100) == (0, 100, 8 * 101, 128)       # sparse: items = b * s_q
-    assert _dims(32, 2, 256, 1, 0, 128) == (0, 128, 8 * 129, 32)
-    assert _dims(4, 1, 16, 2, 0, 8) == (0, 8, 8 * 9, 8)                         # h_kv = 2: items = b * h_kv
-    assert _dims(4, 2, 2 * 16, 4, 64, 8) == (0, 8, 8 * 9, 32)                  # sparse: items = b * s_q * h_kv
+    # words = 8 (W + 1) plan rows + one arrival counter per item and 64- (or 16-) row tile
+    assert _dims(64, 1, 16, 1, 0, 256) == (0, 256, 8 * 257 + 64, 64)
+    assert _dims(16, 8, 8 * 128, 1, 2048, 100) == (0, 100, 8 * 101 + 128 * 2, 128)  # sparse: items = b * s_q
+    assert _dims(32, 2, 256, 1, 0, 128) == (0, 128, 8 * 129 + 32 * 4, 32)
+    assert _dims(4, 1, 16, 2, 0, 8) == (0, 8, 8 * 9 + 8, 8)                     # h_kv = 2: items = b * h_kv
+    assert _dims(4, 2, 2 * 16, 4, 64, 8) == (0, 8, 8 * 9 + 32, 32)             # sparse: items = b * s_q * h_kv
     assert _dims(4, 3, 16, 1, 64, 8)[0] == _lib.MLA_ERR_INVALID_ARGUMENT        # rows not a multiple of s_q
     assert _dims(-1, 1, 16, 1, 0, 8)[0] == _lib.MLA_ERR_INVALID_ARGUMENT
     assert _dims(4, 1, 16, 1, 0, -3)[0] == _lib.MLA_ERR_INVALID_ARGUMENT
@@ -63,6 +64,7 @@ def test_plan_dims():
 
 def test_workspace_bytes():
     l = _lib.lib()
+    # (items + W) partial slots of rows x 513 floats
     assert l.mla_workspace_bytes(64, 1, 16, 1, 0, 512, 256) == (64 + 256) * 16 * 513 * 4
     assert l.mla_workspace_bytes(16, 8, 1024, 1, 2048, 512, 256) == (128 + 256) * 128 * 513 * 4
     assert l.mla_workspace_bytes(64, 1, 16, 1, 0, 512, 0) == 0
@@ -113,7 +115,7 @@ def test_phase_argument_checked():
     args = [DUMMY, DUMMY, 10, 64, DUMMY, 4, DUMMY, 2, 1, 16, 1, 576, 512, DUMMY, DUMMY, 8, 0,
             ctypes.c_float(0.05), None, 0, DUMMY, DUMMY, DUMMY, 1 << 40]
     assert l.mla_decode_with_kvcache_phase(*args, 0, None) == _lib.MLA_ERR_INVALID_ARGUMENT
-    assert l.mla_decode_with_kvcache_phase(*args, 4, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert l.mla_decode_with_kvcache_phase(*args, 5, None) == _lib.MLA_ERR_INVALID_ARGUMENT
 
 
 def test_fp8_entries_reject():
@@ -191,5 +193,5 @@ def test_plan_num_workers_inverts_plan_dims():
             assert st == 0 and Wd == W
             assert l.mla_plan_num_workers(words, *shape) == W
     assert l.mla_plan_num_workers(5, 64, 1, 16, 1, 0) == -1
-    assert l.mla_plan_num_workers(8 * 10 + 3, 64, 1, 16, 1, 0) == -1  # not whole rows
-    assert l.mla_plan_num_workers(8, 64, 1, 16, 1, 0) == -1           # header only
+    assert l.mla_plan_num_workers(8 * 10 + 64 + 3, 64, 1, 16, 1, 0) == -1  # not whole rows
+    assert l.mla_plan_num_workers(8 + 64, 64, 1, 16, 1, 0) == -1           # header only
