@@ -150,6 +150,21 @@ __device__ __forceinline__ int read_scalar(const int32_t* p) {
   asm volatile("s_load_dword %0, %1, 0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
   return v;
 }
+// Two such reads in flight together, one wait.
+__device__ __forceinline__ void read_scalar2(const int32_t* p0, const int32_t* p1, int& v0, int& v1) {
+  asm volatile("s_load_dword %0, %2, 0\n\ts_load_dword %1, %3, 0\n\ts_waitcnt lgkmcnt(0)"
+               : "=&s"(v0), "=&s"(v1)
+               : "s"(p0), "s"(p1)
+               : "memory");
+}
+
+// The same for eight consecutive ints (a plan row).
+typedef int int32x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ int32x8 read_scalar8(const int32_t* p) {
+  int32x8 v;
+  asm volatile("s_load_dwordx8 %0, %1, 0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return v;
+}
 
 // One global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane
 // l's bytes land at lds + 16 l.  Issued from inline assembly, M0 saved and
@@ -358,6 +373,13 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
   // scalar round trip sits on the critical path of a step.
   __shared__ __attribute__((aligned(256))) int idxbuf[kWide ? 4 : 1][4][64];
 
+  // The arguments on the way to the first tile copy, loaded in one go (left
+  // to itself, the compiler loads each one where it is first used, a round
+  // trip apiece).
+  asm volatile("" ::"s"(a.q), "s"(a.kv), "s"(a.block_table), "s"(a.seqlens), "s"(a.plan), "s"(a.m_tiles),
+               "s"(a.num_workers), "s"(a.max_blocks), "s"(a.s_q), "s"(a.M), "s"(a.h_kv), "s"(a.G),
+               "s"(a.topk));
+
   // Worker and row tile of this workgroup.  Row tiles of one worker are placed
   // 8 workgroups apart so that they land on the same XCD (workgroups are
   // dealt to the 8 XCDs round-robin) and share its L2 for the common tiles.
@@ -387,7 +409,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
   const bool row_ok = row < a.M;
   constexpr bool sparse = SPARSE;      // top-k index lists (a.topk > 0)
 
-  const int32_t* prow = a.plan + kPlanWords * (1 + w);
+  const int32x8 prow = read_scalar8(a.plan + kPlanWords * (1 + w));
   const int it_first = prow[0], blk_first = prow[1], it_last = prow[2], blk_end = prow[3],
             split_first = prow[4];
 
@@ -446,8 +468,13 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
       const int x = it_first + lane;
       lens_v = a.seqlens[item_seq(a, x)];
     }
+    // The first item's length and the page of the first tile (dense) come in
+    // by scalar loads in the prologue, so that the first copy does not wait
+    // for the vector loads (the other lengths, the query rows).
+    int len_first = 0, page_first = 0;
     auto item_len = [&](int x) __attribute__((always_inline)) -> int {      // x is wave-uniform
       const int j = x - it_first;
+      if (j == 0) return len_first;
       if (j < 64) return __builtin_amdgcn_readlane(lens_v, j);
       return read_scalar(a.seqlens + item_seq(a, x));
     };
@@ -1090,9 +1117,14 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     // first copy is issued: a tracked load still pending behind a copy would
     // make its first use wait for the copy as well.
     TileRaw raw;
-    if constexpr (!sparse) raw.v[0] = a.block_table[(int64_t)item_seq(a, cur_item) * a.max_blocks + cur_blk];
-    else tile_fetch(cur_item, cur_blk, raw);
+    if constexpr (sparse) tile_fetch(cur_item, cur_blk, raw);
     load_q(cur_item);
+    {
+      const int seq = item_seq(a, cur_item);
+      read_scalar2(a.seqlens + seq, a.block_table + (int64_t)seq * a.max_blocks + (sparse ? 0 : cur_blk),
+                   len_first, page_first);
+    }
+    if constexpr (!sparse) raw.v[0] = page_first;
     int cur_hi = seg_hi(cur_item);
     int nx_item, nx_blk, nx_hi;
     advance(cur_item, cur_blk, cur_hi, nx_item, nx_blk, nx_hi);

@@ -16,31 +16,39 @@
 namespace mla {
 namespace {
 
-constexpr int kPlanThreads = 1024;
+constexpr int kPlanThreads = 256;
+constexpr int kPlanWaves = kPlanThreads / 64;
 constexpr int kPlanMaxItems = 16384;
 
-// Inclusive scan of one int per thread over the workgroup.
-__device__ int block_inclusive_scan(int v, int* wave_sums) {
+// floor(num / den) for 0 <= num < 2^53 and den >= 1: the quotient in double
+// precision is within one of the floor, and one comparison each way fixes it.
+__device__ __forceinline__ int64_t floor_div(int64_t num, int64_t den) {
+  int64_t q = (int64_t)((double)num / (double)den);
+  if (q * den > num) --q;
+  else if ((q + 1) * den <= num) ++q;
+  return q;
+}
+
+// Inclusive scan of one int per thread over the workgroup; `total` receives
+// the sum over all threads.  One barrier; `wave_sums` must not be written
+// again before the next barrier.
+__device__ int block_inclusive_scan(int v, int* wave_sums, int& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
-    int o = __shfl_up(v, d, 64);
+    const int o = __shfl_up(v, d, 64);
     if (lane >= d) v += o;
   }
   if (lane == 63) wave_sums[wave] = v;
   __syncthreads();
-  if (wave == 0) {
-    int s = lane < (kPlanThreads / 64) ? wave_sums[lane] : 0;
+  int before = 0, tot = 0;
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      int o = __shfl_up(s, d, 64);
-      if (lane >= d) s += o;
-    }
-    if (lane < kPlanThreads / 64) wave_sums[lane] = s;
+  for (int j = 0; j < kPlanWaves; ++j) {
+    const int s = wave_sums[j];
+    before += j < wave ? s : 0;
+    tot += s;
   }
-  __syncthreads();
-  const int before = wave > 0 ? wave_sums[wave - 1] : 0;
-  __syncthreads();
+  total = tot;
   return v + before;
 }
 
@@ -59,26 +67,35 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
                                                             int32_t* __restrict__ counters,
                                                             int num_counters) {
   __shared__ int start[kPlanMaxItems + 1];
-  __shared__ int wave_sums[kPlanThreads / 64];
+  __shared__ int sums_a[kPlanWaves], sums_b[kPlanWaves];
   const int tid = threadIdx.x;
   const int per = (num_items + kPlanThreads - 1) / kPlanThreads;
   const int i0 = min(tid * per, num_items), i1 = min(i0 + per, num_items);
 
-  // Start of every item on the cost axis.
+  // arrival counters of the single-launch decode start at zero
+  for (int i = tid; i < num_counters; i += kPlanThreads) counters[i] = 0;
+
+  // Start of every item on the cost axis (the blocks are parked in start[]
+  // until the scan is done).
   int local = 0;
-  for (int i = i0; i < i1; ++i) local += c + item_blocks(seqlens, topk, item_div, i);
-  const int incl = block_inclusive_scan(local, wave_sums);
+  for (int i = i0; i < i1; ++i) {
+    const int n = item_blocks(seqlens, topk, item_div, i);
+    start[i] = n;
+    local += c + n;
+  }
+  int T;
+  const int incl = block_inclusive_scan(local, sums_a, T);
   int run = incl - local;
   for (int i = i0; i < i1; ++i) {
+    const int n = start[i];
     start[i] = run;
-    run += c + item_blocks(seqlens, topk, item_div, i);
+    run += c + n;
   }
-  if (tid == kPlanThreads - 1) start[num_items] = incl;
+  if (tid == 0) start[num_items] = T;
   __syncthreads();
-  const int T = start[num_items];
   const int We = min(W, T);
   // Owner of unit x (T >= 1 whenever an item has a block).
-  auto owner = [&](int x) -> int { return T > 0 ? (int)((((int64_t)x + 1) * We - 1) / T) : 0; };
+  auto owner = [&](int x) -> int { return T > 0 ? (int)floor_div(((int64_t)x + 1) * We - 1, T) : 0; };
 
   // Split counts and their exclusive prefix.
   local = 0;
@@ -86,22 +103,23 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     const int first = start[i] + c, end = start[i + 1];
     if (end > first) local += owner(end - 1) - owner(first) + 1;
   }
-  const int sincl = block_inclusive_scan(local, wave_sums);
+  int S;
+  const int sincl = block_inclusive_scan(local, sums_b, S);
   run = sincl - local;
   for (int i = i0; i < i1; ++i) {
     num_splits[i] = run;
     const int first = start[i] + c, end = start[i + 1];
     if (end > first) run += owner(end - 1) - owner(first) + 1;
   }
-  if (tid == kPlanThreads - 1) num_splits[num_items] = sincl;
+  if (tid == 0) num_splits[num_items] = S;
 
   // One row per worker.
   for (int w = tid; w < W; w += kPlanThreads) {
     int32_t* row = plan + kPlanWords * (1 + w);
     int lo = T, hi = T;
     if (w < We) {
-      lo = (int)(((int64_t)w * T) / We);
-      hi = (int)(((int64_t)(w + 1) * T) / We);
+      lo = (int)floor_div((int64_t)w * T, We);
+      hi = (int)floor_div((int64_t)(w + 1) * T, We);
     }
     int first_item = -1, first_blk = 0, last_item = -1, last_end = 0, split = 0;
     if (lo < hi) {
@@ -147,8 +165,6 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     row[6] = 0;
     row[7] = 0;
   }
-  // arrival counters of the single-launch decode start at zero
-  for (int i = tid; i < num_counters; i += kPlanThreads) counters[i] = 0;
   if (tid == 0) {
     plan[0] = W;
     plan[1] = c;

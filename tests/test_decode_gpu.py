@@ -33,6 +33,9 @@ def test_plan_bit_exact(W):
         (list(rng.integers(0, 300, 50)) + [0, 0, 5000], 128, 2, None),
         ([65536] * 4, 128, 8, 2048),
     ]
+    if W in (256, None):
+        # many items per scheduler thread, empty ones among them
+        cases.append((list(rng.integers(0, 1500, 3000)), 16, 1, None))
     for lengths, h_q, s_q, topk in cases:
         sl = i32_dev(np.array(lengths))
         plan, ns = m.get_mla_metadata(sl, s_q * h_q, 1, s_q=s_q, topk=topk, num_workers=W)
