@@ -102,7 +102,8 @@ __device__ __forceinline__ int64_t q_row(const DecodeArgs& a, int item, int row)
 }
 // Sequence (block-table row, length) of work item `item`.
 __device__ __forceinline__ int item_seq(const DecodeArgs& a, int item) {
-  return a.topk > 0 ? item / (a.h_kv * a.s_q) : item / a.h_kv;
+  const int d = a.topk > 0 ? a.h_kv * a.s_q : a.h_kv;
+  return d == 1 ? item : item / d;      // one KV head, one token: no division
 }
 
 // Launchers (defined next to their kernels).

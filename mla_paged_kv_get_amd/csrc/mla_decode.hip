@@ -530,6 +530,13 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     };
     // FP8: the row whose scales this lane copies (lanes 0..15 of the wave)
     const int sc_row = 16 * wave + (lane & 15);
+    // Dense: bytes per page (all heads), and the offsets inside a page of the
+    // rows this lane copies (tile_finish adds the page's offset).
+    const int64_t page_bytes = (int64_t)kPage * a.h_kv * C::kRowB;
+    int64_t row_in_page[C::kOffs];
+#pragma unroll
+    for (int r = 0; r < C::kOffs; ++r)
+      row_in_page[r] = (int64_t)(KV8 && r == 2 ? sc_row : cp_row[r < C::kLaneRows ? r : 0]) * a.h_kv * C::kRowB;
     auto tile_fetch = [&](int item, int blk, TileRaw& raw) __attribute__((always_inline)) {
       if constexpr (!sparse) {
         raw.v[0] = read_scalar(a.block_table + (int64_t)item_seq(a, item) * a.max_blocks + blk);   // not a vector load
@@ -549,16 +556,22 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     auto tile_finish = [&](int item, int blk, const TileRaw& raw, int64_t (&off)[C::kOffs],
                            unsigned char* vslot) __attribute__((always_inline)) {
       const int L = item_len(item);
-      const int kvh = item % a.h_kv;      // latent KV head of the item
+      const int kvh = a.h_kv == 1 ? 0 : item % a.h_kv;      // latent KV head of the item
       if constexpr (!sparse) {
-        const int64_t page = raw.v[0];
+        // byte offset of the tile's page and head (wave-uniform), plus each
+        // copied row's offset inside the page (precomputed for full tiles)
+        const int64_t base = (int64_t)__builtin_amdgcn_readfirstlane(raw.v[0]) * page_bytes +
+                             (int64_t)kvh * C::kRowB;
         const int nvalid = min(kPage, L - blk * kPage);
+        if (nvalid == kPage) {
 #pragma unroll
-        for (int r = 0; r < C::kLaneRows; ++r) {
-          const int t = min(cp_row[r], nvalid - 1);
-          off[r] = ((page * kPage + t) * a.h_kv + kvh) * (int64_t)C::kRowB;
+          for (int r = 0; r < C::kOffs; ++r) off[r] = base + row_in_page[r];
+        } else {
+#pragma unroll
+          for (int r = 0; r < C::kLaneRows; ++r)
+            off[r] = base + (int64_t)min(cp_row[r], nvalid - 1) * a.h_kv * C::kRowB;
+          if constexpr (KV8) off[2] = base + (int64_t)min(sc_row, nvalid - 1) * a.h_kv * C::kRowB;
         }
-        if constexpr (KV8) off[2] = ((page * kPage + min(sc_row, nvalid - 1)) * a.h_kv + kvh) * (int64_t)C::kRowB;
       } else {
         // auxiliary-cache tiles: its block table, lengths and rows (offsets
         // taken from the main cache's base)
