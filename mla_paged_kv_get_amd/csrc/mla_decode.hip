@@ -160,6 +160,7 @@ __device__ __forceinline__ void read_scalar2(const int32_t* p0, const int32_t* p
 
 // The same for eight consecutive ints (a plan row).
 typedef int int32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ int32x8 read_scalar8(const int32_t* p) {
   int32x8 v;
   asm volatile("s_load_dwordx8 %0, %1, 0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
@@ -650,40 +651,55 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
 
     // FP8: expand the copied tile `raw` into the bf16 tile layout in `tb`.
     // Thread (row t, latent block b) writes the 128 codes of block b of row t
-    // as bf16 (exact) and moves RoPE chunks 2b, 2b + 1 as they are.
+    // as bf16 (exact: every E4M3 value is a bf16 value) and moves RoPE chunks
+    // 2b, 2b + 1 as they are.  The LDS reads go out kBatch at a time ahead of
+    // the conversions (rows16: all of them; the wide variant has fewer
+    // registers to spare).
     auto expand_tile = [&](const char* raw, char* tb) __attribute__((always_inline)) {
+      constexpr int kBatch = kWide ? 2 : 8;
       const int t = threadIdx.x >> 2, b = threadIdx.x & 3;
       const int tr = t & 7, rb = t >> 3, sw = swz(t);
       const char* src = raw + ((rb * 5 + b) << 10) + (tr << 7);
       char* dst = tb + ((rb * C::kCG) << 10) + (tr << 7);
       const int sz = raw8_swz(t, b);
+      uint4 rope[2];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int pc = (i + b) & 7;      // 16 codes: latent values 128 b + 16 pc .. + 15
-        const uint4 u = *reinterpret_cast<const uint4*>(src + ((pc ^ sz) << 4));
-        const unsigned w4[4] = {u.x, u.y, u.z, u.w};
-        bf16x8 h[2];
+      for (int e = 0; e < 2; ++e) {
+        const int c = 2 * b + e;                 // RoPE chunk c -> bf16 chunk 64 + c
+        rope[e] = *reinterpret_cast<const uint4*>(raw + ((rb * 5 + 4) << 10) + (tr << 7) +
+                                                  ((c ^ raw8_swz(t, 4)) << 4));
+      }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w4[k], false);   // codes 4k, 4k + 1
-          const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w4[k], true);    // codes 4k + 2, 4k + 3
-          h[k >> 1][4 * (k & 1) + 0] = (__bf16)lo[0];
-          h[k >> 1][4 * (k & 1) + 1] = (__bf16)lo[1];
-          h[k >> 1][4 * (k & 1) + 2] = (__bf16)hi[0];
-          h[k >> 1][4 * (k & 1) + 3] = (__bf16)hi[1];
-        }
+      for (int i0 = 0; i0 < 8; i0 += kBatch) {
+        uint4 u[kBatch];
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int c = 16 * b + 2 * pc + e;       // bf16 chunk: values 8 c .. 8 c + 7
-          *reinterpret_cast<bf16x8*>(dst + ((c >> 3) << 10) + (((c & 7) ^ sw) << 4)) = h[e];
+        for (int i = 0; i < kBatch; ++i)         // 16 codes: latent values 128 b + 16 pc .. + 15
+          u[i] = *reinterpret_cast<const uint4*>(src + ((((i0 + i + b) & 7) ^ sz) << 4));
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+          const int pc = (i0 + i + b) & 7;
+          const unsigned w4[4] = {u[i].x, u[i].y, u[i].z, u[i].w};
+          bf16x8 h[2];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w4[k], 1.0f, false);   // codes 4k, 4k + 1
+            const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w4[k], 1.0f, true);    // codes 4k + 2, 4k + 3
+            h[k >> 1][4 * (k & 1) + 0] = lo[0];
+            h[k >> 1][4 * (k & 1) + 1] = lo[1];
+            h[k >> 1][4 * (k & 1) + 2] = hi[0];
+            h[k >> 1][4 * (k & 1) + 3] = hi[1];
+          }
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int c = 16 * b + 2 * pc + e;     // bf16 chunk: values 8 c .. 8 c + 7
+            *reinterpret_cast<bf16x8*>(dst + ((c >> 3) << 10) + (((c & 7) ^ sw) << 4)) = h[e];
+          }
         }
       }
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const int c = 2 * b + e;                 // RoPE chunk c -> bf16 chunk 64 + c
-        const uint4 u = *reinterpret_cast<const uint4*>(raw + ((rb * 5 + 4) << 10) + (tr << 7) +
-                                                        ((c ^ raw8_swz(t, 4)) << 4));
-        *reinterpret_cast<uint4*>(dst + (8 << 10) + ((c ^ sw) << 4)) = u;
+        const int c = 2 * b + e;
+        *reinterpret_cast<uint4*>(dst + (8 << 10) + ((c ^ sw) << 4)) = rope[e];
       }
     };
 
