@@ -63,6 +63,11 @@ __device__ __forceinline__ int swz(int t) { return (((t & 3) << 1) | ((t >> 2) &
 // lanes (4 rows x 4 segments) of each quarter wave hit 16 distinct 16-byte
 // bank groups.
 __device__ __forceinline__ int raw8_swz(int t, int sg) { return ((sg & 3) << 1) | ((t >> 1) & 1); }
+// The same for the rows16 variant, whose MFMA operands are read from the
+// copied tile itself: the rows of any 16-row group aligned to 16 that share
+// a parity get 8 distinct patterns, so that a quarter wave reading one chunk
+// of each of 16 rows hits 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int raw16_swz(int t) { return (t >> 1) & 7; }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -161,6 +166,28 @@ __device__ __forceinline__ void read_scalar2(const int32_t* p0, const int32_t* p
 // The same for eight consecutive ints (a plan row).
 typedef int int32x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+// Eight E4M3 codes (bytes of v, lowest first) as eight bf16 values (exact).
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(i32x2 v) {
+  bf16x8 r;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)v[k], 1.0f, false);
+    const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)v[k], 1.0f, true);
+    r[4 * k + 0] = lo[0];
+    r[4 * k + 1] = lo[1];
+    r[4 * k + 2] = hi[0];
+    r[4 * k + 3] = hi[1];
+  }
+  return r;
+}
+// Transposed read of 8-bit elements (ds_read_b64_tr_b8).  Within each group
+// of 16 lanes, lane i receives as byte b the byte at offset i mod 8 of the
+// 8 bytes addressed by lane 2 b + (i >= 8) of the group.
+__device__ __forceinline__ i32x2 read_tr8(const char* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(p));
+}
 __device__ __forceinline__ int32x8 read_scalar8(const int32_t* p) {
   int32x8 v;
   asm volatile("s_load_dwordx8 %0, %1, 0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
@@ -355,7 +382,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) char s0[C::kStageBytes];
   __shared__ __attribute__((aligned(1024))) char s1[C::kStageBytes];
   // FP8: the current tile expanded to bf16 (the layout of a bf16 stage)
-  __shared__ __attribute__((aligned(1024))) char tbuf[KV8 ? C::kTileB : 16];
+  __shared__ __attribute__((aligned(1024))) char tbuf[(KV8 && kWide) ? C::kTileB : 16];
   __shared__ __attribute__((aligned(16))) unsigned char kvalid[4][64];   // sparse key validity, tile t -> t & 3
   __shared__ float red_m[4][kRw];     // per-wave row maxima of the tile
   __shared__ float red_l[4][kRw];     // per-wave row sums at the end of a run
@@ -450,6 +477,28 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int b = 0; b < 2; ++b)
           v_x[e][b] = (((4 * b + 2 * (g & 1) + ((li & 3) >> 1)) ^ swz(tv + 8 * e)) << 4);
+    }
+
+    // Rows16 FP8: the MFMA operands come straight from the copied tile, the
+    // codes converted in registers.  K (QK^T): row t = 16 tg + li, values
+    // 32 ks + 8 g .. + 7 of latent segment ks / 4 (8 bytes), or for the RoPE
+    // k-steps 16, 17 the bf16 chunk 4 (ks - 16) + g of segment 4.  V^T (PV):
+    // for a transposed read this lane addresses row 32 c + 8 G + b, bytes
+    // 16 dt + 8 h .. + 7 of latent segment tg (G = lane / 16, b = (lane % 16)
+    // / 2, h = lane % 2), which hands lane i of each 16-lane group column
+    // 16 dt + i of the 8 rows 32 c + 8 G + 0..7.
+    int k8_base = 0, v8_base = 0, v8_sw = 0;
+    int k8_x[4] = {0, 0, 0, 0}, r8_x[2] = {0, 0};
+    if constexpr (!kWide && KV8) {
+      const int tk = 16 * tg + li, sw = raw16_swz(tk);
+      k8_base = ((tk >> 3) * 5 << 10) + ((tk & 7) << 7);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) k8_x[q] = (((2 * q + (g >> 1)) ^ sw) << 4) + 8 * (g & 1);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) r8_x[e] = (4 << 10) + (((4 * e + g) ^ sw) << 4);
+      const int G = lane >> 4, b = (lane & 15) >> 1, h = lane & 1;
+      v8_base = ((G * 5 + tg) << 10) + (b << 7) + 8 * h;
+      v8_sw = raw16_swz(8 * G + b);   // that of row 32 c + 8 G + b
     }
 
     // Tile rows this lane copies: t = 8 * (2 wave + r) + lane / 8 (the wave's 16 rows).
@@ -601,7 +650,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     // Copy instruction j (0 .. kLoads - 1) of this wave for a tile: 8 rows x 128 B.
     // FP8 stage layout: segment sg (0..3: latent bytes 128 sg .., 4: RoPE) of
     // row t at ((t / 8) * 5 + sg) * 1024 + (t % 8) * 128, its 16-byte chunks
-    // XOR-swizzled by raw8_swz; scale b of row t at kRaw8ScaleOff + 4 (64 b + t).
+    // XOR-swizzled by raw8_swz (wide) or raw16_swz (rows16); scale b of row t
+    // at kRaw8ScaleOff + 4 (64 b + t).
     auto issue_one = [&](char* stage, const int64_t (&off)[C::kOffs], int j) __attribute__((always_inline)) {
       if constexpr (!KV8) {
         const int ii = wave * C::kLoads + j;
@@ -611,7 +661,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
       } else if (j < 10) {
         const int r = j / 5, sg = j % 5;
         const char* src = kv_bytes + off[r] + (sg < 4 ? sg * 128 : 528) +
-                          (((lane & 7) ^ raw8_swz(cp_row[r], sg)) << 4);
+                          (((lane & 7) ^ (kWide ? raw8_swz(cp_row[r], sg) : raw16_swz(cp_row[r]))) << 4);
         copy_to_lds_16(src, lds_addr(stage + ((2 * wave + r) * 5 + sg) * 1024));
       } else if (lane < 16) {
         const int b = j - 10;
@@ -711,7 +761,9 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     auto clear_if_empty = [&](char* tile, const unsigned char* vslot) __attribute__((always_inline)) {
       if constexpr (sparse) {
         if (__builtin_amdgcn_ballot_w64(vslot[lane] != 0) == 0) {
-          for (int i = threadIdx.x; i < C::kTileB / 16; i += C::kThreads)
+          // the bf16 tile, or (rows16 FP8) the copied codes and RoPE values
+          constexpr int kClearB = (KV8 && !kWide) ? kRaw8ScaleOff : C::kTileB;
+          for (int i = threadIdx.x; i < kClearB / 16; i += C::kThreads)
             reinterpret_cast<uint4*>(tile)[i] = uint4{0, 0, 0, 0};
           if constexpr (KV8) reinterpret_cast<float*>(const_cast<float*>(sc_tab))[threadIdx.x] = 0.f;
           barrier_keep_loads();
@@ -786,9 +838,18 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
         // S^T (16 keys x 16 rows): all kQf K fragments first, one LDS latency for the chain.
         floatx4 sacc = floatx4{0.f, 0.f, 0.f, 0.f};
         bf16x8 kf[C::kQf];
+        if constexpr (KV8) {
 #pragma unroll
-        for (int ks = 0; ks < C::kQf; ++ks)
-          kf[ks] = *reinterpret_cast<const bf16x8*>(stage + k_base + ((ks >> 1) << 10) + k_x[ks & 1]);
+          for (int ks = 0; ks < 16; ++ks)
+            kf[ks] = fp8x8_to_bf16(*reinterpret_cast<const i32x2*>(stage + k8_base + ((ks >> 2) << 10) + k8_x[ks & 3]));
+#pragma unroll
+          for (int ks = 16; ks < 18; ++ks)
+            kf[ks] = *reinterpret_cast<const bf16x8*>(stage + k8_base + r8_x[ks - 16]);
+        } else {
+#pragma unroll
+          for (int ks = 0; ks < C::kQf; ++ks)
+            kf[ks] = *reinterpret_cast<const bf16x8*>(stage + k_base + ((ks >> 1) << 10) + k_x[ks & 1]);
+        }
         // element i: key 16 tg + 4 g + i
         const int t0 = 16 * tg + 4 * g;
         if constexpr (!KV8) {
@@ -915,7 +976,12 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
           bf16x4 pv;
 #pragma unroll
           for (int i = 0; i < 4; ++i) pv[i] = (__bf16)p[i];
-          *reinterpret_cast<bf16x4*>(pbuf + li * 128 + (tg >> 1) * 64 + g * 16 + (tg & 1) * 8) = pv;
+          // FP8 keeps the keys of a (c, g) slot group in natural order (key
+          // 32 c + 8 g + j in slot j), as its transposed V^T reads deliver them
+          if constexpr (KV8)
+            *reinterpret_cast<bf16x4*>(pbuf + li * 128 + (tg >> 1) * 64 + (2 * (tg & 1) + (g >> 1)) * 16 + (g & 1) * 8) = pv;
+          else
+            *reinterpret_cast<bf16x4*>(pbuf + li * 128 + (tg >> 1) * 64 + g * 16 + (tg & 1) * 8) = pv;
         } else {
 #pragma unroll
           for (int m = 0; m < 2; ++m) {
@@ -968,8 +1034,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
           // the wave's output columns are latent block tg: each key's scale for it
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
-            const floatx4 s0 = *reinterpret_cast<const floatx4*>(sc_tab + 64 * tg + 32 * c + 4 * g);
-            const floatx4 s1 = *reinterpret_cast<const floatx4*>(sc_tab + 64 * tg + 32 * c + 16 + 4 * g);
+            const floatx4 s0 = *reinterpret_cast<const floatx4*>(sc_tab + 64 * tg + 32 * c + 8 * g);
+            const floatx4 s1 = *reinterpret_cast<const floatx4*>(sc_tab + 64 * tg + 32 * c + 8 * g + 4);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               pb[c][i] = (__bf16)((float)pb[c][i] * s0[i]);
@@ -978,6 +1044,24 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
           }
         }
         constexpr int kPv = 6;
+        if constexpr (KV8) {
+          // V^T fragments (16 columns x 32 keys) by transposed 8-bit reads of
+          // the copied codes, converted in registers; keys in natural order
+          auto v8addr = [&](int n) __attribute__((always_inline)) -> const char* {
+            const int c = n >> 3, dt = n & 7;
+            return stage + v8_base + c * (20 << 10) + ((dt ^ v8_sw) << 4);
+          };
+          i32x2 vr[kPv];
+#pragma unroll
+          for (int n = 0; n < kPv; ++n) vr[n] = read_tr8(v8addr(n));
+#pragma unroll
+          for (int n = 0; n < 16; ++n) {
+            const bf16x8 va = fp8x8_to_bf16(vr[n % kPv]);
+            if (n + kPv < 16) vr[n % kPv] = read_tr8(v8addr(n + kPv));
+            oacc[n & 7] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[n >> 3], oacc[n & 7], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);   // keep the reads kPv MFMAs ahead
+          }
+        } else {
         auto vaddr = [&](int n, int e) __attribute__((always_inline)) -> const char* {
           const int c = n >> 3, dt = n & 7;
           return stage + v_base + (2 * c + e) * (2 * C::kCG * 1024) + ((dt >> 2) << 10) + v_x[0][dt & 3];
@@ -997,6 +1081,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
           }
           oacc[n & 7] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[n >> 3], oacc[n & 7], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);   // keep the reads kPv MFMAs ahead
+        }
         }
       } else {
         // O^T += V^T P^T over the 64 keys in k-steps of 16.  k-step j = 2 kb + m
@@ -1242,16 +1327,12 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
         __builtin_amdgcn_s_waitcnt(0);     // wave 0 with staged query rows: tile t, then the rows
       }
       barrier_keep_loads();                              // tile t is in LDS for every wave
-      if constexpr (KV8) {
-        expand_tile(cur, tbuf);
-        barrier_keep_loads();                            // the bf16 tile is complete
-        sc_tab = reinterpret_cast<const float*>(cur + kRaw8ScaleOff);
-      }
+      if constexpr (KV8) sc_tab = reinterpret_cast<const float*>(cur + kRaw8ScaleOff);   // operands read from the codes
       if (q_pending) q_from_lds(nxt);
       if (n2_item >= 0) tile_finish(n2_item, n2_blk, raw, off, kvalid[(t + 2) & 3]);
       const bool ends = !has_next || nx_item != cur_item;
-      clear_if_empty(KV8 ? tbuf : cur, kvalid[t & 3]);
-      compute(KV8 ? tbuf : cur, kvalid[t & 3], cur_blk, cur_lim, q_lds && has_next ? nxt : nullptr);
+      clear_if_empty(cur, kvalid[t & 3]);
+      compute(cur, kvalid[t & 3], cur_blk, cur_lim, q_lds && has_next ? nxt : nullptr);
       q_pending = false;
       if (ends) {
         finish(cur_item, cur_split);
