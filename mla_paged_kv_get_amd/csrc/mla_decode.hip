@@ -58,16 +58,11 @@ constexpr float kLazy = 8.f;   // log2 of the growth allowed before a rescale
 // the transposed reads.
 __device__ __forceinline__ int swz(int t) { return (((t & 3) << 1) | ((t >> 2) & 1)) ^ (((t >> 3) & 1) << 1); }
 
-// XOR pattern of the 16-byte chunks of segment sg of row t in a copied FP8
-// tile.  The expansion reads one segment per thread; with this pattern the 16
-// lanes (4 rows x 4 segments) of each quarter wave hit 16 distinct 16-byte
-// bank groups.
-__device__ __forceinline__ int raw8_swz(int t, int sg) { return ((sg & 3) << 1) | ((t >> 1) & 1); }
-// The same for the rows16 variant, whose MFMA operands are read from the
-// copied tile itself: the rows of any 16-row group aligned to 16 that share
-// a parity get 8 distinct patterns, so that a quarter wave reading one chunk
-// of each of 16 rows hits 16 distinct 16-byte bank groups.
-__device__ __forceinline__ int raw16_swz(int t) { return (t >> 1) & 7; }
+// XOR pattern of the 16-byte chunks of row t in a copied FP8 tile, whose
+// codes the MFMA operands are read from: the rows of any 16-row group aligned
+// to 16 that share a parity get 8 distinct patterns, so that a quarter wave
+// reading one chunk of each of 16 rows hits 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int raw_swz(int t) { return (t >> 1) & 7; }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -167,6 +162,7 @@ __device__ __forceinline__ void read_scalar2(const int32_t* p0, const int32_t* p
 typedef int int32x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // Eight E4M3 codes (bytes of v, lowest first) as eight bf16 values (exact).
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16(i32x2 v) {
@@ -382,7 +378,6 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) char s0[C::kStageBytes];
   __shared__ __attribute__((aligned(1024))) char s1[C::kStageBytes];
   // FP8: the current tile expanded to bf16 (the layout of a bf16 stage)
-  __shared__ __attribute__((aligned(1024))) char tbuf[(KV8 && kWide) ? C::kTileB : 16];
   __shared__ __attribute__((aligned(16))) unsigned char kvalid[4][64];   // sparse key validity, tile t -> t & 3
   __shared__ float red_m[4][kRw];     // per-wave row maxima of the tile
   __shared__ float red_l[4][kRw];     // per-wave row sums at the end of a run
@@ -390,10 +385,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
   // Probabilities of the tile in bf16.  Rows16: P^T [row][key pair block c][lane
   // group g][8], slot 4 h + i of (c, g) = key 16 (2 c + h) + 4 g + i.  Wide: the
   // B operands of the wave's two PV k-steps, [wave][k-step][lane][8].
-  // (Wide FP8: in the copied stage of the tile being computed, which is free
-  // once it has been expanded; there is no room for it elsewhere.)
-  __shared__ __attribute__((aligned(16))) char pbuf_s[(kWide && KV8) ? 16 : (kWide ? 4 * 2 * 64 * 16 : 16 * 128)];
-  char* pbuf = pbuf_s;
+  __shared__ __attribute__((aligned(16))) char pbuf[kWide ? 4 * 2 * 64 * 16 : 16 * 128];
   const float* sc_tab = nullptr;   // FP8: scale table [block][row] of the tile being computed
   // Wide: index data of the next tiles (sparse: the 64 index-list entries;
   // dense: the page id, in every entry), copied in by each wave ([tile & 3]
@@ -487,10 +479,28 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     // 16 dt + 8 h .. + 7 of latent segment tg (G = lane / 16, b = (lane % 16)
     // / 2, h = lane % 2), which hands lane i of each 16-lane group column
     // 16 dt + i of the 8 rows 32 c + 8 G + 0..7.
-    int k8_base = 0, v8_base = 0, v8_sw = 0;
-    int k8_x[4] = {0, 0, 0, 0}, r8_x[2] = {0, 0};
+    int k8_base = 0, v8_base = 0, v8_sw = 0, k8_sw = 0;
+    int k8_x[4] = {0, 0, 0, 0}, r8_x[2] = {0, 0}, v8_x[4] = {0, 0, 0, 0};
+    if constexpr (kWide && KV8) {
+      // Wide FP8: K row tk = 32 half + lrow, values 16 ks + 8 hl .. + 7 of
+      // latent segment ks / 8 (8 bytes of chunk ks % 8), or for the RoPE
+      // k-steps 32..35 the bf16 chunk 2 (ks - 32) + hl of segment 4.  V^T for
+      // PV k-step j and column block db: this lane addresses row
+      // 16 j + 8 (G / 2) + b, bytes 32 (db % 4) + 16 (G % 2) + 8 h .. + 7 of
+      // latent segment 2 half + db / 4, which hands lane i of each 16-lane
+      // group column 256 half + 32 db + 16 (G % 2) + i of the 8 rows
+      // 16 j + 8 (G / 2) + 0..7: the A operand of a 32x32x16 MFMA.
+      const int tk = 32 * half + lrow;
+      k8_sw = raw_swz(tk);
+      k8_base = ((tk >> 3) * 5 << 10) + ((tk & 7) << 7);
+      const int G = lane >> 4, b = (lane & 15) >> 1, h = lane & 1;
+      v8_base = ((((G >> 1) * 5) + 2 * half) << 10) + (b << 7) + 8 * h;
+      v8_sw = raw_swz(8 * (G >> 1) + b);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v8_x[q] = ((2 * q + (G & 1)) ^ v8_sw) << 4;   // PV chunk offsets by db % 4
+    }
     if constexpr (!kWide && KV8) {
-      const int tk = 16 * tg + li, sw = raw16_swz(tk);
+      const int tk = 16 * tg + li, sw = raw_swz(tk);
       k8_base = ((tk >> 3) * 5 << 10) + ((tk & 7) << 7);
 #pragma unroll
       for (int q = 0; q < 4; ++q) k8_x[q] = (((2 * q + (g >> 1)) ^ sw) << 4) + 8 * (g & 1);
@@ -498,7 +508,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
       for (int e = 0; e < 2; ++e) r8_x[e] = (4 << 10) + (((4 * e + g) ^ sw) << 4);
       const int G = lane >> 4, b = (lane & 15) >> 1, h = lane & 1;
       v8_base = ((G * 5 + tg) << 10) + (b << 7) + 8 * h;
-      v8_sw = raw16_swz(8 * G + b);   // that of row 32 c + 8 G + b
+      v8_sw = raw_swz(8 * G + b);   // that of row 32 c + 8 G + b
     }
 
     // Tile rows this lane copies: t = 8 * (2 wave + r) + lane / 8 (the wave's 16 rows).
@@ -650,8 +660,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     // Copy instruction j (0 .. kLoads - 1) of this wave for a tile: 8 rows x 128 B.
     // FP8 stage layout: segment sg (0..3: latent bytes 128 sg .., 4: RoPE) of
     // row t at ((t / 8) * 5 + sg) * 1024 + (t % 8) * 128, its 16-byte chunks
-    // XOR-swizzled by raw8_swz (wide) or raw16_swz (rows16); scale b of row t
-    // at kRaw8ScaleOff + 4 (64 b + t).
+    // XOR-swizzled by raw_swz; scale b of row t at kRaw8ScaleOff + 4 (64 b + t).
     auto issue_one = [&](char* stage, const int64_t (&off)[C::kOffs], int j) __attribute__((always_inline)) {
       if constexpr (!KV8) {
         const int ii = wave * C::kLoads + j;
@@ -661,7 +670,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
       } else if (j < 10) {
         const int r = j / 5, sg = j % 5;
         const char* src = kv_bytes + off[r] + (sg < 4 ? sg * 128 : 528) +
-                          (((lane & 7) ^ (kWide ? raw8_swz(cp_row[r], sg) : raw16_swz(cp_row[r]))) << 4);
+                          (((lane & 7) ^ raw_swz(cp_row[r])) << 4);
         copy_to_lds_16(src, lds_addr(stage + ((2 * wave + r) * 5 + sg) * 1024));
       } else if (lane < 16) {
         const int b = j - 10;
@@ -699,60 +708,6 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
 
     int64_t off[C::kOffs];   // cache byte offsets of the rows this lane copies for the next tile issued
 
-    // FP8: expand the copied tile `raw` into the bf16 tile layout in `tb`.
-    // Thread (row t, latent block b) writes the 128 codes of block b of row t
-    // as bf16 (exact: every E4M3 value is a bf16 value) and moves RoPE chunks
-    // 2b, 2b + 1 as they are.  The LDS reads go out kBatch at a time ahead of
-    // the conversions (rows16: all of them; the wide variant has fewer
-    // registers to spare).
-    auto expand_tile = [&](const char* raw, char* tb) __attribute__((always_inline)) {
-      constexpr int kBatch = kWide ? 2 : 8;
-      const int t = threadIdx.x >> 2, b = threadIdx.x & 3;
-      const int tr = t & 7, rb = t >> 3, sw = swz(t);
-      const char* src = raw + ((rb * 5 + b) << 10) + (tr << 7);
-      char* dst = tb + ((rb * C::kCG) << 10) + (tr << 7);
-      const int sz = raw8_swz(t, b);
-      uint4 rope[2];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int c = 2 * b + e;                 // RoPE chunk c -> bf16 chunk 64 + c
-        rope[e] = *reinterpret_cast<const uint4*>(raw + ((rb * 5 + 4) << 10) + (tr << 7) +
-                                                  ((c ^ raw8_swz(t, 4)) << 4));
-      }
-#pragma unroll
-      for (int i0 = 0; i0 < 8; i0 += kBatch) {
-        uint4 u[kBatch];
-#pragma unroll
-        for (int i = 0; i < kBatch; ++i)         // 16 codes: latent values 128 b + 16 pc .. + 15
-          u[i] = *reinterpret_cast<const uint4*>(src + ((((i0 + i + b) & 7) ^ sz) << 4));
-#pragma unroll
-        for (int i = 0; i < kBatch; ++i) {
-          const int pc = (i0 + i + b) & 7;
-          const unsigned w4[4] = {u[i].x, u[i].y, u[i].z, u[i].w};
-          bf16x8 h[2];
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w4[k], 1.0f, false);   // codes 4k, 4k + 1
-            const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w4[k], 1.0f, true);    // codes 4k + 2, 4k + 3
-            h[k >> 1][4 * (k & 1) + 0] = lo[0];
-            h[k >> 1][4 * (k & 1) + 1] = lo[1];
-            h[k >> 1][4 * (k & 1) + 2] = hi[0];
-            h[k >> 1][4 * (k & 1) + 3] = hi[1];
-          }
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int c = 16 * b + 2 * pc + e;     // bf16 chunk: values 8 c .. 8 c + 7
-            *reinterpret_cast<bf16x8*>(dst + ((c >> 3) << 10) + (((c & 7) ^ sw) << 4)) = h[e];
-          }
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int c = 2 * b + e;
-        *reinterpret_cast<uint4*>(dst + (8 << 10) + ((c ^ sw) << 4)) = rope[e];
-      }
-    };
-
     // Sparse: a tile without a single valid key adds nothing, but its rows
     // need not hold finite values (a sequence with no row at all in a cache
     // has its padding read the pool's first row), and 0 * NaN would reach O
@@ -761,8 +716,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     auto clear_if_empty = [&](char* tile, const unsigned char* vslot) __attribute__((always_inline)) {
       if constexpr (sparse) {
         if (__builtin_amdgcn_ballot_w64(vslot[lane] != 0) == 0) {
-          // the bf16 tile, or (rows16 FP8) the copied codes and RoPE values
-          constexpr int kClearB = (KV8 && !kWide) ? kRaw8ScaleOff : C::kTileB;
+          // the bf16 tile, or (FP8) the copied codes and RoPE values
+          constexpr int kClearB = KV8 ? kRaw8ScaleOff : C::kTileB;
           for (int i = threadIdx.x; i < kClearB / 16; i += C::kThreads)
             reinterpret_cast<uint4*>(tile)[i] = uint4{0, 0, 0, 0};
           if constexpr (KV8) reinterpret_cast<float*>(const_cast<float*>(sc_tab))[threadIdx.x] = 0.f;
@@ -892,16 +847,34 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
         floatx16 sblk[KV8 ? 4 : 1] = {};   // FP8: one accumulation per latent block
         auto qk = [&](auto with_dma) __attribute__((always_inline)) {
           constexpr int kPre = 6;
-          bf16x8 kf[kPre];
+          // K fragment of k-step ks: bf16 values, or (FP8) the 8 codes of a
+          // latent k-step (converted when used) / 8 bf16 RoPE values
+          auto kread = [&](int ks) __attribute__((always_inline)) -> i32x4 {
+            if constexpr (KV8) {
+              if (ks < 32) {   // the codes in the low half, converted in kuse
+                const i32x2 c8 = *reinterpret_cast<const i32x2*>(stage + k8_base + ((ks >> 3) << 10) +
+                                                                 (((ks & 7) ^ k8_sw) << 4) + 8 * hl);
+                return __builtin_shufflevector(c8, c8, 0, 1, -1, -1);
+              }
+              return *reinterpret_cast<const i32x4*>(stage + k8_base + (4 << 10) +
+                                                     (((2 * (ks - 32) + hl) ^ k8_sw) << 4));
+            } else {
+              return *reinterpret_cast<const i32x4*>(stage + k_base + ((ks >> 2) << 10) + k_x[ks & 3]);
+            }
+          };
+          auto kuse = [&](int ks, i32x4 v) __attribute__((always_inline)) -> bf16x8 {
+            if constexpr (KV8) {
+              if (ks < 32) return fp8x8_to_bf16(__builtin_shufflevector(v, v, 0, 1));
+            }
+            return __builtin_bit_cast(bf16x8, v);
+          };
+          i32x4 kf[kPre];
 #pragma unroll
-          for (int ks = 0; ks < kPre; ++ks)
-            kf[ks] = *reinterpret_cast<const bf16x8*>(stage + k_base + ((ks >> 2) << 10) + k_x[ks & 3]);
+          for (int ks = 0; ks < kPre; ++ks) kf[ks] = kread(ks);
 #pragma unroll
           for (int ks = 0; ks < C::kQf; ++ks) {
-            const bf16x8 kcur = kf[ks % kPre];
-            if (ks + kPre < C::kQf)
-              kf[ks % kPre] = *reinterpret_cast<const bf16x8*>(stage + k_base + (((ks + kPre) >> 2) << 10) +
-                                                               k_x[(ks + kPre) & 3]);
+            const bf16x8 kcur = kuse(ks, kf[ks % kPre]);
+            if (ks + kPre < C::kQf) kf[ks % kPre] = kread(ks + kPre);
             // FP8: each latent block (k-steps 8 b .. 8 b + 7) accumulates on
             // its own; the RoPE k-steps go into sacc
             if constexpr (KV8) {
@@ -982,6 +955,20 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
             *reinterpret_cast<bf16x4*>(pbuf + li * 128 + (tg >> 1) * 64 + (2 * (tg & 1) + (g >> 1)) * 16 + (g & 1) * 8) = pv;
           else
             *reinterpret_cast<bf16x4*>(pbuf + li * 128 + (tg >> 1) * 64 + g * 16 + (tg & 1) * 8) = pv;
+        } else if constexpr (KV8) {
+          // FP8: natural key order, as the transposed V^T reads deliver the
+          // keys: k-step 2 half + m, key 16 (2 half + m) + 8 q + 4 hl + i (score
+          // element 8 m + 4 q + i of this lane) goes to slot 4 hl + i of lane
+          // 32 q + lrow
+#pragma unroll
+          for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              bf16x4 v;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) v[i] = (__bf16)p[8 * m + 4 * q + i];
+              *reinterpret_cast<bf16x4*>(pbuf + ((wave * 2 + m) * 64 + 32 * q + lrow) * 16 + 8 * hl) = v;
+            }
         } else {
 #pragma unroll
           for (int m = 0; m < 2; ++m) {
@@ -1090,47 +1077,67 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
         // of the same lane in the wave with half == kb.
         bf16x8 pb[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          pb[j] = (j >> 1) == half ? pown[j & 1]
-                                   : *reinterpret_cast<const bf16x8*>(pbuf + (((wave ^ 1) * 2 + (j & 1)) * 64 + lane) * 16);
+        for (int j = 0; j < 4; ++j) {
+          const int owner = (j >> 1) == half ? wave : (wave ^ 1);
+          if constexpr (KV8)   // FP8: both halves through LDS, in natural key order
+            pb[j] = *reinterpret_cast<const bf16x8*>(pbuf + ((owner * 2 + (j & 1)) * 64 + lane) * 16);
+          else
+            pb[j] = (j >> 1) == half ? pown[j & 1]
+                                     : *reinterpret_cast<const bf16x8*>(pbuf + ((owner * 2 + (j & 1)) * 64 + lane) * 16);
+        }
         // 32 MFMAs, (j, db) in order; the V^T fragments are read kPv MFMAs ahead.
         constexpr int kPv = 6;
-        auto vaddr = [&](int n, int e) __attribute__((always_inline)) -> const char* {
-          const int j = n >> 3, db = n & 7;
-          return stage + v_base + (2 * j + e) * (C::kCG * 1024) + ((db >> 1) << 10) + v_x[e][db & 1];
-        };
-        bf16x4 vq0[kPv], vq1[kPv];
+        if constexpr (KV8) {
+          // V^T fragments by transposed 8-bit reads of the codes, converted in
+          // registers; P scaled by the keys' scales of the columns' latent
+          // block 2 half + db / 4
+          auto v8addr = [&](int n) __attribute__((always_inline)) -> const char* {
+            const int j = n >> 3, db = n & 7;
+            return stage + v8_base + ((10 * j + (db >> 2)) << 10) + v8_x[db & 3];
+          };
+          i32x2 vr[kPv];
 #pragma unroll
-        for (int n = 0; n < kPv; ++n) {
-          vq0[n] = read_tr(vaddr(n, 0));
-          vq1[n] = read_tr(vaddr(n, 1));
-        }
-        bf16x8 pbs;   // FP8: scaled probabilities of the current (k-step, block)
+          for (int n = 0; n < kPv; ++n) vr[n] = read_tr8(v8addr(n));
+          bf16x8 pbs;   // scaled probabilities of the current (k-step, block)
 #pragma unroll
-        for (int n = 0; n < 32; ++n) {
-          const bf16x8 va = __builtin_shufflevector(vq0[n % kPv], vq1[n % kPv], 0, 1, 2, 3, 4, 5, 6, 7);
-          if (n + kPv < 32) {
-            vq0[n % kPv] = read_tr(vaddr(n + kPv, 0));
-            vq1[n % kPv] = read_tr(vaddr(n + kPv, 1));
-          }
-          bf16x8 pbn = pb[n >> 3];
-          if constexpr (KV8) {
-            // columns of oacc[db] lie in latent block 2 half + db / 4: the
-            // probabilities of k-step j times the keys' scales for that block
+          for (int n = 0; n < 32; ++n) {
+            const bf16x8 va = fp8x8_to_bf16(vr[n % kPv]);
+            if (n + kPv < 32) vr[n % kPv] = read_tr8(v8addr(n + kPv));
             if ((n & 3) == 0) {
-              const float* st = sc_tab + 64 * (2 * half + ((n & 7) >> 2)) + 16 * (n >> 3) + 4 * hl;
+              const bf16x8 pbn = pb[n >> 3];
+              const float* st = sc_tab + 64 * (2 * half + ((n & 7) >> 2)) + 16 * (n >> 3) + 8 * hl;
               const floatx4 s0 = *reinterpret_cast<const floatx4*>(st);
-              const floatx4 s1 = *reinterpret_cast<const floatx4*>(st + 8);
+              const floatx4 s1 = *reinterpret_cast<const floatx4*>(st + 4);
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
                 pbs[i] = (__bf16)((float)pbn[i] * s0[i]);
                 pbs[4 + i] = (__bf16)((float)pbn[4 + i] * s1[i]);
               }
             }
-            pbn = pbs;
+            oacc[n & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pbs, oacc[n & 7], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);   // keep the reads kPv MFMAs ahead
           }
-          oacc[n & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pbn, oacc[n & 7], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);   // keep the reads kPv MFMAs ahead
+        } else {
+          auto vaddr = [&](int n, int e) __attribute__((always_inline)) -> const char* {
+            const int j = n >> 3, db = n & 7;
+            return stage + v_base + (2 * j + e) * (C::kCG * 1024) + ((db >> 1) << 10) + v_x[e][db & 1];
+          };
+          bf16x4 vq0[kPv], vq1[kPv];
+#pragma unroll
+          for (int n = 0; n < kPv; ++n) {
+            vq0[n] = read_tr(vaddr(n, 0));
+            vq1[n] = read_tr(vaddr(n, 1));
+          }
+#pragma unroll
+          for (int n = 0; n < 32; ++n) {
+            const bf16x8 va = __builtin_shufflevector(vq0[n % kPv], vq1[n % kPv], 0, 1, 2, 3, 4, 5, 6, 7);
+            if (n + kPv < 32) {
+              vq0[n % kPv] = read_tr(vaddr(n + kPv, 0));
+              vq1[n % kPv] = read_tr(vaddr(n + kPv, 1));
+            }
+            oacc[n & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[n >> 3], oacc[n & 7], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);   // keep the reads kPv MFMAs ahead
+          }
         }
       }
     };
@@ -1270,20 +1277,15 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
         // the index list of tile t + 1 before it): nothing else is in flight.
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         barrier_keep_loads();          // tile t in LDS for every wave; every wave is done with `nxt`
-        if constexpr (KV8) {
-          expand_tile(cur, tbuf);
-          barrier_keep_loads();        // the bf16 tile is complete
-          pbuf = cur;                  // the copied codes are free until tile t + 2 is copied in
-          sc_tab = reinterpret_cast<const float*>(cur + kRaw8ScaleOff);
-        }
+        if constexpr (KV8) sc_tab = reinterpret_cast<const float*>(cur + kRaw8ScaleOff);   // operands read from the codes
         if (has_next) {
           idx_from_lds(nx_item, nx_blk, t + 1, raw);
           tile_finish(nx_item, nx_blk, raw, off, kvalid[(t + 1) & 3]);
         }
         if (n2_item >= 0) idx_dma(n2_item, n2_blk, t + 2);
         const bool ends = !has_next || nx_item != cur_item;
-        clear_if_empty(KV8 ? tbuf : cur, kvalid[t & 3]);
-        compute(KV8 ? tbuf : cur, kvalid[t & 3], cur_blk, cur_lim, has_next ? nxt : nullptr);
+        clear_if_empty(cur, kvalid[t & 3]);
+        compute(cur, kvalid[t & 3], cur_blk, cur_lim, has_next ? nxt : nullptr);
         if (ends) {
           finish(cur_item, cur_split);
           if (has_next) {
