@@ -106,13 +106,13 @@ __device__ __forceinline__ bf16x4 read_tr(const char* p) {
 // In both, the waves sharing a row share its softmax reference, so no partial
 // outputs are merged when a run ends.
 // With packed FP8 rows (KV8) the tiles are copied as they are stored (41 KB
-// per 64 rows) into the two stages, and each step first expands its tile into
-// a third buffer in the bf16 tile layout above: the E4M3 codes themselves
-// (every one is a bf16 value) and the RoPE values.  The block scales stay
-// out of the bf16 operands, so no dequantized value is rounded: QK^T keeps
-// one accumulation per 128-value block and adds them up with the keys'
-// scales, and PV takes each key's scale (for the output columns' block) into
-// its probability.
+// per 64 rows) into the two stages, and the MFMA operands are read from the
+// codes: K fragments by 8-byte reads, V^T fragments by transposed 8-bit reads,
+// converted to bf16 in registers (exact: every E4M3 value is a bf16 value).
+// The block scales stay out of the bf16 operands, so no dequantized value is
+// rounded: QK^T keeps one accumulation per 128-value block and adds them up
+// with the keys' scales, and PV takes each key's scale (for the output
+// columns' block) into its probability.
 template <int V, bool KV8, int D>
 struct Cfg {
   static_assert(D == 576 || D == 512, "latent rows of 576 (512 + 64 RoPE) or 512 values");
@@ -377,7 +377,6 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
   static_assert(C::kLoads + kRaw < 64, "vmcnt holds 6 bits");
   __shared__ __attribute__((aligned(1024))) char s0[C::kStageBytes];
   __shared__ __attribute__((aligned(1024))) char s1[C::kStageBytes];
-  // FP8: the current tile expanded to bf16 (the layout of a bf16 stage)
   __shared__ __attribute__((aligned(16))) unsigned char kvalid[4][64];   // sparse key validity, tile t -> t & 3
   __shared__ float red_m[4][kRw];     // per-wave row maxima of the tile
   __shared__ float red_l[4][kRw];     // per-wave row sums at the end of a run
