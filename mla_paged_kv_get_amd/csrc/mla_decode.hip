@@ -57,6 +57,11 @@ constexpr float kLazy = 8.f;   // log2 of the growth allowed before a rescale
 // 16 distinct 16-byte bank groups, and so do the 4-row x 2-chunk patterns of
 // the transposed reads.
 __device__ __forceinline__ int swz(int t) { return (((t & 3) << 1) | ((t >> 2) & 1)) ^ (((t >> 3) & 1) << 1); }
+// The rows16 variant's pattern.  Its K reads need the 8 rows of either parity
+// in a 16-row group on 8 distinct patterns (as above); its V^T reads (8-byte
+// halves of chunk pairs 2 d, 2 d + 1 of 8 consecutive rows per half wave) need
+// the 4 rows of either parity in an 8-row group to differ in bits 1..2.
+__device__ __forceinline__ int swz16(int t) { return (((t >> 1) & 3) << 1) | ((t >> 3) & 1); }
 
 // XOR pattern of the 16-byte chunks of row t in a copied FP8 tile, whose
 // codes the MFMA operands are read from: the rows of any 16-row group aligned
@@ -384,7 +389,10 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
   // Probabilities of the tile in bf16.  Rows16: P^T [row][key pair block c][lane
   // group g][8], slot 4 h + i of (c, g) = key 16 (2 c + h) + 4 g + i.  Wide: the
   // B operands of the wave's two PV k-steps, [wave][k-step][lane][8].
-  __shared__ __attribute__((aligned(16))) char pbuf[kWide ? 4 * 2 * 64 * 16 : 16 * 128];
+  // rows16: bytes per row of the probability buffer (padded so that the 16
+  // rows of a quarter wave fall on distinct 16-byte bank groups)
+  constexpr int kPRow = 144;
+  __shared__ __attribute__((aligned(16))) char pbuf[kWide ? 4 * 2 * 64 * 16 : 16 * kPRow];
   const float* sc_tab = nullptr;   // FP8: scale table [block][row] of the tile being computed
   // Wide: index data of the next tiles (sparse: the 64 index-list entries;
   // dense: the page id, in every entry), copied in by each wave ([tile & 3]
@@ -427,6 +435,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
   const int row = row0 + (kWide ? 32 * pair : 0) + lrow;   // query row inside the item (S^T column)
   const bool row_ok = row < a.M;
   constexpr bool sparse = SPARSE;      // top-k index lists (a.topk > 0)
+  // chunk swizzle of a bf16 tile row (the variants read their tiles differently)
+  auto tswz = [](int t) __attribute__((always_inline)) { return kWide ? swz(t) : swz16(t); };
 
   const int32x8 prow = read_scalar8(a.plan + kPlanWords * (1 + w));
   const int it_first = prow[0], blk_first = prow[1], it_last = prow[2], blk_end = prow[3],
@@ -434,7 +444,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
 
   if (it_first >= 0) {
     // LDS read offsets of this lane.  Byte offset of chunk c of tile row t:
-    // ((t / 8) * kCG + c / 8) * 1024 + (t % 8) * 128 + ((c % 8) ^ swz(t)) * 16
+    // ((t / 8) * kCG + c / 8) * 1024 + (t % 8) * 128 + ((c % 8) ^ tswz(t)) * 16
     // (kCG = 9 chunk groups of 128 B for 576-value rows, 8 for 512).
     int k_base, v_base;
     int k_x[4];       // rows16: [0] even ks, [1] odd ks; wide: by ks & 3
@@ -443,14 +453,14 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
       //  K: key row t = 16 tg + li, chunk 4 ks + g.
       const int tk = 16 * tg + li;
       k_base = ((tk >> 3) * C::kCG << 10) + ((tk & 7) << 7);
-      k_x[0] = ((g ^ swz(tk)) << 4);
-      k_x[1] = (((4 + g) ^ swz(tk)) << 4);
+      k_x[0] = ((g ^ tswz(tk)) << 4);
+      k_x[1] = (((4 + g) ^ tswz(tk)) << 4);
       //  V^T: source row t = 16 s + 4 g + li / 4 of key subtile s, columns
       //  128 tg + 16 dt + 4 (li & 3) .. + 3: chunk 16 tg + 2 dt + (li & 3) / 2, half li & 1.
       const int tv = 4 * g + (li >> 2);
       v_base = ((tv >> 3) * C::kCG << 10) + ((tv & 7) << 7) + ((li & 1) << 3) + ((2 * tg) << 10);
 #pragma unroll
-      for (int d = 0; d < 4; ++d) v_x[0][d] = (((2 * d + ((li & 3) >> 1)) ^ swz(tv)) << 4);
+      for (int d = 0; d < 4; ++d) v_x[0][d] = (((2 * d + ((li & 3) >> 1)) ^ tswz(tv)) << 4);
     } else {
       //  K: key row t = 32 half + lrow, chunk 2 ks + hl.
       const int tk = 32 * half + lrow;
@@ -516,7 +526,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int r = 0; r < C::kLaneRows; ++r) {
       cp_row[r] = 8 * (2 * wave + r) + (lane >> 3);
-      cp_swz[r] = swz(cp_row[r]);
+      cp_swz[r] = tswz(cp_row[r]);
     }
     const char* kv_bytes = reinterpret_cast<const char*>(a.kv);
 
@@ -761,7 +771,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     auto q_from_lds = [&](const char* stage) __attribute__((always_inline)) {
       // row li, chunk 4 ks + g, in the tile layout
       const int qb = ((li >> 3) * C::kCG << 10) + ((li & 7) << 7);
-      const int qx0 = (g ^ swz(li)) << 4, qx1 = ((4 + g) ^ swz(li)) << 4;
+      const int qx0 = (g ^ tswz(li)) << 4, qx1 = ((4 + g) ^ tswz(li)) << 4;
 #pragma unroll
       for (int ks = 0; ks < C::kQf; ++ks)
         qf[ks] = *reinterpret_cast<const bf16x8*>(stage + qb + ((ks >> 1) << 10) + ((ks & 1) ? qx1 : qx0));
@@ -951,9 +961,9 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
           // FP8 keeps the keys of a (c, g) slot group in natural order (key
           // 32 c + 8 g + j in slot j), as its transposed V^T reads deliver them
           if constexpr (KV8)
-            *reinterpret_cast<bf16x4*>(pbuf + li * 128 + (tg >> 1) * 64 + (2 * (tg & 1) + (g >> 1)) * 16 + (g & 1) * 8) = pv;
+            *reinterpret_cast<bf16x4*>(pbuf + li * kPRow + (tg >> 1) * 64 + (2 * (tg & 1) + (g >> 1)) * 16 + (g & 1) * 8) = pv;
           else
-            *reinterpret_cast<bf16x4*>(pbuf + li * 128 + (tg >> 1) * 64 + g * 16 + (tg & 1) * 8) = pv;
+            *reinterpret_cast<bf16x4*>(pbuf + li * kPRow + (tg >> 1) * 64 + g * 16 + (tg & 1) * 8) = pv;
         } else if constexpr (KV8) {
           // FP8: natural key order, as the transposed V^T reads deliver the
           // keys: k-step 2 half + m, key 16 (2 half + m) + 8 q + 4 hl + i (score
@@ -1015,7 +1025,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
         // 16 MFMAs, (c, dt) in order; the V^T fragments are read kPv MFMAs ahead.
         bf16x8 pb[2];
 #pragma unroll
-        for (int c = 0; c < 2; ++c) pb[c] = *reinterpret_cast<const bf16x8*>(pbuf + li * 128 + c * 64 + g * 16);
+        for (int c = 0; c < 2; ++c) pb[c] = *reinterpret_cast<const bf16x8*>(pbuf + li * kPRow + c * 64 + g * 16);
         if constexpr (KV8) {
           // the wave's output columns are latent block tg: each key's scale for it
 #pragma unroll
