@@ -57,11 +57,11 @@ constexpr float kLazy = 8.f;   // log2 of the growth allowed before a rescale
 // 16 distinct 16-byte bank groups, and so do the 4-row x 2-chunk patterns of
 // the transposed reads.
 __device__ __forceinline__ int swz(int t) { return (((t & 3) << 1) | ((t >> 2) & 1)) ^ (((t >> 3) & 1) << 1); }
-// The rows16 variant's pattern.  Its K reads need the 8 rows of either parity
-// in a 16-row group on 8 distinct patterns (as above); its V^T reads (8-byte
-// halves of chunk pairs 2 d, 2 d + 1 of 8 consecutive rows per half wave) need
-// the 4 rows of either parity in an 8-row group to differ in bits 1..2.
-__device__ __forceinline__ int swz16(int t) { return (((t >> 1) & 3) << 1) | ((t >> 3) & 1); }
+// The rows16 variant's pattern, for its K reads (16 rows, one chunk each per
+// quarter wave) and V^T reads (8-byte halves of chunk pairs of 8 rows per
+// quarter wave).  Found by measuring SQ_LDS_BANK_CONFLICT for candidate
+// patterns on both access shapes: this one leaves both without conflicts.
+__device__ __forceinline__ int swz16(int t) { return t & 7; }
 
 // XOR pattern of the 16-byte chunks of row t in a copied FP8 tile, whose
 // codes the MFMA operands are read from: the rows of any 16-row group aligned
@@ -389,9 +389,10 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
   // Probabilities of the tile in bf16.  Rows16: P^T [row][key pair block c][lane
   // group g][8], slot 4 h + i of (c, g) = key 16 (2 c + h) + 4 g + i.  Wide: the
   // B operands of the wave's two PV k-steps, [wave][k-step][lane][8].
-  // rows16: bytes per row of the probability buffer (padded so that the 16
-  // rows of a quarter wave fall on distinct 16-byte bank groups)
-  constexpr int kPRow = 144;
+  // rows16: bytes per row of the probability buffer, padded by 8 so that its
+  // 16-byte reads and 8-byte writes hit no bank conflict (measured; 128 and
+  // 144 do)
+  constexpr int kPRow = 136;
   __shared__ __attribute__((aligned(16))) char pbuf[kWide ? 4 * 2 * 64 * 16 : 16 * kPRow];
   const float* sc_tab = nullptr;   // FP8: scale table [block][row] of the tile being computed
   // Wide: index data of the next tiles (sparse: the 64 index-list entries;
