@@ -482,13 +482,14 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     }
 
     // Rows16 FP8: the MFMA operands come straight from the copied tile, the
-    // codes converted in registers.  K (QK^T): row t = 16 tg + li, values
-    // 32 ks + 8 g .. + 7 of latent segment ks / 4 (8 bytes), or for the RoPE
-    // k-steps 16, 17 the bf16 chunk 4 (ks - 16) + g of segment 4.  V^T (PV):
-    // for a transposed read this lane addresses row 32 c + 8 G + b, bytes
-    // 16 dt + 8 h .. + 7 of latent segment tg (G = lane / 16, b = (lane % 16)
-    // / 2, h = lane % 2), which hands lane i of each 16-lane group column
-    // 16 dt + i of the 8 rows 32 c + 8 G + 0..7.
+    // codes converted in registers.  K (QK^T): row t = 16 tg + li; latent
+    // k-steps 2 p and 2 p + 1 take values 64 p + 16 g .. + 15 (one 16-byte
+    // chunk of segment p / 2; the query fragments follow the same order), the
+    // RoPE k-steps 16, 17 the bf16 chunk 4 (ks - 16) + g of segment 4.  V^T
+    // (PV): for a transposed read this lane addresses row 32 c + 8 G + b,
+    // bytes 16 dt + 8 h .. + 7 of latent segment tg (G = lane / 16,
+    // b = (lane % 16) / 2, h = lane % 2), which hands lane i of each 16-lane
+    // group column 16 dt + i of the 8 rows 32 c + 8 G + 0..7.
     int k8_base = 0, v8_base = 0, v8_sw = 0, k8_sw = 0;
     int k8_x[4] = {0, 0, 0, 0}, r8_x[2] = {0, 0}, v8_x[4] = {0, 0, 0, 0};
     if constexpr (kWide && KV8) {
@@ -513,7 +514,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
       const int tk = 16 * tg + li, sw = raw_swz(tk);
       k8_base = ((tk >> 3) * 5 << 10) + ((tk & 7) << 7);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) k8_x[q] = (((2 * q + (g >> 1)) ^ sw) << 4) + 8 * (g & 1);
+      for (int q = 0; q < 2; ++q) k8_x[q] = ((4 * q + g) ^ sw) << 4;
 #pragma unroll
       for (int e = 0; e < 2; ++e) r8_x[e] = (4 << 10) + (((4 * e + g) ^ sw) << 4);
       const int G = lane >> 4, b = (lane & 15) >> 1, h = lane & 1;
@@ -748,9 +749,14 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     auto load_q = [&](int item) __attribute__((always_inline)) {
       const uint16_t* qrow = a.q + q_row(a, item, row_ok ? row : 0) * D;
 #pragma unroll
-      for (int ks = 0; ks < C::kQf; ++ks)
-        qf[ks] = kWide ? *reinterpret_cast<const bf16x8*>(qrow + 16 * ks + 8 * hl)
-                       : *reinterpret_cast<const bf16x8*>(qrow + 32 * ks + 8 * g);
+      for (int ks = 0; ks < C::kQf; ++ks) {
+        // rows16 FP8: the latent k-steps take the values in the order its K
+        // reads deliver them (k-step 2 p + e, lane group g: values
+        // 64 p + 16 g + 8 e .. + 7), so that each lane reads 16 codes at once
+        const int d0 = kWide ? 16 * ks + 8 * hl
+                             : (KV8 && ks < 16 ? 64 * (ks >> 1) + 16 * g + 8 * (ks & 1) : 32 * ks + 8 * g);
+        qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + d0);
+      }
     };
     // Rows16, dense: the query rows of an item that starts mid-run come in
     // through LDS.  Wave 0 copies them into rows 0..15 of the stage the next
@@ -805,8 +811,11 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
         bf16x8 kf[C::kQf];
         if constexpr (KV8) {
 #pragma unroll
-          for (int ks = 0; ks < 16; ++ks)
-            kf[ks] = fp8x8_to_bf16(*reinterpret_cast<const i32x2*>(stage + k8_base + ((ks >> 2) << 10) + k8_x[ks & 3]));
+          for (int p = 0; p < 8; ++p) {   // 16 codes: values 64 p + 16 g .. + 15, k-steps 2 p and 2 p + 1
+            const i32x4 u = *reinterpret_cast<const i32x4*>(stage + k8_base + ((p >> 1) << 10) + k8_x[p & 1]);
+            kf[2 * p] = fp8x8_to_bf16(__builtin_shufflevector(u, u, 0, 1));
+            kf[2 * p + 1] = fp8x8_to_bf16(__builtin_shufflevector(u, u, 2, 3));
+          }
 #pragma unroll
           for (int ks = 16; ks < 18; ++ks)
             kf[ks] = *reinterpret_cast<const bf16x8*>(stage + k8_base + r8_x[ks - 16]);
