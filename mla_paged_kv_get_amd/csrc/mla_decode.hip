@@ -493,9 +493,10 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     int k8_base = 0, v8_base = 0, v8_sw = 0, k8_sw = 0;
     int k8_x[4] = {0, 0, 0, 0}, r8_x[2] = {0, 0}, v8_x[4] = {0, 0, 0, 0};
     if constexpr (kWide && KV8) {
-      // Wide FP8: K row tk = 32 half + lrow, values 16 ks + 8 hl .. + 7 of
-      // latent segment ks / 8 (8 bytes of chunk ks % 8), or for the RoPE
-      // k-steps 32..35 the bf16 chunk 2 (ks - 32) + hl of segment 4.  V^T for
+      // Wide FP8: K row tk = 32 half + lrow; latent k-steps 2 p and 2 p + 1
+      // take values 32 p + 16 hl .. + 15 (chunk 2 (p % 4) + hl of segment
+      // p / 4), the RoPE k-steps 32..35 the bf16 chunk 2 (ks - 32) + hl of
+      // segment 4.  V^T for
       // PV k-step j and column block db: this lane addresses row
       // 16 j + 8 (G / 2) + b, bytes 32 (db % 4) + 16 (G % 2) + 8 h .. + 7 of
       // latent segment 2 half + db / 4, which hands lane i of each 16-lane
@@ -750,10 +751,11 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
       const uint16_t* qrow = a.q + q_row(a, item, row_ok ? row : 0) * D;
 #pragma unroll
       for (int ks = 0; ks < C::kQf; ++ks) {
-        // rows16 FP8: the latent k-steps take the values in the order its K
-        // reads deliver them (k-step 2 p + e, lane group g: values
-        // 64 p + 16 g + 8 e .. + 7), so that each lane reads 16 codes at once
-        const int d0 = kWide ? 16 * ks + 8 * hl
+        // FP8: the latent k-steps take the values in the order the K reads
+        // deliver them (k-step 2 p + e: rows16, lane group g: values
+        // 64 p + 16 g + 8 e .. + 7; wide, lane half hl: 32 p + 16 hl + 8 e ..
+        // + 7), so that each lane reads 16 codes at once
+        const int d0 = kWide ? (KV8 && ks < 32 ? 32 * (ks >> 1) + 16 * hl + 8 * (ks & 1) : 16 * ks + 8 * hl)
                              : (KV8 && ks < 16 ? 64 * (ks >> 1) + 16 * g + 8 * (ks & 1) : 32 * ks + 8 * g);
         qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + d0);
       }
@@ -866,14 +868,16 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
         floatx16 sblk[KV8 ? 4 : 1] = {};   // FP8: one accumulation per latent block
         auto qk = [&](auto with_dma) __attribute__((always_inline)) {
           constexpr int kPre = 6;
-          // K fragment of k-step ks: bf16 values, or (FP8) the 8 codes of a
-          // latent k-step (converted when used) / 8 bf16 RoPE values
+          // K fragment of k-step ks: bf16 values; FP8: for an even latent
+          // k-step the 16 codes of k-steps ks and ks + 1 (values 16 ks + 16 hl
+          // .. + 15, one chunk; the query fragments follow the same order),
+          // nothing for an odd one, 8 bf16 values for a RoPE k-step
           auto kread = [&](int ks) __attribute__((always_inline)) -> i32x4 {
             if constexpr (KV8) {
-              if (ks < 32) {   // the codes in the low half, converted in kuse
-                const i32x2 c8 = *reinterpret_cast<const i32x2*>(stage + k8_base + ((ks >> 3) << 10) +
-                                                                 (((ks & 7) ^ k8_sw) << 4) + 8 * hl);
-                return __builtin_shufflevector(c8, c8, 0, 1, -1, -1);
+              if (ks < 32) {
+                if (ks & 1) return i32x4{};
+                return *reinterpret_cast<const i32x4*>(stage + k8_base + ((ks >> 3) << 10) +
+                                                       (((2 * ((ks >> 1) & 3) + hl) ^ k8_sw) << 4));
               }
               return *reinterpret_cast<const i32x4*>(stage + k8_base + (4 << 10) +
                                                      (((2 * (ks - 32) + hl) ^ k8_sw) << 4));
@@ -881,9 +885,14 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
               return *reinterpret_cast<const i32x4*>(stage + k_base + ((ks >> 2) << 10) + k_x[ks & 3]);
             }
           };
+          i32x2 khi = {0, 0};   // FP8: the upper 8 codes of the last even latent read
           auto kuse = [&](int ks, i32x4 v) __attribute__((always_inline)) -> bf16x8 {
             if constexpr (KV8) {
-              if (ks < 32) return fp8x8_to_bf16(__builtin_shufflevector(v, v, 0, 1));
+              if (ks < 32) {
+                if (ks & 1) return fp8x8_to_bf16(khi);
+                khi = __builtin_shufflevector(v, v, 2, 3);
+                return fp8x8_to_bf16(__builtin_shufflevector(v, v, 0, 1));
+              }
             }
             return __builtin_bit_cast(bf16x8, v);
           };
