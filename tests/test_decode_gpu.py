@@ -337,3 +337,50 @@ def test_phase_split_equals_one_call():
     torch.cuda.synchronize()
     assert torch.equal(o3.view(torch.int16), o1.view(torch.int16)) and torch.equal(l3, l1)
     compare(w, o3, l3, label="phases")
+
+
+def test_graph_capture_replays_match_eager():
+    """The whole step (plan, split decode, merge) captured in a HIP graph: every
+    replay, with eager work and synchronizations in between, gives the eager
+    result bit for bit (the path records no memset and allocates nothing inside
+    the library), and that result matches the oracle."""
+    m = _m()
+    w = wl.build("graph", 41, np.array([1500, 64, 1, 3000, 700]), B=5, s_q=1, h_q=16,
+                 num_pages=200, causal=False, poison=True)
+    d = Dev(w)
+    plan0, _ = m.get_mla_metadata(d.sl, 16, 1, num_workers=23)
+    W = int(plan0[0].item())
+    o = torch.empty((w.B, 1, 16, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.B, 1, 16), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(m.workspace_bytes(w.B, 1, 16, 1, 0, 512, W), 16), dtype=torch.uint8, device="cuda")
+
+    def step():
+        p, n = m.get_mla_metadata(d.sl, 16, 1, num_workers=23)
+        m.mla_decode_with_kvcache(d.q, d.kv, d.bt, d.sl, 512, p, n, out=(o, lse), workspace=ws, phases=1)
+        m.mla_decode_with_kvcache(d.q, d.kv, d.bt, d.sl, 512, p, n, out=(o, lse), workspace=ws, phases=2)
+
+    step()
+    torch.cuda.synchronize()
+    o_ref, l_ref = o.clone(), lse.clone()
+    compare(w, o_ref, l_ref, label="graph eager")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()                                   # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        o.fill_(0)
+        lse.fill_(0)
+        if rep == 2:
+            step()                               # eager work between replays
+        torch.cuda.synchronize()
+        o.fill_(0)
+        lse.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16)), f"replay {rep}: O differs"
+        assert torch.equal(lse, l_ref), f"replay {rep}: LSE differs"
