@@ -234,6 +234,9 @@ int decode_impl(const void* q, const void* kvcache, int64_t num_pages, int page_
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.h_kv = h_kv;
   a.G = h_q / h_kv;
+  a.seq_div = (unsigned)(topk > 0 ? h_kv * s_q : h_kv);
+  a.seq_mul = 0xffffffffu / a.seq_div;
+  a.head_mul = 0xffffffffu / (unsigned)h_kv;
   a.kv_format = kv_format;
   a.d_qk = d_qk;
   a.nb1 = topk > 0 ? (topk + kPage - 1) / kPage : 0;

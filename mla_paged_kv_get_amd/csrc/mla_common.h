@@ -89,21 +89,33 @@ struct DecodeArgs {
   // launch.
   int fused;
   int* arrivals;
+  // Division of an item index by the items per sequence (topk > 0: h_kv s_q,
+  // else h_kv) and by h_kv, by multiplication: mul = floor((2^32 - 1) / div)
+  // (set on the host; see div_by).
+  unsigned seq_div, seq_mul, head_mul;
 };
+
+// floor(n / d) for 0 <= n < 2^31 from m = floor((2^32 - 1) / d): the high
+// word of n m is floor(n / d) or one less (its error is below 2 n / 2^32 < 1),
+// and one comparison settles which.
+__device__ __forceinline__ int div_by(int n, unsigned d, unsigned m) {
+  unsigned q = __umulhi((unsigned)n, m);
+  if ((unsigned)n - q * d >= d) ++q;
+  return (int)q;
+}
 
 // Row of q / o / lse ([batch * s_q * h_q] rows) holding query row `row` of
 // work item `item`.  Dense: item = b * h_kv + g, row = s * G + j -> token
 // (b, s), head g * G + j.  Sparse: item = (b * s_q + s) * h_kv + g, row = j.
 __device__ __forceinline__ int64_t q_row(const DecodeArgs& a, int item, int row) {
-  const int tok_or_b = item / a.h_kv, g = item - tok_or_b * a.h_kv;
+  const int tok_or_b = div_by(item, (unsigned)a.h_kv, a.head_mul), g = item - tok_or_b * a.h_kv;
   if (a.topk > 0) return (int64_t)tok_or_b * (a.h_kv * a.G) + g * a.G + row;
   const int s = row / a.G, j = row - s * a.G;
   return ((int64_t)tok_or_b * a.s_q + s) * (a.h_kv * a.G) + g * a.G + j;
 }
 // Sequence (block-table row, length) of work item `item`.
 __device__ __forceinline__ int item_seq(const DecodeArgs& a, int item) {
-  const int d = a.topk > 0 ? a.h_kv * a.s_q : a.h_kv;
-  return d == 1 ? item : item / d;      // one KV head, one token: no division
+  return div_by(item, a.seq_div, a.seq_mul);
 }
 
 // Launchers (defined next to their kernels).

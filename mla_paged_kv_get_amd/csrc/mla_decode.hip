@@ -396,10 +396,15 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char pbuf[kWide ? 4 * 2 * 64 * 16 : 16 * kPRow];
   const float* sc_tab = nullptr;   // FP8: scale table [block][row] of the tile being computed
   // Wide: index data of the next tiles (sparse: the 64 index-list entries;
-  // dense: the page id, in every entry), copied in by each wave ([tile & 3]
-  // [wave][64]) so that neither a register load left behind a tile copy nor a
-  // scalar round trip sits on the critical path of a step.
-  __shared__ __attribute__((aligned(256))) int idxbuf[kWide ? 4 : 1][4][64];
+  // dense: the page id, in every entry), copied in by wave 0 ([tile & 3][64])
+  // a step ahead, so that neither a register load left behind a tile copy nor
+  // a scalar round trip sits on the critical path of a step (the step's wait
+  // and barrier make it visible to every wave).
+  __shared__ __attribute__((aligned(256))) int idxbuf[kWide ? 4 : 1][64];
+  // Wide, sparse: the block-table entries (pages) of the rows of a tile,
+  // loaded one step ahead ([tile & 1][wave][lane]: lane l of wave w holds the
+  // page of row 16 w + l % 16).
+  __shared__ __attribute__((aligned(256))) int pgbuf[(kWide && SPARSE) ? 2 : 1][4][64];
 
   // The arguments on the way to the first tile copy, loaded in one go (left
   // to itself, the compiler loads each one where it is first used, a round
@@ -565,7 +570,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
       bool aux;
     };
     auto sparse_list = [&](int item, int blk) __attribute__((always_inline)) -> SparseList {
-      const int64_t tok = item / a.h_kv;
+      const int64_t tok = div_by(item, (unsigned)a.h_kv, a.head_mul);
       if (blk < a.nb1) return {a.indices + tok * a.topk, a.topk, blk * kPage, false};
       return {a.indices2 + tok * a.topk2, a.topk2, (blk - a.nb1) * kPage, true};
     };
@@ -625,11 +630,53 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
         }
       }
     };
+    // Sparse: the rows of a tile in two steps.  translate reads the block
+    // table (page of each index-list entry this lane copies; padding reads the
+    // sequence's first row, page 0 of the pool if it has none) and records the
+    // tile's key validity; finish_pre turns the pages into byte offsets
+    // (auxiliary-cache rows taken from the main cache's base).  The wide
+    // variant translates a tile one step before it issues its copy, so the
+    // block-table loads are complete by then.
+    struct TilePre {
+      int page[C::kOffs];
+      int slot[C::kOffs];
+      bool aux;
+    };
+    auto translate = [&](int item, int blk, const TileRaw& raw, TilePre& pre,
+                         unsigned char* vslot) __attribute__((always_inline)) {
+      const bool aux = blk >= a.nb1;
+      const int b = item_seq(a, item);
+      const int32_t* bt_row = aux ? a.block_table2 + (int64_t)b * a.max_blocks2
+                                  : a.block_table + (int64_t)b * a.max_blocks;
+      const int Ls = aux ? read_scalar(a.seqlens2 + b) : item_len(item);
+      pre.aux = aux;
+#pragma unroll
+      for (int r = 0; r < C::kOffs; ++r) {
+        const int idx = raw.v[r];
+        const bool ok = sparse_key_valid(idx, Ls);
+        const int pos = ok ? idx : 0;
+        // the load is unconditional (entry 0 is always inside the table) and
+        // its value is not touched here, so nothing waits for it before the
+        // next step; slot -1 marks "the pool's first row"
+        pre.page[r] = bt_row[pos >> 6];
+        pre.slot[r] = (ok || Ls > 0) ? (pos & (kPage - 1)) : -1;
+        if (r < C::kLaneRows && (lane & 7) == 0) vslot[cp_row[r]] = ok ? 1 : 0;
+      }
+    };
+    auto finish_pre = [&](int item, const TilePre& pre, int64_t (&off)[C::kOffs]) __attribute__((always_inline)) {
+      const int kvh = item - div_by(item, (unsigned)a.h_kv, a.head_mul) * a.h_kv;
+      const int64_t base = pre.aux ? (int64_t)(reinterpret_cast<const char*>(a.kv2) - kv_bytes) : 0;
+#pragma unroll
+      for (int r = 0; r < C::kOffs; ++r) {
+        const int64_t crow = pre.slot[r] < 0 ? 0 : (int64_t)pre.page[r] * kPage + pre.slot[r];
+        off[r] = base + (crow * a.h_kv + kvh) * (int64_t)C::kRowB;
+      }
+    };
     auto tile_finish = [&](int item, int blk, const TileRaw& raw, int64_t (&off)[C::kOffs],
                            unsigned char* vslot) __attribute__((always_inline)) {
-      const int L = item_len(item);
-      const int kvh = a.h_kv == 1 ? 0 : item % a.h_kv;      // latent KV head of the item
       if constexpr (!sparse) {
+        const int L = item_len(item);
+        const int kvh = item - div_by(item, (unsigned)a.h_kv, a.head_mul) * a.h_kv;   // latent KV head of the item
         // byte offset of the tile's page and head (wave-uniform), plus each
         // copied row's offset inside the page (precomputed for full tiles)
         const int64_t base = (int64_t)__builtin_amdgcn_readfirstlane(raw.v[0]) * page_bytes +
@@ -645,28 +692,9 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
           if constexpr (KV8) off[2] = base + (int64_t)min(sc_row, nvalid - 1) * a.h_kv * C::kRowB;
         }
       } else {
-        // auxiliary-cache tiles: its block table, lengths and rows (offsets
-        // taken from the main cache's base)
-        const bool aux = blk >= a.nb1;
-        const int b = item_seq(a, item);
-        const int32_t* bt_row = aux ? a.block_table2 + (int64_t)b * a.max_blocks2
-                                    : a.block_table + (int64_t)b * a.max_blocks;
-        const int Ls = aux ? read_scalar(a.seqlens2 + b) : L;
-        const int64_t base = aux ? (int64_t)(reinterpret_cast<const char*>(a.kv2) - kv_bytes) : 0;
-#pragma unroll
-        for (int r = 0; r < C::kLaneRows; ++r) {
-          const int idx = raw.v[r];
-          const bool ok = sparse_key_valid(idx, Ls);
-          // padding reads the sequence's first row (page 0 of the pool if it has none)
-          const int64_t crow = ok ? cache_row(bt_row, idx) : (Ls > 0 ? cache_row(bt_row, 0) : 0);
-          off[r] = base + (crow * a.h_kv + kvh) * (int64_t)C::kRowB;
-          if ((lane & 7) == 0) vslot[cp_row[r]] = ok ? 1 : 0;
-        }
-        if constexpr (KV8) {
-          const int idx = raw.v[2];
-          const int64_t crow = sparse_key_valid(idx, Ls) ? cache_row(bt_row, idx) : (Ls > 0 ? cache_row(bt_row, 0) : 0);
-          off[2] = base + (crow * a.h_kv + kvh) * (int64_t)C::kRowB;
-        }
+        TilePre pre;
+        translate(item, blk, raw, pre, vslot);
+        finish_pre(item, pre, off);
       }
     };
     // Copy instruction j (0 .. kLoads - 1) of this wave for a tile: 8 rows x 128 B.
@@ -704,17 +732,66 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
       } else {
         src = a.block_table + (int64_t)item_seq(a, item) * a.max_blocks + blk;
       }
-      copy_to_lds_4(src, lds_addr(&idxbuf[slot & 3][wave][0]));
+      if (wave == 0) copy_to_lds_4(src, lds_addr(&idxbuf[slot & 3][0]));
     };
     auto idx_from_lds = [&](int item, int blk, int slot, TileRaw& raw) __attribute__((always_inline)) {
       if constexpr (sparse) {
         const SparseList sl = sparse_list(item, blk);
 #pragma unroll
         for (int r = 0; r < C::kLaneRows; ++r)
-          raw.v[r] = sl.e0 + cp_row[r] < sl.n ? idxbuf[slot & 3][wave][cp_row[r]] : -1;
-        if constexpr (KV8) raw.v[2] = sl.e0 + sc_row < sl.n ? idxbuf[slot & 3][wave][sc_row] : -1;
+          raw.v[r] = sl.e0 + cp_row[r] < sl.n ? idxbuf[slot & 3][cp_row[r]] : -1;
+        if constexpr (KV8) raw.v[2] = sl.e0 + sc_row < sl.n ? idxbuf[slot & 3][sc_row] : -1;
       } else {
-        raw.v[0] = idxbuf[slot & 3][wave][0];
+        raw.v[0] = idxbuf[slot & 3][0];
+      }
+    };
+
+    // Wide, sparse: the translation of a tile's index entries into rows,
+    // split over two steps without registers carried between them (a load
+    // result carried across the loop would have the compiler wait for every
+    // copy in flight).  translate_lds copies the page of each row's entry
+    // (row 16 wave + lane % 16; padding takes entry 0 of the block table) into
+    // pgbuf and records the rows' validity; finish_lds, a step later, turns
+    // the entries and pages into byte offsets.
+    auto sparse_rows = [&](int item, int blk, const int32_t*& bt_row, int& Ls, int64_t& base) __attribute__((always_inline)) {
+      const bool aux = blk >= a.nb1;
+      const int b = item_seq(a, item);
+      bt_row = aux ? a.block_table2 + (int64_t)b * a.max_blocks2 : a.block_table + (int64_t)b * a.max_blocks;
+      Ls = aux ? read_scalar(a.seqlens2 + b) : item_len(item);
+      base = aux ? (int64_t)(reinterpret_cast<const char*>(a.kv2) - kv_bytes) : 0;
+    };
+    auto translate_lds = [&](int item, int blk, int slot, unsigned char* vslot) __attribute__((always_inline)) {
+      if constexpr (kWide && sparse) {
+        const SparseList sl = sparse_list(item, blk);
+        const int32_t* bt_row;
+        int Ls;
+        int64_t base;
+        sparse_rows(item, blk, bt_row, Ls, base);
+        const int rr = 16 * wave + (lane & 15);
+        const int idx = sl.e0 + rr < sl.n ? idxbuf[slot & 3][rr] : -1;
+        const bool ok = sparse_key_valid(idx, Ls);
+        copy_to_lds_4(bt_row + ((ok ? idx : 0) >> 6), lds_addr(&pgbuf[slot & 1][wave][0]));
+        if (lane < 16) vslot[rr] = ok ? 1 : 0;
+      }
+    };
+    auto finish_lds = [&](int item, int blk, int slot, int64_t (&off)[C::kOffs]) __attribute__((always_inline)) {
+      if constexpr (kWide && sparse) {
+        const SparseList sl = sparse_list(item, blk);
+        const int32_t* bt_row;
+        int Ls;
+        int64_t base;
+        sparse_rows(item, blk, bt_row, Ls, base);
+        const int kvh = item - div_by(item, (unsigned)a.h_kv, a.head_mul) * a.h_kv;
+#pragma unroll
+        for (int r = 0; r < C::kOffs; ++r) {
+          const int row = r < C::kLaneRows ? cp_row[r] : sc_row;
+          const int idx = sl.e0 + row < sl.n ? idxbuf[slot & 3][row] : -1;
+          const bool ok = sparse_key_valid(idx, Ls);
+          const int page = pgbuf[slot & 1][row >> 4][row & 15];
+          // padding reads the sequence's first row (the pool's first if it has none)
+          const int64_t crow = (ok || Ls > 0) ? (int64_t)page * kPage + ((ok ? idx : 0) & (kPage - 1)) : 0;
+          off[r] = base + (crow * a.h_kv + kvh) * (int64_t)C::kRowB;
+        }
       }
     };
 
@@ -803,7 +880,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     // `off`) is issued interleaved with the QK^T MFMAs, one instruction every
     // second k-step, so that issuing it never holds the wave up.
     auto compute = [&](const char* stage, const unsigned char* vslot, int blk, int lim,
-                       char* dma_stage) __attribute__((always_inline)) {
+                       char* dma_stage, auto&& mid) __attribute__((always_inline)) {
       constexpr int kX = kWide ? 16 : 4;     // scores per lane
       float x[kX];                           // raw scores of the lane's keys, -inf where masked
       float mx;                              // raw row max over this wave's keys
@@ -916,6 +993,9 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
               static_assert(2 * C::kLoads <= C::kQf, "the copies must fit the k-steps");
               if (ks % 2 == 0 && ks / 2 < C::kLoads) issue_one(dma_stage, off, ks / 2);
             }
+            // work for later tiles placed between MFMAs of the chain, where
+            // the wave has issue slots to spare
+            if (ks == 8) mid();
             __builtin_amdgcn_sched_barrier(0);   // keep the reads kPre MFMAs ahead
           }
         };
@@ -1279,10 +1359,23 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     advance(cur_item, cur_blk, cur_hi, nx_item, nx_blk, nx_hi);
     int cur_lim = key_limit(cur_item);
     int cur_split = split_first;
+    // Wide, sparse: tile 1's index entries come in with tile 0's, and tile 1
+    // is translated here (its pages are copied in before the first copy)
+    if constexpr (kWide && sparse) {
+      if (nx_item >= 0) idx_dma(nx_item, nx_blk, 1);
+    }
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    if constexpr (kWide && sparse) {
+      barrier_keep_loads();                 // tile 1's entries, copied by wave 0, for every wave
+      if (nx_item >= 0) translate_lds(nx_item, nx_blk, 1, kvalid[1]);
+    }
     tile_finish(cur_item, cur_blk, raw, off, kvalid[0]);
     issue(s0, off);
-    if constexpr (kWide) {
+    if constexpr (kWide && sparse) {
+      int p_item = -1, p_blk = 0, p_hi = 0;   // tile 2: its index entries into the ring
+      if (nx_item >= 0) advance(nx_item, nx_blk, nx_hi, p_item, p_blk, p_hi);
+      if (p_item >= 0) idx_dma(p_item, p_blk, 2);
+    } else if constexpr (kWide) {
       if (nx_item >= 0) idx_dma(nx_item, nx_blk, 1);   // tile 1's offsets are made in step 0
     } else if (nx_item >= 0) {
       tile_fetch(nx_item, nx_blk, raw);
@@ -1301,19 +1394,37 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
       int n2_item = -1, n2_blk = 0, n2_hi = 0;
       if (has_next) advance(nx_item, nx_blk, nx_hi, n2_item, n2_blk, n2_hi);
       if constexpr (kWide) {
-        // Tile t was requested during the previous step's QK^T (and, sparse,
-        // the index list of tile t + 1 before it): nothing else is in flight.
+        // Tile t was requested during the previous step's QK^T (and before it
+        // the index data of a later tile; sparse: the block-table entries of
+        // tile t + 1): nothing else is in flight.
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         barrier_keep_loads();          // tile t in LDS for every wave; every wave is done with `nxt`
         if constexpr (KV8) sc_tab = reinterpret_cast<const float*>(cur + kRaw8ScaleOff);   // operands read from the codes
-        if (has_next) {
+        // Tile t + 1's offsets (its copy goes out during QK^T).  Sparse: from
+        // its entries and pages, copied in during the last step.
+        if constexpr (sparse) {
+          if (has_next) finish_lds(nx_item, nx_blk, t + 1, off);
+        } else if (has_next) {
           idx_from_lds(nx_item, nx_blk, t + 1, raw);
           tile_finish(nx_item, nx_blk, raw, off, kvalid[(t + 1) & 3]);
         }
-        if (n2_item >= 0) idx_dma(n2_item, n2_blk, t + 2);
+        // Work for later tiles, done between QK^T MFMAs: sparse, tile t + 2's
+        // pages and validity and tile t + 3's index entries; dense, tile
+        // t + 2's page id.
+        auto mid = [&]() __attribute__((always_inline)) {
+          if (n2_item < 0) return;
+          if constexpr (sparse) {
+            translate_lds(n2_item, n2_blk, t + 2, kvalid[(t + 2) & 3]);
+            int n3_item = -1, n3_blk = 0, n3_hi = 0;
+            advance(n2_item, n2_blk, n2_hi, n3_item, n3_blk, n3_hi);
+            if (n3_item >= 0) idx_dma(n3_item, n3_blk, t + 3);
+          } else {
+            idx_dma(n2_item, n2_blk, t + 2);
+          }
+        };
         const bool ends = !has_next || nx_item != cur_item;
         clear_if_empty(cur, kvalid[t & 3]);
-        compute(cur, kvalid[t & 3], cur_blk, cur_lim, has_next ? nxt : nullptr);
+        compute(cur, kvalid[t & 3], cur_blk, cur_lim, has_next ? nxt : nullptr, mid);
         if (ends) {
           finish(cur_item, cur_split);
           if (has_next) {
@@ -1362,7 +1473,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
       if (n2_item >= 0) tile_finish(n2_item, n2_blk, raw, off, kvalid[(t + 2) & 3]);
       const bool ends = !has_next || nx_item != cur_item;
       clear_if_empty(cur, kvalid[t & 3]);
-      compute(cur, kvalid[t & 3], cur_blk, cur_lim, q_lds && has_next ? nxt : nullptr);
+      compute(cur, kvalid[t & 3], cur_blk, cur_lim, q_lds && has_next ? nxt : nullptr, [] {});
       q_pending = false;
       if (ends) {
         finish(cur_item, cur_split);
