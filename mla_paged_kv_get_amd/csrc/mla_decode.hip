@@ -539,12 +539,15 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     const char* kv_bytes = reinterpret_cast<const char*>(a.kv);
 
     // Sequence length of each of this worker's items, lane j holding item
-    // it_first + j (read in the prologue, before any copy is in flight).
-    int lens_v = 0;
+    // it_first + j, and the split-slot prefix at item it_first + j (read in
+    // the prologue, before any copy is in flight: the end of an item then
+    // waits for no load).
+    int lens_v = 0, splits_v = 0;
     if (lane <= it_last - it_first) {
       const int x = it_first + lane;
       lens_v = a.seqlens[item_seq(a, x)];
     }
+    if (lane <= it_last - it_first + 1) splits_v = a.num_splits[it_first + lane];
     // The first item's length and the page of the first tile (dense) come in
     // by scalar loads in the prologue, so that the first copy does not wait
     // for the vector loads (the other lengths, the query rows).
@@ -1255,8 +1258,14 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     int merge_item[2] = {-1, -1};   // single launch: split items whose partials this workgroup merges
     int n_merge = 0;
     auto finish = [&](int item, int split) __attribute__((always_inline)) {
-      const int slot0 = read_scalar(a.num_splits + item);
-      const int nsplit = read_scalar(a.num_splits + item + 1) - slot0;
+      int slot0, slot1;
+      if (item - it_first < 63) {
+        slot0 = __builtin_amdgcn_readlane(splits_v, item - it_first);
+        slot1 = __builtin_amdgcn_readlane(splits_v, item - it_first + 1);
+      } else {
+        read_scalar2(a.num_splits + item, a.num_splits + item + 1, slot0, slot1);
+      }
+      const int nsplit = slot1 - slot0;
       const bool final_out = nsplit == 1;
       const int64_t part_base = (int64_t)(slot0 + split) * a.M;
       // row sums over the lanes and waves holding the row (same order everywhere)

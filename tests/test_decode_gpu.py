@@ -261,6 +261,23 @@ def test_split_count_invariance_wide_rows():
         compare(w, o, lse, label=f"h128 W={W}")
 
 
+@pytest.mark.parametrize("h_q,topk", [(16, None), (128, None), (16, 32)])
+def test_many_items_per_worker(h_q, topk):
+    # Over 64 items per worker: the lengths and split slots of items past the
+    # first 64 are read one by one instead of from the per-lane tables.
+    rng = np.random.default_rng(77)
+    L = rng.integers(0, 130, size=150)           # empty, one-page and two-page sequences
+    if topk is not None:
+        L = np.maximum(L, topk)
+    w = wl.build("many-items", 77, L, B=len(L), s_q=1, h_q=h_q, num_pages=400, poison=True,
+                 topk=topk, rng=rng)
+    for W in (1, 2):
+        o, lse, plan = run_gpu(Dev(w), num_workers=W)
+        rows = plan[0].cpu().numpy()[8:8 * (W + 1)].reshape(W, 8)   # one row of 8 words per worker
+        assert (rows[:, 2] - rows[:, 0]).max() >= 64
+        compare(w, o, lse, label=f"h_q={h_q} topk={topk} W={W}")
+
+
 def test_page_permutation_bit_exact():
     w = wl.memory_bound()
     d = Dev(w)
