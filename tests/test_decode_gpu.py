@@ -51,6 +51,26 @@ def test_plan_bit_exact(W):
         assert (ns.cpu().numpy() == ref_ns).all()
 
 
+@pytest.mark.parametrize("lengths,W", [
+    ([512000] * 140, 4096),     # W' T >= 2^32, items marking their workers
+    ([64000] * 66, 70000),      # W' T >= 2^32, workers searching the item starts
+    ([6400] * 64, 5000),        # W' T < 2^32, workers searching the item starts
+    ([100000] * 3, 256),        # items reaching over 32 workers each
+])
+def test_plan_bit_exact_division_paths(lengths, W):
+    # the scheduler's quotients by T and W' go by multiplication or in double
+    # precision, and its rows come from item marks or from a search
+    m = _m()
+    sl = i32_dev(np.array(lengths))
+    plan, ns = m.get_mla_metadata(sl, 16, 1, num_workers=W)
+    torch.cuda.synchronize()
+    p = plan.cpu().numpy()
+    c = int(p[1])
+    ref_p, ref_ns = orc.plan(lengths, W, c)
+    assert (p[:ref_p.size] == ref_p).all()
+    assert (ns.cpu().numpy() == ref_ns).all()
+
+
 @pytest.mark.parametrize("name", ["tiny", "memory_bound", "mtp_causal"])
 def test_row_ids_dense_bit_exact(name):
     m = _m()
