@@ -380,6 +380,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
   constexpr int kWaitKeepCopy = waitcnt_vm(C::kLoads);
   constexpr int kWaitKeepRawCopy = waitcnt_vm(C::kLoads + kRaw);
   static_assert(C::kLoads + kRaw < 64, "vmcnt holds 6 bits");
+  static_assert(C::kLoads + 2 * C::kCG + kRaw < 64, "vmcnt holds 6 bits (with a query-row copy)");
   __shared__ __attribute__((aligned(1024))) char s0[C::kStageBytes];
   __shared__ __attribute__((aligned(1024))) char s1[C::kStageBytes];
   __shared__ __attribute__((aligned(16))) unsigned char kvalid[4][64];   // sparse key validity, tile t -> t & 3
@@ -405,6 +406,11 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
   // loaded one step ahead ([tile & 1][wave][lane]: lane l of wave w holds the
   // page of row 16 w + l % 16).
   __shared__ __attribute__((aligned(256))) int pgbuf[(kWide && SPARSE) ? 2 : 1][4][64];
+  // Rows16, FP8 (whose copied tiles leave room): the query rows of the item a
+  // tile starts, copied in by wave 0 with that tile, in the tile layout.  Two
+  // slots, since an item of one tile can start and end between two reads.
+  constexpr bool kQSlots = KV8 && !kWide;
+  __shared__ __attribute__((aligned(1024))) char qbuf[kQSlots ? 2 : 1][kQSlots ? 16 * 2 * D : 16];
 
   // The arguments on the way to the first tile copy, loaded in one go (left
   // to itself, the compiler loads each one where it is first used, a round
@@ -846,10 +852,11 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     // `off_late`), so no register load has to complete behind a tile copy and
     // the copy of the next tile is not held back at the item boundary.
     int64_t off_late[C::kOffs];
+    constexpr int kQLoads = 2 * C::kCG;   // copies of 16 query rows (8 rows x 128 B each)
     auto issue_q = [&](char* stage, int item) __attribute__((always_inline)) {
       const char* q_bytes = reinterpret_cast<const char*>(a.q);
 #pragma unroll
-      for (int j = 0; j < C::kLoads; ++j) {
+      for (int j = 0; j < kQLoads; ++j) {
         const int r = j / C::kCG, cl = j % C::kCG;
         const int qr = cp_row[r] < a.M ? cp_row[r] : 0;     // rows past M borrow row 0
         const char* src = q_bytes + q_row(a, item, qr) * (int64_t)(2 * D) + cl * 128 +
@@ -858,12 +865,14 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
       }
     };
     auto q_from_lds = [&](const char* stage) __attribute__((always_inline)) {
-      // row li, chunk 4 ks + g, in the tile layout
+      // row li, in the tile layout; fragment ks holds the values load_q puts
+      // there: chunk 4 ks + g (FP8 latent k-steps: 8 (ks / 2) + 2 g + ks % 2)
       const int qb = ((li >> 3) * C::kCG << 10) + ((li & 7) << 7);
-      const int qx0 = (g ^ tswz(li)) << 4, qx1 = ((4 + g) ^ tswz(li)) << 4;
 #pragma unroll
-      for (int ks = 0; ks < C::kQf; ++ks)
-        qf[ks] = *reinterpret_cast<const bf16x8*>(stage + qb + ((ks >> 1) << 10) + ((ks & 1) ? qx1 : qx0));
+      for (int ks = 0; ks < C::kQf; ++ks) {
+        const int c = (KV8 && ks < 16) ? 8 * (ks >> 1) + 2 * g + (ks & 1) : 4 * ks + g;
+        qf[ks] = *reinterpret_cast<const bf16x8*>(stage + qb + ((c >> 3) << 10) + (((c & 7) ^ tswz(li)) << 4));
+      }
     };
     auto key_limit = [&](int item) __attribute__((always_inline)) -> int {   // dense: keys of this lane's row are < limit
       const int L = item_len(item);
@@ -1393,6 +1402,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     }
 
     bool q_pending = false;   // rows16, dense: the query rows of tile t's item come through LDS
+    bool q8_pending = false;  // rows16, FP8: they wait in qbuf[q8_rd]
+    int q8_wr = 0, q8_rd = 0;
 
     // One step: tile t sits in `cur`; tile t + 1 goes into `nxt`.  Tile t + 1
     // is requested before waiting for tile t, so two tiles are in flight while
@@ -1463,22 +1474,34 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
           issue(nxt, off);
         }
       }
+      // FP8: tile t + 1 starts an item; its query rows follow the tile's copy
+      const bool q8 = kQSlots && has_next && nx_item != cur_item;   // same in every wave
+      const int q8_slot = q8_wr;
+      if (q8 && wave == 0) issue_q(qbuf[q8_slot], nx_item);
       if (n2_item >= 0) tile_fetch(n2_item, n2_blk, raw);  // index data of tile t + 2
       // Vector-memory operations issued after tile t's copy: the copy of tile
-      // t + 1 and, in sparse mode, the index loads of tile t + 2.  Waiting
-      // until no more than those are outstanding completes tile t's copy
-      // (loads complete in order).  The compiler barrier keeps the index loads
-      // above the wait.
+      // t + 1, wave 0's query-row copies (FP8, at an item start) and, in sparse
+      // mode, the index loads of tile t + 2.  Waiting until no more than those
+      // are outstanding completes tile t's copy (loads complete in order).  The
+      // compiler barrier keeps the index loads above the wait.
       asm volatile("" ::: "memory");
       if (has_next && !q_lds) {
-        if (sparse && n2_item >= 0) __builtin_amdgcn_s_waitcnt(kWaitKeepRawCopy);
-        else __builtin_amdgcn_s_waitcnt(kWaitKeepCopy);
+        if (q8 && wave == 0) {
+          if (sparse && n2_item >= 0) __builtin_amdgcn_s_waitcnt(waitcnt_vm(C::kLoads + kQLoads + kRaw));
+          else __builtin_amdgcn_s_waitcnt(waitcnt_vm(C::kLoads + kQLoads));
+        } else if (sparse && n2_item >= 0) {
+          __builtin_amdgcn_s_waitcnt(kWaitKeepRawCopy);
+        } else {
+          __builtin_amdgcn_s_waitcnt(kWaitKeepCopy);
+        }
       } else {
         __builtin_amdgcn_s_waitcnt(0);     // wave 0 with staged query rows: tile t, then the rows
       }
       barrier_keep_loads();                              // tile t is in LDS for every wave
       if constexpr (KV8) sc_tab = reinterpret_cast<const float*>(cur + kRaw8ScaleOff);   // operands read from the codes
       if (q_pending) q_from_lds(nxt);
+      if (q8_pending) q_from_lds(qbuf[q8_rd]);
+      q8_pending = false;
       if (n2_item >= 0) tile_finish(n2_item, n2_blk, raw, off, kvalid[(t + 2) & 3]);
       const bool ends = !has_next || nx_item != cur_item;
       clear_if_empty(cur, kvalid[t & 3]);
@@ -1489,7 +1512,10 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
         if (has_next) {
           cur_lim = key_limit(nx_item);
           cur_split = 0;
-          if constexpr (sparse || KV8) {
+          if constexpr (kQSlots) {
+            q8_rd = q8_slot;           // copied in with the next tile
+            q8_pending = true;
+          } else if constexpr (sparse) {
             // Query rows of the next item, completed before the next copy is
             // issued (see the prologue).
             load_q(nx_item);
@@ -1499,6 +1525,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
           }
         }
       }
+      if (q8) q8_wr ^= 1;
       cur_item = nx_item;
       cur_blk = nx_blk;
       cur_hi = nx_hi;

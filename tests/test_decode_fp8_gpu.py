@@ -91,3 +91,18 @@ def test_fp8_split_count_invariance():
     for W in (1, 33, 700):
         o, lse, _ = run_gpu(Dev(w), num_workers=W)
         compare(w, o, lse, label=f"fp8 W={W}")
+
+
+@pytest.mark.parametrize("topk", [None, 32])
+def test_fp8_many_short_items(topk):
+    # Items of one or two tiles back to back (16-row tiles): the query rows of
+    # each come in with its first tile, through two alternating LDS slots.
+    rng = np.random.default_rng(78)
+    L = rng.integers(0, 130, size=150)
+    if topk is not None:
+        L = np.maximum(L, topk)
+    w = wl.build("many-fp8", 78, L, B=len(L), s_q=1, h_q=16, num_pages=400, poison=True,
+                 topk=topk, rng=rng, kv_format="fp8")
+    for W in (1, 2, 37):
+        o, lse, _ = run_gpu(Dev(w), num_workers=W)
+        compare(w, o, lse, label=f"fp8 many items topk={topk} W={W}")
