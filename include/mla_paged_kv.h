@@ -168,6 +168,8 @@ size_t mla_workspace_bytes(int batch, int s_q, int num_q_rows, int h_kv, int top
  *   softmax_scale   > 0 (the Python binding defaults to d_qk^-0.5)
  *   indices, topk   NULL and 0 for dense mode
  *   workspace       device scratch of at least mla_workspace_bytes(...) bytes
+ * With batch = 0 the call does nothing and returns MLA_OK; q, block_table,
+ * cache_seqlens, indices, o and lse may then be NULL (zero-length arrays).
  */
 int mla_decode_with_kvcache(const void* q, const void* kvcache, int64_t num_pages,
                             int page_size, const int32_t* block_table, int max_blocks,

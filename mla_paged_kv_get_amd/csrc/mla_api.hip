@@ -180,20 +180,24 @@ int decode_impl(const void* q, const void* kvcache, int64_t num_pages, int page_
   if (h_q % h_kv) return MLA_ERR_INVALID_ARGUMENT;
   if (page_size != kPage || dv != kDv) return MLA_ERR_UNSUPPORTED;
   if (d_qk != kDqk && !(d_qk == 512 && kv_format == 0)) return MLA_ERR_UNSUPPORTED;
+  // The per-sequence arrays (query rows, block tables, lengths, index lists,
+  // outputs) may be null when there is no sequence.
+  const bool any = batch > 0;
   if (aux) {
     if (topk <= 0 || aux->topk < 0 || aux->num_pages < 1 || aux->max_blocks < 1 || !aux->kv ||
-        !aux->block_table || !aux->seqlens || (aux->topk > 0) != (aux->indices != nullptr))
+        (any && (!aux->block_table || !aux->seqlens)) || (aux->topk <= 0 && aux->indices) ||
+        (any && aux->topk > 0 && !aux->indices))
       return MLA_ERR_INVALID_ARGUMENT;
     if ((int64_t)aux->max_blocks * kPage > (int64_t)0x7fffffff) return MLA_ERR_INVALID_ARGUMENT;
     if (aux->num_pages > ((int64_t)1 << 31) / kPage) return MLA_ERR_UNSUPPORTED;
   }
   if (causal != 0 && causal != 1) return MLA_ERR_INVALID_ARGUMENT;
-  if ((indices != nullptr) != (topk > 0)) return MLA_ERR_INVALID_ARGUMENT;
-  if (indices && causal) return MLA_ERR_INVALID_ARGUMENT;
+  if ((topk <= 0 && indices) || (any && topk > 0 && !indices)) return MLA_ERR_INVALID_ARGUMENT;
+  if (topk > 0 && causal) return MLA_ERR_INVALID_ARGUMENT;
   if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return MLA_ERR_INVALID_ARGUMENT;
   if (num_workers < 1 || num_workers > (1 << 20)) return MLA_ERR_INVALID_ARGUMENT;
-  if (!q || !kvcache || !block_table || !cache_seqlens || !plan || !num_splits || !o || !lse)
-    return MLA_ERR_INVALID_ARGUMENT;
+  if (!kvcache || !plan || !num_splits) return MLA_ERR_INVALID_ARGUMENT;
+  if (any && (!q || !block_table || !cache_seqlens || !o || !lse)) return MLA_ERR_INVALID_ARGUMENT;
   if ((int64_t)max_blocks * kPage > (int64_t)0x7fffffff) return MLA_ERR_INVALID_ARGUMENT;
   if (num_pages > ((int64_t)1 << 31) / kPage) return MLA_ERR_UNSUPPORTED;
   Shape s;

@@ -110,6 +110,16 @@ def test_decode_empty_batch_is_noop():
     assert _decode(batch=0) == _lib.MLA_OK
 
 
+def test_decode_empty_batch_takes_null_arrays():
+    # zero-length per-sequence arrays may be null; the shared ones may not
+    empty = dict(batch=0, q=None, bt=None, sl=None, o=None, lse=None)
+    assert _decode(**empty) == _lib.MLA_OK
+    assert _decode(**empty, idx=None, topk=16) == _lib.MLA_OK
+    assert _decode(**empty, kv=None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert _decode(**empty, plan=None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert _decode(**empty, idx=None, topk=16, causal=1) == _lib.MLA_ERR_INVALID_ARGUMENT
+
+
 def test_phase_argument_checked():
     l = _lib.lib()
     args = [DUMMY, DUMMY, 10, 64, DUMMY, 4, DUMMY, 2, 1, 16, 1, 576, 512, DUMMY, DUMMY, 8, 0,

@@ -71,6 +71,24 @@ def test_plan_bit_exact_division_paths(lengths, W):
     assert (ns.cpu().numpy() == ref_ns).all()
 
 
+def test_empty_batch():
+    # no sequence: every worker row is empty, no split, and the decode writes nothing
+    m = _m()
+    sl = i32_dev(np.zeros(0, dtype=np.int32))
+    plan, ns = m.get_mla_metadata(sl, 16, 1)
+    torch.cuda.synchronize()
+    p = plan.cpu().numpy()
+    ref_p, ref_ns = orc.plan([], int(p[0]), int(p[1]))
+    assert (p[:ref_p.size] == ref_p).all()
+    assert (ns.cpu().numpy() == ref_ns).all()
+    q = torch.zeros((0, 1, 16, 576), dtype=torch.bfloat16, device="cuda")
+    kv = torch.zeros((1, 64, 1, 576), dtype=torch.bfloat16, device="cuda")
+    bt = i32_dev(np.zeros((0, 1), dtype=np.int32))
+    o, lse = m.mla_decode_with_kvcache(q, kv, bt, sl, 512, plan, ns)
+    torch.cuda.synchronize()
+    assert tuple(o.shape) == (0, 1, 16, 512) and tuple(lse.shape) == (0, 1, 16)
+
+
 @pytest.mark.parametrize("name", ["tiny", "memory_bound", "mtp_causal"])
 def test_row_ids_dense_bit_exact(name):
     m = _m()
