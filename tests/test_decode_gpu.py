@@ -71,6 +71,22 @@ def test_plan_bit_exact_division_paths(lengths, W):
     assert (ns.cpu().numpy() == ref_ns).all()
 
 
+@pytest.mark.parametrize("h_q", [16, 128])
+def test_all_sequences_empty(h_q):
+    # every item has no key: no worker gets a block, every row is o = 0, lse = -inf
+    w = wl.build("all-empty", 38, np.zeros(5, dtype=np.int64), B=5, s_q=2, h_q=h_q, num_pages=4,
+                 causal=True, poison=True)
+    for phases in (3, 4):
+        m = _m()
+        d = Dev(w)
+        plan, ns = m.get_mla_metadata(d.sl, 2 * h_q, 1, s_q=2)
+        o, lse = m.mla_decode_with_kvcache(d.q, d.kv, d.bt, d.sl, 512, plan, ns, causal=True, phases=phases)
+        torch.cuda.synchronize()
+        assert (o.float().cpu().numpy() == 0).all()
+        assert np.isneginf(lse.cpu().numpy()).all()
+        assert (ns.cpu().numpy() == 0).all()
+
+
 def test_empty_batch():
     # no sequence: every worker row is empty, no split, and the decode writes nothing
     m = _m()
