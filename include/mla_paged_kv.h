@@ -109,7 +109,7 @@ int mla_plan_num_workers(int plan_words, int batch, int s_q, int num_q_rows, int
  *                  entries outside [0, L_b) are padding)
  * Rule: item i has n_i = ceil(len_i / 64) blocks (len_i = cache_seqlens[i / h_kv]
  * dense, topk sparse) and costs overhead + n_i units (overhead = 1 block
- * for items of at most 16 query rows, 2 for wider items); items are laid end to end on a cost axis (total T); the first
+ * for items of at most 16 query rows, 4 for wider items); items are laid end to end on a cost axis (total T); the first
  * W' = min(W, T) workers share it evenly, worker w owning the units
  * [floor(w T / W'), floor((w + 1) T / W')); block b of item i sits on unit
  * (start of item i) + overhead + b, and a worker gets the blocks on its units.
