@@ -20,10 +20,15 @@ launches costs several microseconds of GPU time.  The duration of each
 launch (plan, split decode, combine) comes from a second pass that enqueues
 K launches of that kernel alone, back to back, between two events.
 
-`roofline.traffic` is the HBM traffic of one decode launch measured with
-rocprofv3 counters (FETCH_SIZE and WRITE_SIZE, each calibrated against a plain
-device copy of known size, see --calibrate-copy) and stored in
-profiles/decode_memory_bound_traffic.json together with the SHA-256 of the
+The default run also times the compute-bound workloads (near-ridge b=128
+h_q=128 L=4096; MTP causal b=32 s_q=2 h_q=128; sparse top-k b=16 s_q=8 h_q=128
+k=2048) and reports their bf16 TFLOPS and MFMA fraction under
+`compute_bound`; --secondary adds the other workloads.
+
+`traffic` is the HBM traffic of one decode launch measured with rocprofv3
+counters (FETCH_SIZE and WRITE_SIZE, each calibrated against a plain device
+copy of known size, see --calibrate-copy) and stored in
+profiles/decode_<workload>_traffic.json together with the SHA-256 of the
 kernel source it was taken on; it is reported only while that source is
 unchanged, else null.
 
@@ -158,7 +163,9 @@ def run_workload(torch, m, w, steps, warmup, ncopies=NCOPIES):
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 DECODE_SRC = os.path.join(HERE, "mla_paged_kv_get_amd", "csrc", "mla_decode.hip")
-TRAFFIC_FILE = os.path.join(HERE, "profiles", "decode_memory_bound_traffic.json")
+PROFILES = os.path.join(HERE, "profiles")
+COMPUTE_BOUND = ("near_ridge", "mtp_causal", "sparse_topk")
+SECONDARY = ("grouped_heads", "sparse_prefill", "memory_bound_fp8", "sparse_topk_fp8", "dual_cache")
 
 
 def source_sha256(path=DECODE_SRC):
@@ -166,11 +173,12 @@ def source_sha256(path=DECODE_SRC):
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic(workload):
-    """HBM bytes per decode launch from the committed counter run, if it was
-    taken on this workload and on the current kernel source; else None."""
+def measured_traffic(key, workload):
+    """HBM bytes per decode launch from the committed counter run of workload
+    `key`, if it was taken on this workload and on the current kernel source;
+    else None."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(os.path.join(PROFILES, f"decode_{key}_traffic.json")) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -193,29 +201,43 @@ def calibrate_copy(torch, mib, reps=10):
     print(json.dumps({"calibrate_copy_bytes": n, "reps": reps}), flush=True)
 
 
-def cpu_baseline(w, budget_s=10.0):
-    """The CPU oracle on the same workload, repeated until ~budget_s of CPU time."""
+def cpu_baseline(w, budget_s=8.0):
+    """The CPU oracle on the same workload, timed twice: with its BLAS pinned to
+    one thread, then with every host core; each leg repeats the whole decode
+    until about budget_s of wall time."""
     from oracle import mla_oracle as orc
-    threads = None
-    try:
-        from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    kv_bytes, flops = algorithmic_work(w)
+
+    def blas_threads():
         infos = [i for i in threadpool_info() if i.get("user_api") == "blas"]
-        threads = max((i.get("num_threads") or 1) for i in infos) if infos else None
-    except Exception:
-        pass
-    kv_bytes, _ = algorithmic_work(w)
-    t0 = time.perf_counter()
-    reps = 0
-    while True:
-        orc.decode(w.q, w.kv, w.block_table, w.cache_seqlens, 512, causal=w.causal,
-                   indices=w.indices)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or reps >= 50:
-            break
-    return {"value": round(kv_bytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": threads or os.cpu_count(),
-            "kind": "oracle",
-            "sample": f"float64 NumPy oracle, whole workload ({w.B} sequences) decoded {reps}x in {el:.1f} s"}
+        return max((i.get("num_threads") or 1) for i in infos) if infos else 1
+
+    def leg():
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            orc.decode(w.q, w.kv, w.block_table, w.cache_seqlens, 512, causal=w.causal,
+                       indices=w.indices, aux=w.aux)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or reps >= 50:
+                return reps, el
+
+    with threadpool_limits(limits=1, user_api="blas"):
+        one = blas_threads()
+        r1, e1 = leg()
+    cores = blas_threads()
+    rn, en = leg()
+    return {"value": round(kv_bytes * rn / en / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"float64 NumPy oracle, whole workload ({w.B} sequences) decoded {rn}x in {en:.1f} s "
+                      f"with {cores} BLAS threads",
+            "gflops": round(flops * rn / en / 1e9, 3),
+            "one_thread": {"value": round(kv_bytes * r1 / e1 / 1e9, 4), "unit": "GB/s", "cores": one,
+                           "gflops": round(flops * r1 / e1 / 1e9, 3),
+                           "sample": f"the same, decoded {r1}x in {e1:.1f} s with {one} BLAS thread"},
+            "host_cpus": os.cpu_count()}
 
 
 def main():
@@ -228,9 +250,11 @@ def main():
                              "grouped_heads", "sparse_prefill", "memory_bound_fp8", "sparse_topk_fp8",
                              "dual_cache"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-compute-bound", action="store_true",
+                    help="skip the near-ridge, MTP-causal and sparse top-k workloads")
     ap.add_argument("--secondary", action="store_true",
-                    help="also time the near-ridge, MTP-causal, sparse top-k, grouped-heads, "
-                         "sparse-prefill, the two packed-FP8 and the dual-cache workloads")
+                    help="also time the grouped-heads, sparse-prefill, the two packed-FP8 and the "
+                         "dual-cache workloads")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run plain device copies of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -253,6 +277,7 @@ def main():
     kv_bytes, flops = algorithmic_work(w)
     r = run_workload(torch, m, w, args.steps, args.warmup)
     dec_s = r["decode_ms"] / 1e3
+    dc_s = (r["decode_ms"] + r["combine_ms"]) / 1e3      # decode + combine, the step without the plan
     achieved = kv_bytes / dec_s / 1e9
     step_s = r["ms_per_step"] / 1e3
     line = {
@@ -279,27 +304,38 @@ def main():
                               "single_launch_step": round(r["ms_per_step_single"], 5)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(w.name),
+                     "traffic": measured_traffic(args.workload, w.name),
+                     "frac_decode_plus_combine": round(kv_bytes / dc_s / 1e9 / HBM_PEAK_GBS, 4),
                      "kernel": "split decode kernel", "launch_ms": round(r["decode_ms"], 5),
                      "mfma_tflops": round(flops / dec_s / 1e12, 2),
                      "mfma_frac": round(flops / dec_s / 1e12 / BF16_PEAK_TFLOPS, 4)},
     }
-    if args.secondary:
-        sec = {}
-        for name in ("near_ridge", "mtp_causal", "sparse_topk", "grouped_heads", "sparse_prefill",
-                     "memory_bound_fp8", "sparse_topk_fp8", "dual_cache"):
+    def other(names, steps):
+        out = {}
+        for name in names:
+            print(f"bench: timing {name}", file=sys.stderr, flush=True)
             w2 = wl.NAMED[name]()
             kb, fl = algorithmic_work(w2)
-            r2 = run_workload(torch, m, w2, max(10, args.steps // 2), 3)
+            r2 = run_workload(torch, m, w2, steps, 3)
             d2 = r2["decode_ms"] / 1e3
-            sec[name] = {"workload": w2.name, "decode_ms": round(r2["decode_ms"], 5),
-                         "combine_ms": round(r2["combine_ms"], 5), "plan_ms": round(r2["plan_ms"], 5),
-                         "kv_GBps": round(kb / d2 / 1e9, 1), "hbm_frac": round(kb / d2 / 1e9 / HBM_PEAK_GBS, 4),
+            dc2 = (r2["decode_ms"] + r2["combine_ms"]) / 1e3
+            out[name] = {"workload": w2.name, "kv_bytes": kb, "flops": fl,
+                         "decode_ms": round(r2["decode_ms"], 5), "combine_ms": round(r2["combine_ms"], 5),
+                         "plan_ms": round(r2["plan_ms"], 5), "step_ms": round(r2["ms_per_step"], 5),
+                         "num_workers": r2["num_workers"],
                          "TFLOPS": round(fl / d2 / 1e12, 1), "mfma_frac": round(fl / d2 / 1e12 / BF16_PEAK_TFLOPS, 4),
-                         "step_ms": round(r2["ms_per_step"], 5)}
-            del r2
+                         "kv_GBps": round(kb / d2 / 1e9, 1), "hbm_frac": round(kb / d2 / 1e9 / HBM_PEAK_GBS, 4),
+                         "mfma_frac_decode_plus_combine": round(fl / dc2 / 1e12 / BF16_PEAK_TFLOPS, 4),
+                         "hbm_frac_decode_plus_combine": round(kb / dc2 / 1e9 / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic(name, w2.name)}
+            del r2, w2
             torch.cuda.empty_cache()
-        line["secondary"] = sec
+        return out
+
+    if not args.no_compute_bound and args.workload == "memory_bound":
+        line["compute_bound"] = other(COMPUTE_BOUND, max(10, args.steps // 2))
+    if args.secondary:
+        line["secondary"] = other(SECONDARY, max(10, args.steps // 2))
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)

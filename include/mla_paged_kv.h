@@ -62,6 +62,7 @@ extern "C" {
 #define MLA_D_QK 576
 #define MLA_D_V 512
 #define MLA_PLAN_WORDS 8             /* int32 words per plan row */
+#define MLA_PLAN_MAX_ITEMS 16384     /* items one metadata call can plan */
 
 /* Human-readable text of a status code (static storage, never NULL). */
 const char* mla_status_string(int status);
@@ -80,9 +81,15 @@ const char* mla_status_string(int status);
  *   num_workers_request  0 = let the library choose (CU count and the decode
  *                        variant picked for this row count); > 0 forces it
  *   out_num_workers      workers W of the plan (host)
- *   out_plan_words       int32 words of the plan buffer = 8 * (W + 1) (host)
+ *   out_plan_words       int32 words of the plan buffer (host): 8 * (W + 1)
+ *                        words of plan rows, then items * ceil(num_q_rows' /
+ *                        tile rows) int32 arrival counters of the single-launch
+ *                        decode (num_q_rows' = rows per item; tile rows = 16,
+ *                        64 or 128 depending on the decode variant the row
+ *                        count selects)
  *   out_num_items        items of the call; num_splits holds items + 1 words (host)
- * Needs the current HIP device only when num_workers_request == 0.
+ * Needs the current HIP device only when num_workers_request == 0.  A call
+ * with more than MLA_PLAN_MAX_ITEMS items returns MLA_ERR_UNSUPPORTED.
  */
 int mla_plan_dims(int batch, int s_q, int num_q_rows, int h_kv, int topk,
                   int num_workers_request, int* out_num_workers,
@@ -107,33 +114,44 @@ int mla_plan_num_workers(int plan_words, int batch, int s_q, int num_q_rows, int
  *
  *   cache_seqlens  [batch] int32, device (read in sparse mode as well: index
  *                  entries outside [0, L_b) are padding)
- * Rule: item i has n_i = ceil(len_i / 64) blocks (len_i = cache_seqlens[i / h_kv]
- * dense, topk sparse) and costs overhead + n_i units (overhead = 1 block
+ * Rule: item i has n_i blocks (dense: ceil(cache_seqlens[i / h_kv] / 64);
+ * sparse: ceil(topk / 64) + ceil(topk2 / 64), topk2 being the length of the
+ * auxiliary index lists of the dual-cache decode, 0 otherwise) and costs
+ * overhead + n_i units (overhead = 1 block
  * for items of at most 16 query rows, 4 for wider items); items are laid end to end on a cost axis (total T); the first
  * W' = min(W, T) workers share it evenly, worker w owning the units
  * [floor(w T / W'), floor((w + 1) T / W')); block b of item i sits on unit
  * (start of item i) + overhead + b, and a worker gets the blocks on its units.
  *
- *   plan           [8 * (W + 1)] int32, device (output).  Row 0 = {W, per-run
+ *   topk, topk2    index-list lengths of the sparse modes (0 for dense; topk2
+ *                  only with topk > 0)
+ *   plan           [out_plan_words] int32, device (output).  Row 0 = {W, per-run
  *                  overhead in blocks, W', items, version 2, 64, total cost T,
  *                  0}; row 1 + w = {first item, its first
  *                  block, last item, end block (exclusive) in the last item,
  *                  split number of the run in the first item, 0, 0, 0}, or
  *                  {-1, 0, -1, 0, 0, 0, 0, 0} for a worker with no blocks.
+ *                  The rows are followed by the arrival counters of the
+ *                  single-launch decode, which this call sets to zero.
  *   num_splits     [items + 1] int32, device (output): exclusive prefix sum
  *                  of the per-item split counts.
  * The plan stays valid for every decode call with the same lengths, batch,
- * s_q, topk and W; items of length 0 get no split.
+ * s_q, topk, topk2 and W; items of length 0 get no split.  The decode calls
+ * only read it, except the single-launch decode (phases = 4), which counts
+ * finished runs in the plan's arrival counters and leaves them zero when it
+ * completes: single-launch calls that share one plan must not overlap (two
+ * streams), while two-launch calls may.  More than MLA_PLAN_MAX_ITEMS items:
+ * MLA_ERR_UNSUPPORTED.  The cost axis is 32-bit: the sum over items of
+ * (overhead + n_i) must stay below 2^31 (about 1.4e11 cached tokens).
  */
 int mla_get_metadata(const int32_t* cache_seqlens, int batch, int s_q,
-                     int num_q_rows, int h_kv, int topk, int num_workers,
+                     int num_q_rows, int h_kv, int topk, int topk2, int num_workers,
                      int32_t* plan, int32_t* num_splits, void* stream);
 
 /*
- * mla_workspace_bytes — host only; bytes of the decode scratch buffer:
- * (items + W) partial results of num_q_rows x (dv + 1) fp32 values each, then
- * one int32 arrival counter per item and row tile (the single-launch mode of
- * mla_decode_with_kvcache_phase).
+ * mla_workspace_bytes — host only; bytes of the decode scratch buffer: room
+ * for (items + W) partial results of (rows per item) x (dv + 1) fp32 values
+ * (split runs write one each; at most items + W - 1 are used).
  */
 size_t mla_workspace_bytes(int batch, int s_q, int num_q_rows, int h_kv, int topk,
                            int dv, int num_workers);
@@ -192,12 +210,11 @@ int mla_decode_with_kvcache(const void* q, const void* kvcache, int64_t num_page
  * item 3): one kernel, in
  * which the last run of each split item to finish merges the item's partials
  * and items without a key are written as well.  Its runs exchange partials
- * through memory at agent scope and count arrivals in the last
- * items * ceil(rows / tile rows) ints of `workspace`, which must be zero
- * before the first phases = 4 call on a workspace; every completed call
- * leaves them zero (calls sharing one workspace must not overlap).  Any other
- * value returns MLA_ERR_INVALID_ARGUMENT.  Same arguments, checks and
- * ownership rules as mla_decode_with_kvcache.
+ * through `workspace` at agent scope and count arrivals in the plan's arrival
+ * counters (after its rows; zeroed by mla_get_metadata, left zero by every
+ * completed call): single-launch calls that share a plan or a workspace must
+ * not overlap.  Any other value returns MLA_ERR_INVALID_ARGUMENT.  Same
+ * arguments, checks and ownership rules as mla_decode_with_kvcache.
  */
 int mla_decode_with_kvcache_phase(const void* q, const void* kvcache, int64_t num_pages,
                                   int page_size, const int32_t* block_table, int max_blocks,
@@ -222,9 +239,13 @@ int mla_decode_with_kvcache_phase(const void* q, const void* kvcache, int64_t nu
  *
  * K_j is the row's 576 values (latent code x its block's scale, then RoPE),
  * V_j its first 512; d_qk must be 576 (the number of values, not bytes).  In
- * the kernels each dequantized latent value is rounded to bf16 before the
- * bf16 matrix products.  Every other argument, check, status and the phases
- * argument are those of mla_decode_with_kvcache(_phase), with the same plan.
+ * the kernels the codes enter the bf16 matrix products as they are (every
+ * E4M3 value is a bf16 value) and the scales never do: Q K^T is accumulated
+ * per 128-value block and each block's sum is multiplied by the key's scale
+ * in fp32, and in P V each key's probability is multiplied by its scale for
+ * the output columns' block before P is rounded to bf16.  Every other
+ * argument, check, status and the phases argument are those of
+ * mla_decode_with_kvcache(_phase), with the same plan.
  */
 int mla_decode_with_kvcache_fp8(const void* q, const void* kvcache, int64_t num_pages,
                                 int page_size, const int32_t* block_table, int max_blocks,
@@ -253,9 +274,9 @@ int mla_decode_with_kvcache_fp8_phase(const void* q, const void* kvcache, int64_
  * cache, valid below cache_seqlens2[b]), with one softmax over both; entries
  * outside [0, L) of their list are padding.  Both caches are bf16 [pages, 64,
  * h_kv, d_qk] with their own block tables; d_qk is 576 or 512 (the same rows
- * as mla_decode_with_kvcache).  The plan comes from mla_get_metadata with
- * topk = 64 * (ceil(topk / 64) + ceil(topk2 / 64)): every item has that many
- * 64-key tiles, the main list's first.  topk2 may be 0 (indices2 NULL).
+ * as mla_decode_with_kvcache).  The plan comes from mla_get_metadata with the
+ * same topk and topk2: every item has ceil(topk / 64) + ceil(topk2 / 64)
+ * tiles of 64 keys, the main list's first.  topk2 may be 0 (indices2 NULL).
  * causal is not an argument (sparse mode); the other arguments, checks and
  * phases are those of mla_decode_with_kvcache_phase.
  */

@@ -37,7 +37,7 @@ _SIGS = {
     "mla_status_string": (ctypes.c_char_p, [_c_int]),
     "mla_plan_dims": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _ip, _ip, _ip]),
     "mla_plan_num_workers": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
-    "mla_get_metadata": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp]),
+    "mla_get_metadata": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp]),
     "mla_workspace_bytes": (ctypes.c_size_t, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
     "mla_decode_with_kvcache": (_c_int, [
         _vp, _vp, _c_i64, _c_int, _vp, _c_int, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,

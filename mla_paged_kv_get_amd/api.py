@@ -70,15 +70,12 @@ def get_mla_metadata(cache_seqlens: torch.Tensor, num_q_rows: int, h_kv: int, *,
     _need(cache_seqlens.is_cuda, "cache_seqlens must be on the GPU")
     batch = cache_seqlens.numel()
     tk = int(topk or 0)
-    if topk2:
-        _need(tk > 0, "topk2 needs topk (dual-cache decode is sparse)")
-        tk = 64 * (-(-tk // 64) + -(-int(topk2) // 64))
     W, words, items = plan_dims(batch, s_q, num_q_rows, h_kv, tk, int(num_workers or 0))
     dev = cache_seqlens.device
     plan = torch.empty(words, dtype=torch.int32, device=dev)
     num_splits = torch.empty(items + 1, dtype=torch.int32, device=dev)
-    _lib.check(_lib.lib().mla_get_metadata(_ptr(cache_seqlens), batch, s_q, num_q_rows, h_kv, tk, W,
-                                           _ptr(plan), _ptr(num_splits), _stream(dev)),
+    _lib.check(_lib.lib().mla_get_metadata(_ptr(cache_seqlens), batch, s_q, num_q_rows, h_kv, tk,
+                                           int(topk2), W, _ptr(plan), _ptr(num_splits), _stream(dev)),
                "mla_get_metadata")
     return plan, num_splits
 

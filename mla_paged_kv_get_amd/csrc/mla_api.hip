@@ -126,16 +126,25 @@ int mla_plan_num_workers(int plan_words, int batch, int s_q, int num_q_rows, int
 }
 
 int mla_get_metadata(const int32_t* cache_seqlens, int batch, int s_q, int num_q_rows, int h_kv,
-                     int topk, int num_workers, int32_t* plan, int32_t* num_splits, void* stream) {
+                     int topk, int topk2, int num_workers, int32_t* plan, int32_t* num_splits,
+                     void* stream) {
   if (!plan || !num_splits) return MLA_ERR_INVALID_ARGUMENT;
   if (topk <= 0 && !cache_seqlens && batch > 0) return MLA_ERR_INVALID_ARGUMENT;
   if (num_workers < 1 || num_workers > (1 << 20)) return MLA_ERR_INVALID_ARGUMENT;
+  if (topk2 < 0 || (topk2 > 0 && topk <= 0)) return MLA_ERR_INVALID_ARGUMENT;
   Shape s;
   const int st = shape_of(batch, s_q, num_q_rows, h_kv, topk, &s);
   if (st != MLA_OK) return st;
   if (s.items > mla::plan_max_items()) return MLA_ERR_UNSUPPORTED;
+  // Sparse items: the tiles of the main list, then those of the auxiliary list
+  // (dual cache), each list in 64-key tiles.
+  int64_t tile_keys = 0;
+  if (topk > 0) {
+    tile_keys = (int64_t)kPage * (((int64_t)topk + kPage - 1) / kPage + ((int64_t)topk2 + kPage - 1) / kPage);
+    if (tile_keys > 0x7fffffff) return MLA_ERR_UNSUPPORTED;
+  }
   const int overhead = variant_overhead(s.variant);
-  const hipError_t e = launch_plan(cache_seqlens, topk > 0 ? topk : 0, s.items, h_kv, num_workers,
+  const hipError_t e = launch_plan(cache_seqlens, (int)tile_keys, s.items, h_kv, num_workers,
                                    overhead, plan, num_splits,
                                    plan + (int64_t)kPlanWords * (num_workers + 1),
                                    (int)plan_counters(s), reinterpret_cast<hipStream_t>(stream));

@@ -354,37 +354,41 @@ def decode_by_plan(q_bits, kv_bits, block_table, cache_seqlens, dv, plan_words,
 # Work accounting used by the benchmark (algorithmic bytes and flops)
 # --------------------------------------------------------------------------
 def work(cache_seqlens, s_q: int, h_q: int, causal: bool, d_qk: int = D_QK, dv: int = D_V,
-         topk: int | None = None, indices=None, h_kv: int = 1):
+         topk: int | None = None, indices=None, h_kv: int = 1, row_bytes: int | None = None,
+         aux=None):
     """(KV bytes read once per key, FLOPs) of one decode call.
 
-    KV bytes count each (sequence, key, latent head) row once at 2 bytes per
-    value; FLOPs are 2 * (d_qk + dv) per (query row, key).
+    KV bytes count each (sequence, key, latent head) row once at its stored
+    size: ``row_bytes`` (default 2 bytes per value, i.e. a bf16 row; a packed
+    FP8 row is 656 bytes).  FLOPs are 2 * (d_qk + dv) per (query row, key).
+    ``aux = (cache_seqlens2, indices2)`` adds the auxiliary cache's keys of a
+    dual-cache sparse decode (entries inside [0, cache_seqlens2[b])), whose
+    rows have the same size.
     """
+    if row_bytes is None:
+        row_bytes = d_qk * 2
     if indices is not None:
         idx = np.asarray(indices)
         L = np.asarray(cache_seqlens).reshape(-1, 1, 1)
         keys_per_token = ((idx >= 0) & (idx < L)).sum()
+        if aux is not None:
+            L2 = np.asarray(aux[0]).reshape(-1, 1, 1)
+            idx2 = np.asarray(aux[1])
+            keys_per_token = keys_per_token + ((idx2 >= 0) & (idx2 < L2)).sum()
         kv_rows = keys_per_token
         qk = keys_per_token * h_q
     else:
+        if aux is not None:
+            raise ValueError("an auxiliary cache needs sparse mode")
         kv_rows = 0
         qk = 0
         for L in (int(x) for x in cache_seqlens):
             kv_rows += L
             for s in range(s_q):
                 qk += h_q * (max(L - s_q + s + 1, 0) if causal else L)
-    return int(kv_rows) * h_kv * d_qk * 2, int(qk) * 2 * (d_qk + dv)
-
-
-def bf16_round_f64(x: np.ndarray) -> np.ndarray:
-    """Round float64 values to the nearest bf16 (ties to even), returned as float64."""
-    f = np.asarray(x, dtype=np.float64).astype(np.float32)
-    u = f.view(np.uint32).astype(np.uint64)
-    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    r = np.where(np.isnan(f), 0x7FC0, r).astype(np.uint16)
-    return bf16_to_f64(r)
+    return int(kv_rows) * h_kv * int(row_bytes), int(qk) * 2 * (d_qk + dv)
 
 
 __all__ = ["PAGE", "D_QK", "D_V", "FP8_ROW_BYTES", "FP8_BLOCK", "e4m3_to_f64", "fp8_rows_to_f64", "bf16_to_f64", "physical_rows", "key_positions", "decode",
-           "merge_splits", "plan", "plan_runs", "decode_by_plan", "work", "bf16_round_f64",
+           "merge_splits", "plan", "plan_runs", "decode_by_plan", "work",
            "PLAN_WORDS", "PLAN_VERSION"]

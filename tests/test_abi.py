@@ -169,12 +169,32 @@ def test_dual_rejects(kw, code):
 
 def test_metadata_rejects():
     l = _lib.lib()
-    assert l.mla_get_metadata(DUMMY, 4, 1, 16, 1, 0, 8, None, DUMMY, None) == _lib.MLA_ERR_INVALID_ARGUMENT
-    assert l.mla_get_metadata(DUMMY, 4, 1, 16, 1, 0, 0, DUMMY, DUMMY, None) == _lib.MLA_ERR_INVALID_ARGUMENT
-    assert l.mla_get_metadata(DUMMY, 4, 1, 16, 0, 0, 8, DUMMY, DUMMY, None) == _lib.MLA_ERR_INVALID_ARGUMENT
-    assert l.mla_get_metadata(DUMMY, 10000, 1, 16, 2, 0, 8, DUMMY, DUMMY, None) == _lib.MLA_ERR_UNSUPPORTED
-    assert l.mla_get_metadata(None, 4, 1, 16, 1, 0, 8, DUMMY, DUMMY, None) == _lib.MLA_ERR_INVALID_ARGUMENT
-    assert l.mla_get_metadata(DUMMY, 20000, 1, 16, 1, 0, 8, DUMMY, DUMMY, None) == _lib.MLA_ERR_UNSUPPORTED
+    # (cache_seqlens, batch, s_q, num_q_rows, h_kv, topk, topk2, W, plan, num_splits, stream)
+    assert l.mla_get_metadata(DUMMY, 4, 1, 16, 1, 0, 0, 8, None, DUMMY, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert l.mla_get_metadata(DUMMY, 4, 1, 16, 1, 0, 0, 0, DUMMY, DUMMY, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert l.mla_get_metadata(DUMMY, 4, 1, 16, 0, 0, 0, 8, DUMMY, DUMMY, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert l.mla_get_metadata(None, 4, 1, 16, 1, 0, 0, 8, DUMMY, DUMMY, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    # topk2 (the auxiliary lists of the dual-cache decode) needs topk and is >= 0
+    assert l.mla_get_metadata(DUMMY, 4, 1, 16, 1, 0, 32, 8, DUMMY, DUMMY, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert l.mla_get_metadata(DUMMY, 4, 1, 16, 1, 64, -1, 8, DUMMY, DUMMY, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    # the tiles of an item (both lists) must be countable in an int
+    assert l.mla_get_metadata(DUMMY, 4, 1, 16, 1, 2 ** 31 - 1, 2 ** 31 - 1, 8, DUMMY, DUMMY,
+                              None) == _lib.MLA_ERR_UNSUPPORTED
+
+
+def test_metadata_item_cap():
+    # one call plans at most MLA_PLAN_MAX_ITEMS = 16384 items (dense: batch * h_kv;
+    # sparse: batch * s_q * h_kv); one more is rejected before anything is enqueued
+    l = _lib.lib()
+    cap = 16384
+    assert l.mla_get_metadata(DUMMY, cap + 1, 1, 16, 1, 0, 0, 8, DUMMY, DUMMY, None) == _lib.MLA_ERR_UNSUPPORTED
+    assert l.mla_get_metadata(DUMMY, cap // 2 + 1, 1, 32, 2, 0, 0, 8, DUMMY, DUMMY, None) == _lib.MLA_ERR_UNSUPPORTED
+    assert l.mla_get_metadata(DUMMY, 1, cap + 1, (cap + 1) * 16, 1, 64, 0, 8, DUMMY, DUMMY,
+                              None) == _lib.MLA_ERR_UNSUPPORTED
+    assert l.mla_get_metadata(DUMMY, 2, cap // 2 + 1, (cap // 2 + 1) * 16, 1, 64, 32, 8, DUMMY, DUMMY,
+                              None) == _lib.MLA_ERR_UNSUPPORTED
+    hdr = open(os.path.join(ROOT, "include", "mla_paged_kv.h")).read()
+    assert re.search(r"#define MLA_PLAN_MAX_ITEMS\s+16384\b", hdr)
 
 
 def test_debug_and_validate_reject():

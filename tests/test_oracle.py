@@ -551,6 +551,40 @@ def test_work_closed_forms():
     assert b == 2 * 1152 and f == 8 * 2 * 2176
     b, f = orc.work([100, 7], 1, 32, False, h_kv=4)     # each key read once per latent head
     assert b == 107 * 4 * 1152 and f == 32 * 107 * 2176
+    b, f = orc.work([100, 7], 1, 16, False, row_bytes=656)   # packed FP8 rows
+    assert b == 107 * 656 and f == 16 * 107 * 2176
+    # dual cache: 2 main keys (0, 5) and 1 auxiliary key (3 < 4) for the one token
+    b, f = orc.work([50], 1, 8, False, d_qk=512, indices=idx,
+                    aux=(np.array([4]), np.array([[[3, 4, -1]]])))
+    assert b == 3 * 1024 and f == 8 * 3 * 2 * 1024
+
+
+def test_bench_work_accounting_matches_oracle():
+    """bench.py's byte and FLOP counts agree with orc.work on every kind of
+    workload it times (dense, causal, sparse, grouped heads, packed FP8, dual
+    cache with 512-value rows)."""
+    import bench
+    cases = [
+        wl.build("w-dense", 90, np.array([300, 1, 0, 129]), B=4, s_q=1, h_q=16, num_pages=20),
+        wl.build("w-causal", 91, np.array([300, 1, 0, 129]), B=4, s_q=3, h_q=32, num_pages=20, causal=True),
+        wl.build("w-grouped", 92, np.array([77, 640]), B=2, s_q=2, h_q=64, h_kv=4, num_pages=20),
+        wl.build("w-sparse", 93, np.array([300, 200]), B=2, s_q=2, h_q=128, num_pages=20, topk=100),
+        wl.build("w-fp8", 94, np.array([300, 5]), B=2, s_q=1, h_q=16, num_pages=20, kv_format="fp8"),
+        wl.build("w-fp8-sparse", 95, np.array([300, 90]), B=2, s_q=2, h_q=128, num_pages=20, topk=64,
+                 kv_format="fp8"),
+    ]
+    cases[3].indices[1, 0, :7] = -1        # padding entries
+    rng = np.random.default_rng(96)
+    dual = wl.build("w-dual", 96, np.array([300, 200]), B=2, s_q=2, h_q=128, num_pages=20, topk=64,
+                    rng=rng, d_qk=512)
+    cases.append(wl.add_aux_cache(dual, rng, np.array([100, 0]), 80, 8))
+    for w in cases:
+        h_kv = w.kv.shape[2]
+        row_bytes = w.kv.shape[3] * w.kv.itemsize
+        aux = (w.aux[2], w.aux[3]) if w.aux is not None else None
+        ref = orc.work(w.cache_seqlens, w.s_q, w.h_q, w.causal, d_qk=w.q.shape[3], topk=w.topk,
+                       indices=w.indices, h_kv=h_kv, row_bytes=row_bytes, aux=aux)
+        assert bench.algorithmic_work(w) == ref, w.name
 
 
 def test_named_workload_recipes():
