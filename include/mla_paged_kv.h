@@ -293,16 +293,38 @@ int mla_decode_with_kvcache_dual(const void* q, const void* kvcache, int64_t num
                                  void* stream);
 
 /*
- * mla_debug_row_ids — indexing probe (test use).  Writes, through the same
- * device address function the decode kernels use, the physical cache row
- * (page * 64 + slot) of every key, or -1 where a key is not in the key set:
- *   dense:  out [batch, max_blocks * 64] int64, device; entry (b, j) for
- *           j < L_b, -1 for j >= L_b
- *   sparse: out [batch, s_q, topk] int64, device; -1 for padding entries
+ * mla_debug_copy_rows — indexing probe (test use).  Runs the split decode
+ * kernel (phase 1 of the decode: every argument as for the decode entry point
+ * of the same cache format; kv_format 0 = bf16 rows, 1 = packed FP8 rows;
+ * kvcache2 != NULL selects the dual-cache decode, bf16 and sparse only,
+ * with its auxiliary arguments as for mla_decode_with_kvcache_dual, else they
+ * are ignored), and has the kernel also write, for every cache row one of its
+ * tile copies reads, the byte offset of that row from kvcache, taken from the
+ * very registers the copy instructions use.  The tiles and rows of 64-token
+ * pages follow "What is FlashMLA" (topnet.top), section "FlashMLA의 주요 특성",
+ * and the block table the installation-and-use section, step 3.
+ *
+ *   rows_out       int64, device: [items, T, 64] with T = max_blocks (dense)
+ *                  or ceil(topk / 64) + ceil(topk2 / 64) (sparse); entry
+ *                  (i, t, r) is the offset read for row r of tile t of item i
+ *                  (auxiliary-cache rows as offsets from kvcache too).  FP8
+ *                  adds a second plane [items, T, 64] after the first: the
+ *                  row whose float32 scales the copy reads.  Entries of tiles
+ *                  no run copies are not written (the caller fills them).
+ *   rows_out_elems capacity of rows_out in int64 values; too small:
+ *                  MLA_ERR_INVALID_ARGUMENT.
+ * The softmax scale is d_qk^-0.5; o, lse and workspace receive what phase 1
+ * of the decode writes.
  */
-int mla_debug_row_ids(const int32_t* block_table, int max_blocks,
-                      const int32_t* cache_seqlens, int batch, int s_q,
-                      const int32_t* indices, int topk, int64_t* out, void* stream);
+int mla_debug_copy_rows(const void* q, const void* kvcache, int64_t num_pages, int kv_format,
+                        const int32_t* block_table, int max_blocks, const int32_t* cache_seqlens,
+                        const int32_t* indices, int topk, const void* kvcache2, int64_t num_pages2,
+                        const int32_t* block_table2, int max_blocks2,
+                        const int32_t* cache_seqlens2, const int32_t* indices2, int topk2,
+                        int batch, int s_q, int h_q, int h_kv, int d_qk, int causal,
+                        const int32_t* plan, const int32_t* num_splits, int num_workers, void* o,
+                        float* lse, void* workspace, size_t workspace_bytes, int64_t* rows_out,
+                        int64_t rows_out_elems, void* stream);
 
 /*
  * mla_validate_inputs — opt-in device-side check of the index data the host

@@ -24,7 +24,7 @@ EXPORTS = (
     "mla_status_string", "mla_plan_dims", "mla_plan_num_workers", "mla_get_metadata",
     "mla_workspace_bytes",
     "mla_decode_with_kvcache", "mla_decode_with_kvcache_phase", "mla_decode_with_kvcache_fp8",
-    "mla_decode_with_kvcache_fp8_phase", "mla_decode_with_kvcache_dual", "mla_debug_row_ids",
+    "mla_decode_with_kvcache_fp8_phase", "mla_decode_with_kvcache_dual", "mla_debug_copy_rows",
     "mla_validate_inputs",
 )
 
@@ -58,7 +58,11 @@ _SIGS = {
         _vp, _c_i64, _vp, _c_int, _vp, _vp, _c_int,
         _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
         _vp, _vp, _c_int, ctypes.c_float, _vp, _vp, _vp, ctypes.c_size_t, _c_int, _vp]),
-    "mla_debug_row_ids": (_c_int, [_vp, _c_int, _vp, _c_int, _c_int, _vp, _c_int, _vp, _vp]),
+    "mla_debug_copy_rows": (_c_int, [
+        _vp, _vp, _c_i64, _c_int, _vp, _c_int, _vp, _vp, _c_int,
+        _vp, _c_i64, _vp, _c_int, _vp, _vp, _c_int,
+        _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+        _vp, _vp, _c_int, _vp, _vp, _vp, ctypes.c_size_t, _vp, _c_i64, _vp]),
     "mla_validate_inputs": (_c_int, [_vp, _c_int, _vp, _c_int, _c_int, _vp, _c_int, _c_i64, _vp, _vp]),
 }
 

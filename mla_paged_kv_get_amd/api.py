@@ -169,22 +169,40 @@ def mla_decode_with_kvcache(q: torch.Tensor, kvcache: torch.Tensor, block_table:
     return o, lse
 
 
-def debug_row_ids(block_table: torch.Tensor, cache_seqlens: torch.Tensor,
-                  indices: torch.Tensor | None = None, s_q: int = 1) -> torch.Tensor:
-    """Physical cache row of every key, as the decode kernels address it (int64, -1 = no key)."""
-    _i32(block_table, "block_table")
-    _i32(cache_seqlens, "cache_seqlens")
-    B, mb = block_table.shape
-    if indices is None:
-        out = torch.empty((B, mb * PAGE), dtype=torch.int64, device=block_table.device)
-        topk = 0
-    else:
-        _i32(indices, "indices")
-        s_q, topk = indices.shape[1], indices.shape[2]
-        out = torch.empty(tuple(indices.shape), dtype=torch.int64, device=block_table.device)
-    _lib.check(_lib.lib().mla_debug_row_ids(_ptr(block_table), mb, _ptr(cache_seqlens), B, s_q,
-                                            _ptr(indices), topk, _ptr(out), _stream(block_table.device)),
-               "mla_debug_row_ids")
+def debug_copy_rows(q: torch.Tensor, kvcache: torch.Tensor, block_table: torch.Tensor,
+                    cache_seqlens: torch.Tensor, tile_scheduler_metadata: torch.Tensor,
+                    num_splits: torch.Tensor, causal: bool = False, indices: torch.Tensor | None = None,
+                    aux: tuple | None = None) -> torch.Tensor:
+    """Indexing probe: run the split decode kernel and return, for every cache
+    row its tile copies read, the byte offset of that row from ``kvcache``
+    (int64 ``[planes, items, tiles, 64]``, -1 where no copy read; packed FP8
+    caches add a second plane: the row whose scales were read)."""
+    fp8 = kvcache.dtype == torch.uint8
+    B, s_q, h_q, d = q.shape
+    num_pages, _, h_kv, _ = kvcache.shape
+    topk = 0 if indices is None else indices.shape[2]
+    topk2 = 0 if aux is None else aux[3].shape[2]
+    num_q_rows = s_q * h_q // h_kv
+    W = int(_lib.lib().mla_plan_num_workers(tile_scheduler_metadata.numel(), B, s_q, num_q_rows, h_kv, topk))
+    _need(W >= 1, "tile_scheduler_metadata does not match this call's shape")
+    items = B * h_kv * (s_q if topk else 1)
+    tiles = (-(-topk // 64) + -(-topk2 // 64)) if topk else block_table.shape[1]
+    planes = 2 if fp8 else 1
+    out = torch.full((planes, items, tiles, 64), -1, dtype=torch.int64, device=q.device)
+    o = torch.empty((B, s_q, h_q, D_V), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((B, s_q, h_q), dtype=torch.float32, device=q.device)
+    need = workspace_bytes(B, s_q, num_q_rows, h_kv, topk, D_V, W)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    kv2 = bt2 = sl2 = idx2 = None
+    if aux is not None:
+        kv2, bt2, sl2, idx2 = aux
+    _lib.check(_lib.lib().mla_debug_copy_rows(
+        _ptr(q), _ptr(kvcache), num_pages, 1 if fp8 else 0, _ptr(block_table), block_table.shape[1],
+        _ptr(cache_seqlens), _ptr(indices), topk, _ptr(kv2), kv2.shape[0] if kv2 is not None else 0,
+        _ptr(bt2), bt2.shape[1] if bt2 is not None else 0, _ptr(sl2),
+        _ptr(idx2) if topk2 > 0 else None, topk2, B, s_q, h_q, h_kv, 576 if fp8 else d, int(bool(causal)),
+        _ptr(tile_scheduler_metadata), _ptr(num_splits), W, _ptr(o), _ptr(lse), _ptr(ws),
+        ws.numel(), _ptr(out), out.numel(), _stream(q.device)), "mla_debug_copy_rows")
     return out
 
 

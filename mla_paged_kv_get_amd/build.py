@@ -21,17 +21,21 @@ LIB_PATH = os.path.join(HERE, LIB_NAME)
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 CFLAGS = [
-    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+    "-O3", "-std=c++20", "-fPIC", f"--offload-arch={ARCH}",
     # packed fp32 VALU forms are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # MFMA accumulators in VGPRs: the register allocator then keeps the wide
-    # decode's output accumulators in place across the tile loop (in AGPRs it
-    # copied all 128 of them to VGPRs and back on every tile) and parks the
-    # query fragments, which only MFMAs read, in AGPRs
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
     "-Wall", "-Wno-unused-function",
 ]
+# Per-source flags.  mla_decode.hip (the 16- and 64-row decode variants):
+# MFMA accumulators in VGPRs; the register allocator then keeps the 64-row
+# variant's output accumulators in place across the tile loop (in AGPRs it
+# copied all 128 of them to VGPRs and back on every tile) and parks the query
+# fragments, which only MFMAs read, in AGPRs.  mla_decode_rows128.hip keeps the
+# default AGPR accumulators: its 256 output accumulators per lane fill the AGPRs.
+FILE_FLAGS = {
+    "mla_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def _run(cmd):
@@ -49,7 +53,8 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
     objs = [os.path.join(objdir, os.path.basename(s)[:-4] + ".o") for s in srcs]
-    cmds = [[HIPCC, *CFLAGS, "-c", s, "-o", o] for s, o in zip(srcs, objs)]
+    cmds = [[HIPCC, *CFLAGS, *FILE_FLAGS.get(os.path.basename(s), []), "-c", s, "-o", o]
+            for s, o in zip(srcs, objs)]
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         for cmd, err in zip(cmds, ex.map(_run, cmds)):
             if verbose and err.strip():

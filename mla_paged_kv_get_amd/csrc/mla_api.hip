@@ -39,7 +39,11 @@ struct Shape {
   int m_tiles;      // workgroups per worker
 };
 
-int shape_of(int batch, int s_q, int num_q_rows, int h_kv, int topk, Shape* s) {
+// kv_format selects the decode variant (0: bf16 rows; 1: packed FP8 rows).
+// Plans are sized for bf16 rows: an FP8 decode may run more workgroups per
+// worker than the plan's W assumed (its row tiles are narrower), which only
+// lengthens the grid.
+int shape_of(int batch, int s_q, int num_q_rows, int h_kv, int topk, Shape* s, int kv_format = 0) {
   if (batch < 0 || s_q < 1 || num_q_rows < 1 || h_kv < 1) return MLA_ERR_INVALID_ARGUMENT;
   // Items: (sequence, KV head) in dense mode, (query token, KV head) in sparse mode.
   if (topk > 0) {
@@ -54,7 +58,7 @@ int shape_of(int batch, int s_q, int num_q_rows, int h_kv, int topk, Shape* s) {
     s->items = (int)items;
     s->rows = num_q_rows;
   }
-  s->variant = pick_variant(s->rows);
+  s->variant = pick_variant(s->rows, kv_format);
   const int vr = variant_rows(s->variant);
   s->m_tiles = (s->rows + vr - 1) / vr;
   return MLA_OK;
@@ -80,8 +84,9 @@ size_t workspace_for(const Shape& s, int dv, int W) {
 }
 
 // Arrival counters of the single-launch mode, after the plan's rows: one per
-// item and row tile.
-int64_t plan_counters(const Shape& s) { return (int64_t)s.items * s.m_tiles; }
+// item and row tile of the narrowest variant (so that a decode of either cache
+// format indexes inside them).
+int64_t plan_counters(const Shape& s) { return (int64_t)s.items * counter_tiles(s.rows); }
 
 }  // namespace
 
@@ -182,7 +187,7 @@ int decode_impl(const void* q, const void* kvcache, int64_t num_pages, int page_
                 const int32_t* num_splits, int num_workers, int causal, float softmax_scale,
                 const int32_t* indices, int topk, void* o, float* lse, void* workspace,
                 size_t workspace_bytes, int kv_format, const AuxCache* aux, int phases,
-                void* stream) {
+                void* stream, int64_t* dbg_rows = nullptr, int64_t dbg_elems = 0) {
   if (phases < 1 || phases > 4) return MLA_ERR_INVALID_ARGUMENT;
   if (batch < 0 || s_q < 1 || h_q < 1 || h_kv < 1 || max_blocks < 1 || num_pages < 1)
     return MLA_ERR_INVALID_ARGUMENT;
@@ -211,14 +216,28 @@ int decode_impl(const void* q, const void* kvcache, int64_t num_pages, int page_
   if (num_pages > ((int64_t)1 << 31) / kPage) return MLA_ERR_UNSUPPORTED;
   Shape s;
   const int num_q_rows = s_q * h_q / h_kv;
-  int st = shape_of(batch, s_q, num_q_rows, h_kv, topk, &s);
+  int st = shape_of(batch, s_q, num_q_rows, h_kv, topk, &s, kv_format);
   if (st != MLA_OK) return st;
   const size_t need = workspace_for(s, dv, num_workers);
   if (workspace_bytes < need) return MLA_ERR_WORKSPACE_TOO_SMALL;
   if (!workspace) return MLA_ERR_INVALID_ARGUMENT;
+  // Probe: one int64 per (item, tile, row) of every tile an item can have (and
+  // a second plane for the scale rows of packed FP8 tiles).
+  const int nb_sparse = topk > 0 ? (topk + kPage - 1) / kPage +
+                                       (aux && aux->topk > 0 ? (aux->topk + kPage - 1) / kPage : 0)
+                                 : 0;
+  const int dbg_tiles = topk > 0 ? nb_sparse : max_blocks;
+  const int64_t dbg_plane = (int64_t)s.items * dbg_tiles * kPage;
+  if (dbg_rows) {
+    if (phases == 2 || phases == 4) return MLA_ERR_INVALID_ARGUMENT;
+    if (dbg_elems < dbg_plane * (kv_format == 1 ? 2 : 1)) return MLA_ERR_INVALID_ARGUMENT;
+  }
   if (batch == 0) return MLA_OK;
 
   DecodeArgs a;
+  a.dbg_rows = dbg_rows;
+  a.dbg_tiles = dbg_tiles;
+  a.dbg_plane = dbg_plane;
   a.q = static_cast<const uint16_t*>(q);
   a.kv = static_cast<const uint16_t*>(kvcache);
   a.block_table = block_table;
@@ -253,7 +272,7 @@ int decode_impl(const void* q, const void* kvcache, int64_t num_pages, int page_
   a.kv_format = kv_format;
   a.d_qk = d_qk;
   a.nb1 = topk > 0 ? (topk + kPage - 1) / kPage : 0;
-  a.nb_sparse = a.nb1;
+  a.nb_sparse = nb_sparse;
   a.kv2 = nullptr;
   a.block_table2 = nullptr;
   a.seqlens2 = nullptr;
@@ -267,7 +286,6 @@ int decode_impl(const void* q, const void* kvcache, int64_t num_pages, int page_
     a.indices2 = aux->indices;
     a.max_blocks2 = aux->max_blocks;
     a.topk2 = aux->topk;
-    a.nb_sparse += (aux->topk + kPage - 1) / kPage;
   }
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   if (phases == 4) {
@@ -361,16 +379,22 @@ int mla_decode_with_kvcache_dual(const void* q, const void* kvcache, int64_t num
                      phases, stream);
 }
 
-int mla_debug_row_ids(const int32_t* block_table, int max_blocks, const int32_t* cache_seqlens,
-                      int batch, int s_q, const int32_t* indices, int topk, int64_t* out,
-                      void* stream) {
-  if (!block_table || !cache_seqlens || !out || max_blocks < 1 || batch < 0 || s_q < 1)
-    return MLA_ERR_INVALID_ARGUMENT;
-  if ((indices != nullptr) != (topk > 0)) return MLA_ERR_INVALID_ARGUMENT;
-  if (batch == 0) return MLA_OK;
-  const hipError_t e = launch_row_ids(block_table, max_blocks, cache_seqlens, batch, s_q, indices,
-                                      topk, out, reinterpret_cast<hipStream_t>(stream));
-  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+int mla_debug_copy_rows(const void* q, const void* kvcache, int64_t num_pages, int kv_format,
+                        const int32_t* block_table, int max_blocks, const int32_t* cache_seqlens,
+                        const int32_t* indices, int topk, const void* kvcache2, int64_t num_pages2,
+                        const int32_t* block_table2, int max_blocks2,
+                        const int32_t* cache_seqlens2, const int32_t* indices2, int topk2,
+                        int batch, int s_q, int h_q, int h_kv, int d_qk, int causal,
+                        const int32_t* plan, const int32_t* num_splits, int num_workers, void* o,
+                        float* lse, void* workspace, size_t workspace_bytes, int64_t* rows_out,
+                        int64_t rows_out_elems, void* stream) {
+  if (!rows_out || (kv_format != 0 && kv_format != 1)) return MLA_ERR_INVALID_ARGUMENT;
+  if (kvcache2 && (kv_format != 0 || topk <= 0)) return MLA_ERR_INVALID_ARGUMENT;
+  const AuxCache aux{kvcache2, num_pages2, block_table2, max_blocks2, cache_seqlens2, indices2, topk2};
+  return decode_impl(q, kvcache, num_pages, kPage, block_table, max_blocks, cache_seqlens, batch, s_q,
+                     h_q, h_kv, d_qk, kDv, plan, num_splits, num_workers, causal,
+                     1.f / sqrtf((float)d_qk), indices, topk, o, lse, workspace, workspace_bytes,
+                     kv_format, kvcache2 ? &aux : nullptr, 1, stream, rows_out, rows_out_elems);
 }
 
 int mla_validate_inputs(const int32_t* block_table, int max_blocks, const int32_t* cache_seqlens,

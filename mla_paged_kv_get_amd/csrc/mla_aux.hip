@@ -1,42 +1,10 @@
-// Indexing probe and input validation kernels.
-//
-// The probe writes the physical cache row of every key through cache_row(),
-// the same device function the decode kernels address the cache with, so a
-// bit-exact comparison with the page-table definition checks the kernels'
-// addressing ("What is FlashMLA", topnet.top: 64-token pages reached through
-// block_table).
+// Input validation kernels: every block-table entry a key can reach must name
+// a page of the pool ("What is FlashMLA", topnet.top: 64-token pages reached
+// through block_table), and every length must fit the block table.
 #include "mla_common.h"
 
 namespace mla {
 namespace {
-
-__global__ void row_ids_dense(const int32_t* __restrict__ bt, int max_blocks,
-                              const int32_t* __restrict__ seqlens, int batch,
-                              int64_t* __restrict__ out) {
-  const int64_t per = (int64_t)max_blocks * kPage;
-  const int64_t n = per * batch;
-  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n;
-       e += (int64_t)gridDim.x * blockDim.x) {
-    const int b = (int)(e / per);
-    const int j = (int)(e % per);
-    const int L = seqlens[b];
-    out[e] = j < L ? cache_row(bt + (int64_t)b * max_blocks, j) : -1;
-  }
-}
-
-__global__ void row_ids_sparse(const int32_t* __restrict__ bt, int max_blocks,
-                               const int32_t* __restrict__ seqlens, int batch, int s_q,
-                               const int32_t* __restrict__ indices, int topk,
-                               int64_t* __restrict__ out) {
-  const int64_t n = (int64_t)batch * s_q * topk;
-  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n;
-       e += (int64_t)gridDim.x * blockDim.x) {
-    const int b = (int)(e / ((int64_t)s_q * topk));
-    const int idx = indices[e];
-    const int L = seqlens[b];
-    out[e] = sparse_key_valid(idx, L) ? cache_row(bt + (int64_t)b * max_blocks, idx) : -1;
-  }
-}
 
 __global__ void zero_i32(int32_t* p) { if (threadIdx.x == 0 && blockIdx.x == 0) p[0] = 0; }
 
@@ -85,21 +53,6 @@ int grid_for(int64_t n) {
 }
 
 }  // namespace
-
-hipError_t launch_row_ids(const int32_t* block_table, int max_blocks, const int32_t* seqlens,
-                          int batch, int s_q, const int32_t* indices, int topk, int64_t* out,
-                          hipStream_t stream) {
-  if (indices == nullptr) {
-    const int64_t n = (int64_t)batch * max_blocks * kPage;
-    hipLaunchKernelGGL(row_ids_dense, dim3(grid_for(n)), dim3(256), 0, stream, block_table,
-                       max_blocks, seqlens, batch, out);
-  } else {
-    const int64_t n = (int64_t)batch * s_q * topk;
-    hipLaunchKernelGGL(row_ids_sparse, dim3(grid_for(n)), dim3(256), 0, stream, block_table,
-                       max_blocks, seqlens, batch, s_q, indices, topk, out);
-  }
-  return hipGetLastError();
-}
 
 hipError_t launch_validate(const int32_t* block_table, int max_blocks, const int32_t* seqlens,
                            int batch, int s_q, const int32_t* indices, int topk,

@@ -31,13 +31,6 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 #define MLA_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 #define MLA_GBL(p) ((const __attribute__((address_space(1))) void*)(p))
 
-// Physical cache row of logical key position `pos` of a sequence whose block
-// table row is `bt_row` (page = bt_row[pos / 64], slot = pos % 64).  The decode
-// kernels and the indexing probe both address the cache through this function.
-__device__ __forceinline__ int64_t cache_row(const int32_t* __restrict__ bt_row, int pos) {
-  return (int64_t)bt_row[pos >> 6] * kPage + (pos & (kPage - 1));
-}
-
 // Whether an index-list entry is a key of a sequence of length L.
 __device__ __forceinline__ bool sparse_key_valid(int idx, int L) {
   return idx >= 0 && idx < L;
@@ -93,6 +86,14 @@ struct DecodeArgs {
   // else h_kv) and by h_kv, by multiplication: mul = floor((2^32 - 1) / div)
   // (set on the host; see div_by).
   unsigned seq_div, seq_mul, head_mul;
+  // Indexing probe (null in normal calls): the kernel also writes, for every
+  // row it copies, the byte offset from kv of the cache row the copy reads:
+  // dbg_rows[(item * dbg_tiles + tile) * 64 + row of the tile]; packed FP8
+  // rows add the row whose scales the copy reads at dbg_rows[dbg_plane + same
+  // index].  Entries of tiles no run copies are left as they were.
+  int64_t* dbg_rows;
+  int dbg_tiles;
+  int64_t dbg_plane;
 };
 
 // floor(n / d) for 0 <= n < 2^31 from m = floor((2^32 - 1) / d): the high
@@ -124,9 +125,6 @@ hipError_t launch_plan(const int32_t* seqlens, int topk, int num_items, int item
                        int num_counters, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int variant, hipStream_t stream);
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream);
-hipError_t launch_row_ids(const int32_t* block_table, int max_blocks, const int32_t* seqlens,
-                          int batch, int s_q, const int32_t* indices, int topk, int64_t* out,
-                          hipStream_t stream);
 hipError_t launch_validate(const int32_t* block_table, int max_blocks, const int32_t* seqlens,
                            int batch, int s_q, const int32_t* indices, int topk,
                            int64_t num_pages, int32_t* error_count, hipStream_t stream);
@@ -134,13 +132,24 @@ hipError_t launch_validate(const int32_t* block_table, int max_blocks, const int
 // Decode variants: how a workgroup covers an item's query rows.
 enum Variant : int {
   kVariantRows16 = 0,    // <= 16 rows: 4 waves split each 64-token tile 4 ways
-  kVariantRows64 = 1,    // > 16 rows: 64-row tiles, two wave pairs of 32 rows
+  kVariantRows64 = 1,    // 17..64 rows (and packed FP8 caches above 16): 64-row
+                         // tiles, two wave pairs of 32 rows
+  kVariantRows128 = 2,   // > 64 rows, bf16 caches: 128-row tiles, each wave 32
+                         // rows over every key and output column
 };
-constexpr int variant_rows(int v) { return v == kVariantRows16 ? 16 : 64; }
+constexpr int variant_rows(int v) { return v == kVariantRows16 ? 16 : v == kVariantRows64 ? 64 : 128; }
 // Plan cost of starting an item, in blocks (measured: an item boundary costs
 // about 1.6 tiles of a 16-row worker; for 64-row items 4 balanced MTP decode
-// best among 1 to 4).
-constexpr int variant_overhead(int v) { return v == kVariantRows16 ? 1 : 4; }
-inline int pick_variant(int rows_per_item) { return rows_per_item <= 16 ? kVariantRows16 : kVariantRows64; }
+// best among 1 to 4; 128-row items load their next query rows during the
+// last tile's PV).
+constexpr int variant_overhead(int v) { return v == kVariantRows16 ? 1 : v == kVariantRows64 ? 4 : 2; }
+// kv_format 0: bf16 rows; 1: packed FP8 rows (no 128-row variant).
+inline int pick_variant(int rows_per_item, int kv_format) {
+  if (rows_per_item <= 16) return kVariantRows16;
+  return (kv_format == 1 || rows_per_item <= 64) ? kVariantRows64 : kVariantRows128;
+}
+// Arrival counters per item of the single-launch decode: one per row tile of
+// the narrowest variant the row count can run with (any cache format).
+inline int counter_tiles(int rows_per_item) { return rows_per_item <= 16 ? 1 : (rows_per_item + 63) / 64; }
 
 }  // namespace mla

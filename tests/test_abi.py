@@ -199,8 +199,21 @@ def test_metadata_item_cap():
 
 def test_debug_and_validate_reject():
     l = _lib.lib()
-    assert l.mla_debug_row_ids(None, 4, DUMMY, 2, 1, None, 0, DUMMY, None) == _lib.MLA_ERR_INVALID_ARGUMENT
-    assert l.mla_debug_row_ids(DUMMY, 4, DUMMY, 2, 1, DUMMY, 0, DUMMY, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    probe = dict(q=DUMMY, kv=DUMMY, num_pages=10, fmt=0, bt=DUMMY, mb=4, sl=DUMMY, idx=None, topk=0,
+                 kv2=None, num_pages2=0, bt2=None, mb2=0, sl2=None, idx2=None, topk2=0, batch=2, s_q=1,
+                 h_q=16, h_kv=1, d=576, causal=0, plan=DUMMY, ns=DUMMY, W=8, o=DUMMY, lse=DUMMY,
+                 ws=DUMMY, ws_bytes=1 << 40, out=DUMMY, out_elems=2 * 4 * 64, stream=None)
+
+    def copy_rows(**kw):
+        a = dict(probe)
+        a.update(kw)
+        return l.mla_debug_copy_rows(*a.values())
+    assert copy_rows(out=None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert copy_rows(out_elems=2 * 4 * 64 - 1) == _lib.MLA_ERR_INVALID_ARGUMENT       # [items, max_blocks, 64]
+    assert copy_rows(fmt=1, out_elems=2 * 4 * 64) == _lib.MLA_ERR_INVALID_ARGUMENT    # FP8: two planes
+    assert copy_rows(fmt=2) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert copy_rows(kv2=DUMMY) == _lib.MLA_ERR_INVALID_ARGUMENT                      # dual cache is sparse
+    assert copy_rows(d=448) == _lib.MLA_ERR_UNSUPPORTED
     assert l.mla_validate_inputs(DUMMY, 4, DUMMY, 2, 1, None, 0, 10, None, None) == _lib.MLA_ERR_INVALID_ARGUMENT
     assert l.mla_validate_inputs(DUMMY, 4, DUMMY, 2, 1, None, 0, 0, DUMMY, None) == _lib.MLA_ERR_INVALID_ARGUMENT
 

@@ -66,10 +66,11 @@ def test_fp8_sparse_pads(h_q):
     assert np.isneginf(lg[1, 1]).all() and np.isneginf(lg[2]).all()
 
 
-def test_fp8_sparse_topk_sampled():
-    w = wl.sparse_topk_fp8(B=4)
+def test_fp8_sparse_topk_full():
+    # the whole packed-FP8 sparse top-k workload (b=16, s_q=8, h_q=128, k=2048)
+    w = wl.sparse_topk_fp8()
     o, lse, _ = run_gpu(Dev(w))
-    compare(w, o, lse, items=[(0, 0), (1, 7), (3, 3)], label="fp8 sparse-topk")
+    compare(w, o, lse, label="fp8 sparse-topk")
 
 
 @pytest.mark.parametrize("h_q", [16, 128])

@@ -55,10 +55,12 @@ def _cases():
                                  poison=True, kv_format="fp8"), 21),
         ("grouped-d512", lambda: wl.build("g512", 94, np.array([2000, 65, 0, 999]), B=4, s_q=1, h_q=64,
                                           h_kv=2, num_pages=60, poison=True, d_qk=512), 19),
+        ("wide-splits", lambda: wl.build("wsplits", 97, np.array([4096, 1, 2000, 777, 64, 65, 0]), B=7,
+                                         s_q=1, h_q=128, num_pages=200, poison=True), 37),
     ]
 
 
-@pytest.mark.parametrize("case", range(6))
+@pytest.mark.parametrize("case", range(7))
 def test_single_launch_equals_two_launches(case):
     name, make, W = _cases()[case]
     w = make()
