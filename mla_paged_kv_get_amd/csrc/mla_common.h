@@ -139,10 +139,10 @@ enum Variant : int {
 };
 constexpr int variant_rows(int v) { return v == kVariantRows16 ? 16 : v == kVariantRows64 ? 64 : 128; }
 // Plan cost of starting an item, in blocks (measured: an item boundary costs
-// about 1.6 tiles of a 16-row worker; for 64-row items 4 balanced MTP decode
-// best among 1 to 4; 128-row items load their next query rows during the
-// last tile's PV).
-constexpr int variant_overhead(int v) { return v == kVariantRows16 ? 1 : v == kVariantRows64 ? 4 : 2; }
+// about 1.6 tiles of a 16-row worker; for 64-row and 128-row items 4 balanced
+// the MTP decode best among the values tried, 1 to 8, while the wide
+// one-token decodes lost under 3% against 2).
+constexpr int variant_overhead(int v) { return v == kVariantRows16 ? 1 : 4; }
 // kv_format 0: bf16 rows; 1: packed FP8 rows (no 128-row variant).
 inline int pick_variant(int rows_per_item, int kv_format) {
   if (rows_per_item <= 16) return kVariantRows16;

@@ -1017,9 +1017,12 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
       return (int64_t)tok_or_b * (sparse ? a.h_q : a.s_q * a.h_q) + kvg * a.G;
     };
     auto load_q = [&](int item) __attribute__((always_inline)) {
-      const char* qbase = uniform_ptr(reinterpret_cast<const char*>(a.q + q_item(item) * D));
-      const char* qrow_b = qbase + (unsigned)(q_lane * D * 2);
-      const uint16_t* qrow = reinterpret_cast<const uint16_t*>(qrow_b);
+      // global (not generic) pointers: a generic load would also count against
+      // the LDS counter and hold up the waits for LDS reads behind it
+      typedef const __attribute__((address_space(1))) char gchar;
+      typedef const __attribute__((address_space(1))) bf16x8 gbf16x8;
+      gchar* qbase = (gchar*)uniform_ptr(reinterpret_cast<const char*>(a.q + q_item(item) * D));
+      gchar* qrow = qbase + (unsigned)(q_lane * D * 2);
 #pragma unroll
       for (int ks = 0; ks < C::kQf; ++ks) {
         // FP8: the latent k-steps take the values in the order the K reads
@@ -1028,7 +1031,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
         // + 7), so that each lane reads 16 codes at once
         const int d0 = kWide ? (KV8 && ks < 32 ? 32 * (ks >> 1) + 16 * hl + 8 * (ks & 1) : 16 * ks + 8 * hl)
                              : (KV8 && ks < 16 ? 64 * (ks >> 1) + 16 * g + 8 * (ks & 1) : 32 * ks + 8 * g);
-        qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + d0);
+        qf[ks] = *reinterpret_cast<gbf16x8*>(qrow + 2 * d0);
       }
     };
     // Rows16, dense: the query rows of an item that starts mid-run come in
@@ -1180,7 +1183,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
             // FP8: each latent block (k-steps 8 b .. 8 b + 7) accumulates on
             // its own; the RoPE k-steps go into sacc
             if constexpr (KV8) {
-              if (ks < 32) sblk[ks >> 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur, qf[ks], sblk[ks >> 3], 0, 0, 0);
+              if constexpr (ks < 32) sblk[ks >> 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur, qf[ks], sblk[ks >> 3], 0, 0, 0);
               else sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur, qf[ks], sacc, 0, 0, 0);
             } else {
               sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur, qf[ks], sacc, 0, 0, 0);
@@ -1454,10 +1457,10 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     // the softmax of the wave's own rows, which needs no other wave (each lane
     // holds 16 keys of each block for its row, its partner lane ^ 32 the other
     // 16); then O^T += V^T P^T over 4 k-steps of 16 keys and the 16 column
-    // blocks of 32.  The copy of the next tile (dma_stage, `off`) is issued one
-    // instruction every fourth QK^T MFMA; mid() does the index work for later
-    // tiles between MFMAs, and after_qk() runs once the query fragments are no
-    // longer needed for this tile.
+    // blocks of 32.  mid() does the index work for later tiles right after
+    // the first MFMA; the copy of the next tile (dma_stage, `off`) follows, one
+    // instruction every third QK^T MFMA; after_qk() runs once the query
+    // fragments are no longer needed for this tile.
     auto compute_full = [&](const char* stage, const unsigned char* vslot, int blk, int lim,
                             char* dma_stage, auto&& mid, auto&& after_qk, bool first) __attribute__((always_inline)) {
       if constexpr (kFull) {
@@ -1468,7 +1471,11 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
         // them is needed beside the output accumulators.
         constexpr int kN = 2 * C::kQf;
         constexpr int kPre = 4;             // K fragments read ahead
-        static_assert(4 * C::kLoads <= kN, "the copies must fit the QK^T MFMAs");
+        // The copies of the next tile go out one every third MFMA from MFMA
+        // kCopy0 on; the index work for later tiles (mid) comes first, so that
+        // a wait it may contain never waits for this tile's copies.
+        constexpr int kCopy0 = 16;
+        static_assert(kCopy0 + 3 * (C::kLoads - 1) < kN, "the copies must fit the QK^T MFMAs");
         auto kread = [&](int n) __attribute__((always_inline)) -> bf16x8 {
           const int ks = n % C::kQf, kb = n / C::kQf;
           return *reinterpret_cast<const bf16x8*>(stage + k_base + kb * ((4 * C::kCG) << 10) +
@@ -1483,9 +1490,10 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
             if constexpr (n + kPre < kN) kf[n % kPre] = kread(n + kPre);
             if constexpr (n % C::kQf == 0) sacc[n / C::kQf] = mfma_v0(kc, qf[0]);
             else mfma_v(sacc[n / C::kQf], kc, qf[n % C::kQf]);
-            if constexpr (decltype(with_dma)::value && n % 4 == 0 && n / 4 < C::kLoads)
-              issue_one(dma_stage, off, std::integral_constant<int, n / 4>{});
-            if constexpr (n == 16) mid();
+            if constexpr (n == 1) mid();
+            if constexpr (decltype(with_dma)::value && n >= kCopy0 && (n - kCopy0) % 3 == 0 &&
+                          (n - kCopy0) / 3 < C::kLoads)
+              issue_one(dma_stage, off, std::integral_constant<int, (n - kCopy0) / 3>{});
             __builtin_amdgcn_sched_barrier(0);   // keep the reads kPre MFMAs ahead
           });
         };
