@@ -57,12 +57,14 @@ extern "C" {
 #define MLA_ERR_UNSUPPORTED 2        /* a shape this build does not implement */
 #define MLA_ERR_WORKSPACE_TOO_SMALL 3
 #define MLA_ERR_HIP 4                /* a HIP runtime call or kernel launch failed */
+#define MLA_ERR_SCRATCH_LIMIT 5      /* beyond the no-alloc decode's fixed scratch */
 
 #define MLA_PAGE_SIZE 64
 #define MLA_D_QK 576
 #define MLA_D_V 512
 #define MLA_PLAN_WORDS 8             /* int32 words per plan row */
 #define MLA_PLAN_MAX_ITEMS 16384     /* items one metadata call can plan */
+#define MLA_NO_ALLOC_SCRATCH_BYTES ((size_t)128 << 20)   /* per GPU, see below */
 
 /* Human-readable text of a status code (static storage, never NULL). */
 const char* mla_status_string(int status);
@@ -197,6 +199,34 @@ int mla_decode_with_kvcache(const void* q, const void* kvcache, int64_t num_page
                             float softmax_scale, const int32_t* indices, int topk,
                             void* o, float* lse, void* workspace,
                             size_t workspace_bytes, void* stream);
+
+/*
+ * mla_decode_with_kvcache_no_alloc — mla_decode_with_kvcache for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  It takes no workspace: the split
+ * partials go to a buffer of MLA_NO_ALLOC_SCRATCH_BYTES (128 MiB) that the
+ * library holds in a file-scope device array, one copy on every GPU it runs
+ * on, kept until the process ends.  The call allocates nothing (no hipMalloc,
+ * hipFree or allocating library routine); the first call that launches work on
+ * a device looks up that device's copy (hipGetSymbolAddress), so a caller that
+ * captures graphs makes one such call first.  A call whose partials
+ * (mla_workspace_bytes of the same arguments) exceed the buffer returns
+ * MLA_ERR_SCRATCH_LIMIT and launches nothing; fewer workers in the plan need
+ * less.  Nothing in the buffer has to start at zero: every partial the merge
+ * reads is written by the split kernel of the same call, so the contents left
+ * by an earlier call never reach a result.  All calls on one GPU share its
+ * buffer: no-alloc calls that overlap on one GPU (other streams, other host
+ * threads) race and must be ordered by the caller.  bf16 caches, dense or
+ * sparse; every other argument, check and status is that of
+ * mla_decode_with_kvcache (two launches).
+ */
+int mla_decode_with_kvcache_no_alloc(const void* q, const void* kvcache, int64_t num_pages,
+                                     int page_size, const int32_t* block_table, int max_blocks,
+                                     const int32_t* cache_seqlens, int batch, int s_q, int h_q,
+                                     int h_kv, int d_qk, int dv, const int32_t* plan,
+                                     const int32_t* num_splits, int num_workers, int causal,
+                                     float softmax_scale, const int32_t* indices, int topk,
+                                     void* o, float* lse, void* stream);
 
 /*
  * mla_decode_with_kvcache_phase — the same decode in two separately launched

@@ -19,11 +19,14 @@ MLA_ERR_INVALID_ARGUMENT = 1
 MLA_ERR_UNSUPPORTED = 2
 MLA_ERR_WORKSPACE_TOO_SMALL = 3
 MLA_ERR_HIP = 4
+MLA_ERR_SCRATCH_LIMIT = 5
+NO_ALLOC_SCRATCH_BYTES = 128 << 20     # MLA_NO_ALLOC_SCRATCH_BYTES
 
 EXPORTS = (
     "mla_status_string", "mla_plan_dims", "mla_plan_num_workers", "mla_get_metadata",
     "mla_workspace_bytes",
-    "mla_decode_with_kvcache", "mla_decode_with_kvcache_phase", "mla_decode_with_kvcache_fp8",
+    "mla_decode_with_kvcache", "mla_decode_with_kvcache_no_alloc", "mla_decode_with_kvcache_phase",
+    "mla_decode_with_kvcache_fp8",
     "mla_decode_with_kvcache_fp8_phase", "mla_decode_with_kvcache_dual", "mla_debug_copy_rows",
     "mla_validate_inputs",
 )
@@ -42,6 +45,9 @@ _SIGS = {
     "mla_decode_with_kvcache": (_c_int, [
         _vp, _vp, _c_i64, _c_int, _vp, _c_int, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
         _vp, _vp, _c_int, _c_int, ctypes.c_float, _vp, _c_int, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "mla_decode_with_kvcache_no_alloc": (_c_int, [
+        _vp, _vp, _c_i64, _c_int, _vp, _c_int, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+        _vp, _vp, _c_int, _c_int, ctypes.c_float, _vp, _c_int, _vp, _vp, _vp]),
     "mla_decode_with_kvcache_phase": (_c_int, [
         _vp, _vp, _c_i64, _c_int, _vp, _c_int, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
         _vp, _vp, _c_int, _c_int, ctypes.c_float, _vp, _c_int, _vp, _vp, _vp, ctypes.c_size_t,
@@ -93,6 +99,7 @@ def lib() -> ctypes.CDLL:
 
 def check(status: int, where: str) -> None:
     if status != MLA_OK:
-        if status in (MLA_ERR_INVALID_ARGUMENT, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE_TOO_SMALL):
+        if status in (MLA_ERR_INVALID_ARGUMENT, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE_TOO_SMALL,
+                      MLA_ERR_SCRATCH_LIMIT):
             raise ValueError(str(MLAError(status, where)))
         raise MLAError(status, where)

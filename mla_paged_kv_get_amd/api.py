@@ -80,26 +80,8 @@ def get_mla_metadata(cache_seqlens: torch.Tensor, num_q_rows: int, h_kv: int, *,
     return plan, num_splits
 
 
-def mla_decode_with_kvcache(q: torch.Tensor, kvcache: torch.Tensor, block_table: torch.Tensor,
-                            cache_seqlens: torch.Tensor, dv: int, tile_scheduler_metadata: torch.Tensor,
-                            num_splits: torch.Tensor, causal: bool = False,
-                            softmax_scale: float | None = None, indices: torch.Tensor | None = None,
-                            out: tuple | None = None, workspace: torch.Tensor | None = None,
-                            phases: int = 3, aux: tuple | None = None):
-    """Paged MLA decode; returns ``(o [b, s_q, h_q, dv] bf16, lse [b, s_q, h_q] fp32)``.
-
-    ``kvcache`` is bf16 ``[pages, 64, h_kv, 576]``, or uint8 ``[pages, 64, h_kv,
-    656]`` for packed FP8 rows (512 E4M3 latent codes, 4 float32 block scales,
-    64 bf16 RoPE values).  ``phases`` (1 = split kernel, 2 = merge kernel, 3 =
-    both) lets a caller launch the two kernels separately with the same
-    arguments and buffers; ``phases=4`` is the single-launch decode, whose
-    kernel merges split items itself, counting finished runs in counters that
-    the plan carries (zeroed by get_mla_metadata, left zero by every completed
-    call: single-launch calls that share a plan must not overlap).  ``aux = (kvcache2, block_table2, cache_seqlens2,
-    indices2)`` adds an auxiliary bf16 cache (sparse mode): each query token
-    attends to the union of its keys in both caches; the plan then comes from
-    ``get_mla_metadata(..., topk=topk, topk2=indices2.shape[2])``.
-    """
+def _decode_shape(q, kvcache, block_table, cache_seqlens, tile_scheduler_metadata, num_splits, indices):
+    """Checks the decode's tensors; returns their sizes and the plan's worker count."""
     _as_bits(q, "q")
     fp8 = kvcache.dtype == torch.uint8
     if fp8:
@@ -130,6 +112,31 @@ def mla_decode_with_kvcache(q: torch.Tensor, kvcache: torch.Tensor, block_table:
     W = int(_lib.lib().mla_plan_num_workers(tile_scheduler_metadata.numel(), B, s_q, num_q_rows,
                                              h_kv, topk))
     _need(W >= 1, "tile_scheduler_metadata does not match this call's shape")
+    return fp8, B, s_q, h_q, d, num_pages, page, h_kv, topk, num_q_rows, W
+
+
+def mla_decode_with_kvcache(q: torch.Tensor, kvcache: torch.Tensor, block_table: torch.Tensor,
+                            cache_seqlens: torch.Tensor, dv: int, tile_scheduler_metadata: torch.Tensor,
+                            num_splits: torch.Tensor, causal: bool = False,
+                            softmax_scale: float | None = None, indices: torch.Tensor | None = None,
+                            out: tuple | None = None, workspace: torch.Tensor | None = None,
+                            phases: int = 3, aux: tuple | None = None):
+    """Paged MLA decode; returns ``(o [b, s_q, h_q, dv] bf16, lse [b, s_q, h_q] fp32)``.
+
+    ``kvcache`` is bf16 ``[pages, 64, h_kv, 576]``, or uint8 ``[pages, 64, h_kv,
+    656]`` for packed FP8 rows (512 E4M3 latent codes, 4 float32 block scales,
+    64 bf16 RoPE values).  ``phases`` (1 = split kernel, 2 = merge kernel, 3 =
+    both) lets a caller launch the two kernels separately with the same
+    arguments and buffers; ``phases=4`` is the single-launch decode, whose
+    kernel merges split items itself, counting finished runs in counters that
+    the plan carries (zeroed by get_mla_metadata, left zero by every completed
+    call: single-launch calls that share a plan must not overlap).  ``aux = (kvcache2, block_table2, cache_seqlens2,
+    indices2)`` adds an auxiliary bf16 cache (sparse mode): each query token
+    attends to the union of its keys in both caches; the plan then comes from
+    ``get_mla_metadata(..., topk=topk, topk2=indices2.shape[2])``.
+    """
+    fp8, B, s_q, h_q, d, num_pages, page, h_kv, topk, num_q_rows, W = _decode_shape(
+        q, kvcache, block_table, cache_seqlens, tile_scheduler_metadata, num_splits, indices)
     scale = d ** -0.5 if softmax_scale is None else float(softmax_scale)
     dev = q.device
     if out is None:
@@ -166,6 +173,33 @@ def mla_decode_with_kvcache(q: torch.Tensor, kvcache: torch.Tensor, block_table:
         _ptr(num_splits), W, int(bool(causal)), ctypes.c_float(scale), _ptr(indices), topk,
         _ptr(o), _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
         int(phases), _stream(dev)), "mla_decode_with_kvcache")
+    return o, lse
+
+
+def mla_decode_with_kvcache_no_alloc(q: torch.Tensor, kvcache: torch.Tensor, block_table: torch.Tensor,
+                                     cache_seqlens: torch.Tensor, dv: int,
+                                     tile_scheduler_metadata: torch.Tensor, num_splits: torch.Tensor,
+                                     out: tuple, causal: bool = False,
+                                     softmax_scale: float | None = None,
+                                     indices: torch.Tensor | None = None):
+    """The decode without a workspace, writing into ``out = (o, lse)``.
+
+    Neither this function nor the library allocates device memory: the split
+    partials go to the library's fixed per-GPU scratch of
+    ``NO_ALLOC_SCRATCH_BYTES``; a call that needs more raises ``ValueError``
+    (fewer workers in the plan need less).  bf16 caches only.  No-alloc calls
+    that overlap on one GPU share that scratch and race.
+    """
+    _need(kvcache.dtype != torch.uint8, "the no-alloc decode takes bf16 caches")
+    fp8, B, s_q, h_q, d, num_pages, page, h_kv, topk, num_q_rows, W = _decode_shape(
+        q, kvcache, block_table, cache_seqlens, tile_scheduler_metadata, num_splits, indices)
+    o, lse = out
+    scale = d ** -0.5 if softmax_scale is None else float(softmax_scale)
+    _lib.check(_lib.lib().mla_decode_with_kvcache_no_alloc(
+        _ptr(q), _ptr(kvcache), num_pages, page, _ptr(block_table), block_table.shape[1],
+        _ptr(cache_seqlens), B, s_q, h_q, h_kv, d, dv, _ptr(tile_scheduler_metadata),
+        _ptr(num_splits), W, int(bool(causal)), ctypes.c_float(scale), _ptr(indices), topk,
+        _ptr(o), _ptr(lse), _stream(q.device)), "mla_decode_with_kvcache_no_alloc")
     return o, lse
 
 

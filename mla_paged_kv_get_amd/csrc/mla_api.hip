@@ -5,6 +5,9 @@
 
 #include <math.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "mla_common.h"
 
 namespace mla {
@@ -99,6 +102,7 @@ const char* mla_status_string(int status) {
     case MLA_ERR_UNSUPPORTED: return "unsupported shape (needs d_qk=576, dv=512, page 64)";
     case MLA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case MLA_ERR_HIP: return "HIP runtime error";
+    case MLA_ERR_SCRATCH_LIMIT: return "the call needs more scratch than the no-alloc decode's fixed buffer holds";
     default: return "unknown status";
   }
 }
@@ -187,7 +191,8 @@ int decode_impl(const void* q, const void* kvcache, int64_t num_pages, int page_
                 const int32_t* num_splits, int num_workers, int causal, float softmax_scale,
                 const int32_t* indices, int topk, void* o, float* lse, void* workspace,
                 size_t workspace_bytes, int kv_format, const AuxCache* aux, int phases,
-                void* stream, int64_t* dbg_rows = nullptr, int64_t dbg_elems = 0) {
+                void* stream, int64_t* dbg_rows = nullptr, int64_t dbg_elems = 0,
+                int (*fixed_scratch)(void**) = nullptr) {
   if (phases < 1 || phases > 4) return MLA_ERR_INVALID_ARGUMENT;
   if (batch < 0 || s_q < 1 || h_q < 1 || h_kv < 1 || max_blocks < 1 || num_pages < 1)
     return MLA_ERR_INVALID_ARGUMENT;
@@ -219,8 +224,10 @@ int decode_impl(const void* q, const void* kvcache, int64_t num_pages, int page_
   int st = shape_of(batch, s_q, num_q_rows, h_kv, topk, &s, kv_format);
   if (st != MLA_OK) return st;
   const size_t need = workspace_for(s, dv, num_workers);
-  if (workspace_bytes < need) return MLA_ERR_WORKSPACE_TOO_SMALL;
-  if (!workspace) return MLA_ERR_INVALID_ARGUMENT;
+  // fixed_scratch: the no-alloc decode, whose buffer (workspace_bytes long) is
+  // only looked up once every argument has been checked and there is work.
+  if (workspace_bytes < need) return fixed_scratch ? MLA_ERR_SCRATCH_LIMIT : MLA_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace && !fixed_scratch) return MLA_ERR_INVALID_ARGUMENT;
   // Probe: one int64 per (item, tile, row) of every tile an item can have (and
   // a second plane for the scale rows of packed FP8 tiles).
   const int nb_sparse = topk > 0 ? (topk + kPage - 1) / kPage +
@@ -233,6 +240,10 @@ int decode_impl(const void* q, const void* kvcache, int64_t num_pages, int page_
     if (dbg_elems < dbg_plane * (kv_format == 1 ? 2 : 1)) return MLA_ERR_INVALID_ARGUMENT;
   }
   if (batch == 0) return MLA_OK;
+  if (fixed_scratch) {
+    const int st_ws = fixed_scratch(&workspace);
+    if (st_ws != MLA_OK) return st_ws;
+  }
 
   DecodeArgs a;
   a.dbg_rows = dbg_rows;
@@ -301,9 +312,47 @@ int decode_impl(const void* q, const void* kvcache, int64_t num_pages, int page_
   return MLA_OK;
 }
 
+// The no-alloc decode's scratch: one copy per GPU the library runs on, held
+// until the process ends.  Host code never uses this name as an address (on
+// the host it is a stand-in); it uses the device address looked up below.
+static __device__ __align__(256) unsigned char scratch[MLA_NO_ALLOC_SCRATCH_BYTES];
+
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's copy of `scratch`, looked up once per device.
+int scratch_ptr(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MLA_ERR_HIP;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MLA_ERR_HIP;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return MLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int mla_decode_with_kvcache_no_alloc(const void* q, const void* kvcache, int64_t num_pages,
+                                     int page_size, const int32_t* block_table, int max_blocks,
+                                     const int32_t* cache_seqlens, int batch, int s_q, int h_q,
+                                     int h_kv, int d_qk, int dv, const int32_t* plan,
+                                     const int32_t* num_splits, int num_workers, int causal,
+                                     float softmax_scale, const int32_t* indices, int topk,
+                                     void* o, float* lse, void* stream) {
+  return decode_impl(q, kvcache, num_pages, page_size, block_table, max_blocks, cache_seqlens,
+                     batch, s_q, h_q, h_kv, d_qk, dv, plan, num_splits, num_workers, causal,
+                     softmax_scale, indices, topk, o, lse, nullptr, MLA_NO_ALLOC_SCRATCH_BYTES, 0,
+                     nullptr, 3, stream, nullptr, 0, scratch_ptr);
+}
 
 int mla_decode_with_kvcache_phase(const void* q, const void* kvcache, int64_t num_pages,
                                   int page_size, const int32_t* block_table, int max_blocks,

@@ -5,6 +5,7 @@ import os
 import re
 
 import pytest
+import torch
 
 from mla_paged_kv_get_amd import _lib
 
@@ -39,7 +40,7 @@ def test_one_hip_runtime_mapped():
 
 def test_status_strings():
     l = _lib.lib()
-    for s in range(5):
+    for s in range(6):
         assert l.mla_status_string(s)
     assert l.mla_status_string(99) == b"unknown status"
 
@@ -118,6 +119,51 @@ def test_decode_empty_batch_takes_null_arrays():
     assert _decode(**empty, kv=None) == _lib.MLA_ERR_INVALID_ARGUMENT
     assert _decode(**empty, plan=None) == _lib.MLA_ERR_INVALID_ARGUMENT
     assert _decode(**empty, idx=None, topk=16, causal=1) == _lib.MLA_ERR_INVALID_ARGUMENT
+
+
+def _no_alloc(**kw):
+    a = dict(q=DUMMY, kv=DUMMY, num_pages=10, page=64, bt=DUMMY, mb=4, sl=DUMMY, batch=2, s_q=1,
+             h_q=16, h_kv=1, d=576, dv=512, plan=DUMMY, ns=DUMMY, W=8, causal=0, scale=0.05,
+             idx=None, topk=0, o=DUMMY, lse=DUMMY, stream=None)
+    a.update(kw)
+    return _lib.lib().mla_decode_with_kvcache_no_alloc(*a.values())
+
+
+def test_no_alloc_scratch_size_matches_header():
+    txt = open(os.path.join(ROOT, "include", "mla_paged_kv.h")).read()
+    m = re.search(r"#define MLA_NO_ALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", txt)
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.NO_ALLOC_SCRATCH_BYTES
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=448), _lib.MLA_ERR_UNSUPPORTED),
+    (dict(page=32), _lib.MLA_ERR_UNSUPPORTED),
+    (dict(q=None), _lib.MLA_ERR_INVALID_ARGUMENT),
+    (dict(causal=2), _lib.MLA_ERR_INVALID_ARGUMENT),
+    (dict(idx=DUMMY, topk=16, causal=1), _lib.MLA_ERR_INVALID_ARGUMENT),
+    (dict(W=0), _lib.MLA_ERR_INVALID_ARGUMENT),
+    # partials of (items + W) x 128 rows x 513 floats: 4096 + 8 slots need 1.08 GB
+    (dict(batch=4096, h_q=128), _lib.MLA_ERR_SCRATCH_LIMIT),
+    (dict(W=1 << 14, h_q=128), _lib.MLA_ERR_SCRATCH_LIMIT),
+])
+def test_no_alloc_rejects_before_any_hip_call(kw, code):
+    assert _no_alloc(**kw) == code
+
+
+def test_no_alloc_limit_is_the_workspace_size():
+    l = _lib.lib()
+    W = 1
+    while l.mla_workspace_bytes(2, 1, 128, 1, 0, 512, W + 1) <= _lib.NO_ALLOC_SCRATCH_BYTES:
+        W += 1
+    assert _no_alloc(W=W + 1, h_q=128) == _lib.MLA_ERR_SCRATCH_LIMIT
+    if torch.cuda.device_count() == 0:
+        # the largest worker count whose partials fit passes the host checks;
+        # the first HIP call then fails (no GPU: nothing is launched)
+        assert _no_alloc(W=W, h_q=128) == _lib.MLA_ERR_HIP
+
+
+def test_no_alloc_empty_batch_is_noop():
+    assert _no_alloc(batch=0, q=None, bt=None, sl=None, o=None, lse=None) == _lib.MLA_OK
 
 
 def test_phase_argument_checked():
