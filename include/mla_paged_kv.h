@@ -128,10 +128,11 @@ int mla_plan_num_workers(int plan_words, int batch, int s_q, int num_q_rows, int
  *   topk, topk2    index-list lengths of the sparse modes (0 for dense; topk2
  *                  only with topk > 0)
  *   plan           [out_plan_words] int32, device (output).  Row 0 = {W, per-run
- *                  overhead in blocks, W', items, version 2, 64, total cost T,
- *                  0}; row 1 + w = {first item, its first
- *                  block, last item, end block (exclusive) in the last item,
- *                  split number of the run in the first item, 0, 0, 0}, or
+ *                  overhead in blocks, W', items, version 2, 64, total cost T
+ *                  mod 2^32, T div 2^32} (the cost axis is 64-bit); row
+ *                  1 + w = {first item, its first block, last item, end block
+ *                  (exclusive) in the last item, split number of the run in
+ *                  the first item, 0, 0, 0}, or
  *                  {-1, 0, -1, 0, 0, 0, 0, 0} for a worker with no blocks.
  *                  The rows are followed by the arrival counters of the
  *                  single-launch decode, which this call sets to zero.
@@ -143,8 +144,8 @@ int mla_plan_num_workers(int plan_words, int batch, int s_q, int num_q_rows, int
  * finished runs in the plan's arrival counters and leaves them zero when it
  * completes: single-launch calls that share one plan must not overlap (two
  * streams), while two-launch calls may.  More than MLA_PLAN_MAX_ITEMS items:
- * MLA_ERR_UNSUPPORTED.  The cost axis is 32-bit: the sum over items of
- * (overhead + n_i) must stay below 2^31 (about 1.4e11 cached tokens).
+ * MLA_ERR_UNSUPPORTED.  Any lengths up to 2^31 - 1 are planned exactly (the
+ * total cost may pass 2^31; block numbers inside an item stay below 2^25).
  */
 int mla_get_metadata(const int32_t* cache_seqlens, int batch, int s_q,
                      int num_q_rows, int h_kv, int topk, int topk2, int num_workers,

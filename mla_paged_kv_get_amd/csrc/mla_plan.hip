@@ -15,6 +15,10 @@
 // it.  With up to kScatterW workers and no item reaching more than
 // kScatterSpan of them, each item marks its workers (LDS min / max); otherwise
 // each worker searches the item starts.
+// The cost axis is 64-bit: the kernel first sums the item costs in 64 bits;
+// when the total fits 31 bits (every realistic batch) the axis is kept in
+// 32-bit integers, otherwise in 64-bit ones (item starts in LDS as int64, no
+// marking).  Block numbers inside an item always fit 32 bits.
 #include "mla_common.h"
 
 namespace mla {
@@ -34,9 +38,18 @@ __device__ __forceinline__ uint32_t udiv(uint32_t n, uint32_t d, uint32_t m) {
   return q;
 }
 
-// floor(num / den) for 0 <= num < 2^53 and den >= 1: the quotient in double
-// precision is within one of the floor, and one comparison each way fixes it.
+// 64-bit integer division, out of line (a long instruction sequence that only
+// the 64-bit schedule needs).
+__device__ __attribute__((noinline)) int64_t div_wide(int64_t num, int64_t den) { return num / den; }
+
+// floor(num / den) for 0 <= num < 2^53 (kWide: 2^63) and den >= 1.  Below
+// 2^53 the quotient in double precision is within one of the floor, and one
+// comparison each way fixes it; above, 64-bit integer division.
+template <bool kWide>
 __device__ __forceinline__ int64_t floor_div(int64_t num, int64_t den) {
+  if constexpr (kWide) {
+    if (num >= ((int64_t)1 << 53)) return div_wide(num, den);
+  }
   int64_t q = (int64_t)((double)num / (double)den);
   if (q * den > num) --q;
   else if ((q + 1) * den <= num) ++q;
@@ -76,97 +89,117 @@ __device__ int block_inclusive_scan(int v, int* wave_sums, int& total) {
   return v + before;
 }
 
+// Exclusive scan of one int64 per thread over the workgroup, for values below
+// 2^38; `total` receives the sum.  The low 23 and the high bits go through two
+// 32-bit DPP scans (a wave's sums stay below 2^29 and 2^21), joined after one
+// barrier; `wave_lo` / `wave_hi` must not be written again before the next.
+__device__ int64_t block_exclusive_scan64(int64_t v, int* wave_lo, int* wave_hi, int64_t& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lo = wave_inclusive_sum((int)(v & 0x7fffff));
+  const int hi = wave_inclusive_sum((int)(v >> 23));
+  if (lane == 63) {
+    wave_lo[wave] = lo;
+    wave_hi[wave] = hi;
+  }
+  __syncthreads();
+  int64_t before = 0, tot = 0;
+#pragma unroll
+  for (int j = 0; j < kPlanWaves; ++j) {
+    const int64_t s = ((int64_t)wave_hi[j] << 23) + wave_lo[j];
+    before += j < wave ? s : 0;
+    tot += s;
+  }
+  total = tot;
+  return before + ((int64_t)hi << 23) + lo - v;
+}
+
 // Blocks of item i: topk keys (sparse) or the length of its sequence i / item_div
 // (dense; item_div = number of KV heads, items being (sequence, KV head)).
 __device__ __forceinline__ int item_blocks(const int32_t* seqlens, int topk, int item_div, int i) {
   const int len = topk > 0 ? topk : seqlens[i / item_div];
-  return len > 0 ? (len + kPage - 1) / kPage : 0;
+  return len > 0 ? len / kPage + (len % kPage != 0) : 0;   // no overflow near 2^31
 }
 
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ seqlens,
-                                                            int topk, int num_items, int item_div,
-                                                            int W, int c,
-                                                            int32_t* __restrict__ plan,
-                                                            int32_t* __restrict__ num_splits,
-                                                            int32_t* __restrict__ counters,
-                                                            int num_counters) {
-  __shared__ int start[kPlanMaxItems + 1];
-  __shared__ int first_s[kScatterW], last_s[kScatterW];   // least / greatest item reaching worker w
-  __shared__ int sums_a[kPlanWaves], sums_b[kPlanWaves], span_w[kPlanWaves];
+// The schedule once the total cost T is known.  Ax is the cost-axis integer
+// (int when T fits 31 bits, else int64_t); `run` is the start of the thread's
+// first item.  `start` receives the item starts (num_items + 1 of them); for
+// Ax = int it arrives holding each item's block count, parked there by the
+// kernel.  first_s / last_s (kScatterW each) are null when marking is not
+// available.
+template <typename Ax>
+__device__ void plan_body(const int32_t* __restrict__ seqlens, int topk, int num_items,
+                          int item_div, int W, int c, int32_t* __restrict__ plan,
+                          int32_t* __restrict__ num_splits, Ax* start, int* first_s, int* last_s,
+                          Ax run, const Ax T, int* sums_b, int* span_w) {
   const int tid = threadIdx.x;
   const int per = (num_items + kPlanThreads - 1) / kPlanThreads;
   const int i0 = min(tid * per, num_items), i1 = min(i0 + per, num_items);
-
-  // arrival counters of the single-launch decode start at zero
-  for (int i = tid; i < num_counters; i += kPlanThreads) counters[i] = 0;
-  if (W <= kScatterW) {
+  const bool can_mark = first_s != nullptr && W <= kScatterW;
+  if (can_mark) {
     for (int w = tid; w < W; w += kPlanThreads) {
       first_s[w] = num_items;   // none
       last_s[w] = -1;
     }
   }
 
-  // Start of every item on the cost axis (the blocks are parked in start[]
-  // until the scan is done).
-  int local = 0;
+  // Start of every item on the cost axis.
   for (int i = i0; i < i1; ++i) {
-    const int n = item_blocks(seqlens, topk, item_div, i);
-    start[i] = n;
-    local += c + n;
-  }
-  int T;
-  const int incl = block_inclusive_scan(local, sums_a, T);
-  int run = incl - local;
-  for (int i = i0; i < i1; ++i) {
-    const int n = start[i];
+    int n;
+    if constexpr (sizeof(Ax) == 4) {
+      n = start[i];
+    } else {
+      n = item_blocks(seqlens, topk, item_div, i);
+    }
     start[i] = run;
     run += c + n;
   }
   if (tid == 0) start[num_items] = T;
   __syncthreads();
-  const int We = min(W, T);
+  const int We = (int)min((Ax)W, T);
   // The divisions below are by T or by W', with numerators under W' T.  When
-  // that is below 2^32 they go by multiplication, otherwise in double precision.
+  // that is below 2^32 they go by multiplication, otherwise by floor_div (for
+  // a 32-bit axis W' T < 2^51).
+  constexpr bool kWideAx = sizeof(Ax) == 8;
   const bool narrow = T > 0 && (uint64_t)We * (uint64_t)T < (1ull << 32);
   const uint32_t mT = narrow ? 0xffffffffu / (uint32_t)T : 0u;
   const uint32_t mW = narrow ? 0xffffffffu / (uint32_t)We : 0u;
   // Owner of unit x (T >= 1 whenever an item has a block), and the first unit
   // of worker w <= W'.
-  auto owner = [&](int x) -> int {
+  auto owner = [&](Ax x) -> int {
     if (T <= 0) return 0;
     const int64_t n = ((int64_t)x + 1) * We - 1;
-    return narrow ? (int)udiv((uint32_t)n, (uint32_t)T, mT) : (int)floor_div(n, T);
+    return narrow ? (int)udiv((uint32_t)n, (uint32_t)T, mT) : (int)floor_div<kWideAx>(n, T);
   };
-  auto unit0 = [&](int w) -> int {
+  auto unit0 = [&](int w) -> Ax {
     const int64_t n = (int64_t)w * T;
-    return narrow ? (int)udiv((uint32_t)n, (uint32_t)We, mW) : (int)floor_div(n, We);
+    return narrow ? (Ax)udiv((uint32_t)n, (uint32_t)We, mW) : (Ax)floor_div<kWideAx>(n, We);
   };
 
   // Split counts (the number of workers each item reaches) and the largest.
-  local = 0;
+  int nsplit = 0;
   int span = 0;
   for (int i = i0; i < i1; ++i) {
-    const int first = start[i] + c, end = start[i + 1];
+    const Ax first = start[i] + c, end = start[i + 1];
     if (end > first) {
       const int n = owner(end - 1) - owner(first) + 1;
-      local += n;
+      nsplit += n;
       span = max(span, n);
     }
   }
   const bool wide = __builtin_amdgcn_ballot_w64(span > kScatterSpan) != 0;
   if ((tid & 63) == 0) span_w[tid >> 6] = wide;   // published by the scan's barrier
   int S;
-  const int sincl = block_inclusive_scan(local, sums_b, S);
+  const int sincl = block_inclusive_scan(nsplit, sums_b, S);
   bool any_wide = false;
   for (int j = 0; j < kPlanWaves; ++j) any_wide |= span_w[j] != 0;
-  const bool scatter = W <= kScatterW && !any_wide;
-  run = sincl - local;
+  const bool scatter = can_mark && !any_wide;
+  int srun = sincl - nsplit;
   for (int i = i0; i < i1; ++i) {
-    num_splits[i] = run;
-    const int first = start[i] + c, end = start[i + 1];
+    num_splits[i] = srun;
+    const Ax first = start[i] + c, end = start[i + 1];
     if (end > first) {
       const int wl = owner(first), wh = owner(end - 1);
-      run += wh - wl + 1;
+      srun += wh - wl + 1;
       if (scatter) {
         for (int w = wl; w <= wh; ++w) {
           atomicMin(&first_s[w], i);
@@ -181,7 +214,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
   // One row per worker.
   for (int w = tid; w < W; w += kPlanThreads) {
     int32_t* row = plan + kPlanWords * (1 + w);
-    int lo = T, hi = T;
+    Ax lo = T, hi = T;
     if (w < We) {
       lo = unit0(w);
       hi = unit0(w + 1);
@@ -191,10 +224,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
       if (first_s[w] < num_items) {
         first_item = first_s[w];
         last_item = last_s[w];
-        const int ff = start[first_item] + c;
-        first_blk = max(lo, ff) - ff;
+        const Ax ff = start[first_item] + c;
+        first_blk = (int)(max(lo, ff) - ff);
         split = w - owner(ff);
-        last_end = min(hi, start[last_item + 1]) - start[last_item] - c;
+        last_end = (int)(min(hi, start[last_item + 1]) - start[last_item] - c);
       }
     } else if (lo < hi) {
       // Last item starting at or before lo.
@@ -204,10 +237,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
         if (start[m] <= lo) a = m; else b = m - 1;
       }
       for (int i = a; i < num_items && start[i] < hi; ++i) {
-        const int bl = max(lo, start[i] + c), bh = min(hi, start[i + 1]);
+        const Ax bl = max(lo, start[i] + c), bh = min(hi, start[i + 1]);
         if (bl < bh) {
           first_item = i;
-          first_blk = bl - start[i] - c;
+          first_blk = (int)(bl - start[i] - c);
           split = w - owner(start[i] + c);
           break;
         }
@@ -221,10 +254,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
           if (start[m] < hi) a = m; else b = m - 1;
         }
         for (int i = a; i >= first_item; --i) {
-          const int bl = max(lo, start[i] + c), bh = min(hi, start[i + 1]);
+          const Ax bl = max(lo, start[i] + c), bh = min(hi, start[i + 1]);
           if (bl < bh) {
             last_item = i;
-            last_end = bh - start[i] - c;
+            last_end = (int)(bh - start[i] - c);
             break;
           }
         }
@@ -246,8 +279,61 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     plan[3] = num_items;
     plan[4] = kPlanVersion;
     plan[5] = kPage;
-    plan[6] = T;
-    plan[7] = 0;
+    plan[6] = (int32_t)(uint32_t)((uint64_t)T & 0xffffffffu);   // T, low and high words
+    plan[7] = (int32_t)((uint64_t)T >> 32);
+  }
+}
+
+// The 64-bit schedule, out of line: it only runs when the total cost passes
+// 2^31, and the kernel's 32-bit path stays compact.
+__device__ __attribute__((noinline)) void plan_body_wide(const int32_t* seqlens, int topk,
+                                                         int num_items, int item_div, int W, int c,
+                                                         int32_t* plan, int32_t* num_splits,
+                                                         int64_t* start, int64_t run, int64_t T,
+                                                         int* sums_b, int* span_w) {
+  plan_body<int64_t>(seqlens, topk, num_items, item_div, W, c, plan, num_splits, start, nullptr,
+                     nullptr, run, T, sums_b, span_w);
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ seqlens,
+                                                            int topk, int num_items, int item_div,
+                                                            int W, int c,
+                                                            int32_t* __restrict__ plan,
+                                                            int32_t* __restrict__ num_splits,
+                                                            int32_t* __restrict__ counters,
+                                                            int num_counters) {
+  // Item starts: int [num_items + 1] followed by the marking arrays, or int64
+  // [num_items + 1] alone.
+  constexpr int kStartInts = (kPlanMaxItems + 1 + 3) & ~3;
+  static_assert(kStartInts + 2 * kScatterW <= 2 * (kPlanMaxItems + 1), "marking arrays must fit");
+  __shared__ int64_t raw[kPlanMaxItems + 1];
+  __shared__ int sums_lo[kPlanWaves], sums_hi[kPlanWaves], sums_b[kPlanWaves], span_w[kPlanWaves];
+  const int tid = threadIdx.x;
+  const int per = (num_items + kPlanThreads - 1) / kPlanThreads;
+  const int i0 = min(tid * per, num_items), i1 = min(i0 + per, num_items);
+
+  // arrival counters of the single-launch decode start at zero
+  for (int i = tid; i < num_counters; i += kPlanThreads) counters[i] = 0;
+
+  // Block counts, parked in the 32-bit start array, and the 64-bit total
+  // (a thread's items cost below 64 (2^25 + 8) < 2^38).
+  static_assert(kPlanMaxItems <= 64 * kPlanThreads, "at most 64 items per thread");
+  int* start32 = reinterpret_cast<int*>(raw);
+  int64_t local = 0;
+  for (int i = i0; i < i1; ++i) {
+    const int n = item_blocks(seqlens, topk, item_div, i);
+    start32[i] = n;
+    local += c + n;
+  }
+  int64_t total;
+  const int64_t run = block_exclusive_scan64(local, sums_lo, sums_hi, total);
+  if (total <= 0x7fffffff) {
+    plan_body<int>(seqlens, topk, num_items, item_div, W, c, plan, num_splits, start32,
+                   start32 + kStartInts, start32 + kStartInts + kScatterW, (int)run, (int)total,
+                   sums_b, span_w);
+  } else {
+    plan_body_wide(seqlens, topk, num_items, item_div, W, c, plan, num_splits, raw, run, total,
+                   sums_b, span_w);
   }
 }
 

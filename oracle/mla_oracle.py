@@ -246,7 +246,8 @@ def plan(lengths, num_workers: int, overhead: int):
     the item's splits, numbered 0, 1, ...
 
     Returns (plan int32 [(W + 1) * 8], num_splits int32 [num_items + 1]):
-      plan row 0  = [W, overhead, W', num_items, version, 64, T, 0]
+      plan row 0  = [W, overhead, W', num_items, version, 64, T mod 2^32,
+                     T div 2^32] (T as two 32-bit words: the axis may pass 2^31)
       plan row 1+w = [first item, its first block, last item, end block of the
                       last item, split number of the first item's run, 0, 0, 0]
                     or [-1, 0, -1, 0, 0, 0, 0, 0] for a worker with no blocks.
@@ -266,7 +267,8 @@ def plan(lengths, num_workers: int, overhead: int):
     T = acc
     We = min(W, T)
     rows = np.zeros((W + 1, PLAN_WORDS), dtype=np.int64)
-    rows[0] = [W, c, We, len(lengths), PLAN_VERSION, PAGE, T, 0]
+    t_lo = T & 0xFFFFFFFF
+    rows[0] = [W, c, We, len(lengths), PLAN_VERSION, PAGE, t_lo - (t_lo >> 31 << 32), T >> 32]
     counts = [0] * len(lengths)
     for w in range(W):
         if w < We:

@@ -71,6 +71,32 @@ def test_plan_bit_exact_division_paths(lengths, W):
     assert (ns.cpu().numpy() == ref_ns).all()
 
 
+@pytest.mark.parametrize("case", ["dense-random", "dense-halves", "sparse", "search"])
+def test_plan_bit_exact_axis_past_2_31(case):
+    # total cost past 2^31 (lengths near 2^31): the scheduler's 64-bit axis
+    m = _m()
+    rng = np.random.default_rng(77)
+    topk, s_q, h_q, W = None, 1, 16, 256
+    if case == "dense-random":
+        lengths = [int(x) for x in rng.integers(2**30, 2**31 - 1, 120)] + [0, 5, 2**31 - 1]
+    elif case == "dense-halves":
+        lengths, W = [64 * (2**25 - 1)] * 70, 140       # two workers per item, exactly
+    elif case == "sparse":
+        lengths, topk, s_q, h_q, W = [1000] * 100, 2**30, 2, 128, 1000
+    else:
+        lengths, W = [int(x) for x in rng.integers(2**29, 2**31 - 1, 300)], 5000   # no marking
+    sl = i32_dev(np.array(lengths))
+    plan, ns = m.get_mla_metadata(sl, s_q * h_q, 1, s_q=s_q, topk=topk, num_workers=W)
+    torch.cuda.synchronize()
+    p = plan.cpu().numpy()
+    items = [topk] * (len(lengths) * s_q) if topk else lengths
+    ref_p, ref_ns = orc.plan(items, W, int(p[1]))
+    T = (int(ref_p[6]) & 0xFFFFFFFF) + (int(ref_p[7]) << 32)
+    assert T >= 2**31
+    assert (p[:ref_p.size] == ref_p).all(), f"{case}: {(p[:ref_p.size] != ref_p).sum()} plan words differ"
+    assert (ns.cpu().numpy() == ref_ns).all()
+
+
 @pytest.mark.parametrize("h_q", [16, 128])
 def test_all_sequences_empty(h_q):
     # every item has no key: no worker gets a block, every row is o = 0, lse = -inf

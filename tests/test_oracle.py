@@ -484,7 +484,7 @@ def _check_plan_invariants(lengths, W, c):
     p, ns = orc.plan(lengths, W, c)
     rows = p.reshape(-1, 8)
     nblk = [-(-L // 64) for L in lengths]
-    T, We = rows[0, 6], rows[0, 2]
+    T, We = (int(rows[0, 6]) & 0xFFFFFFFF) + (int(rows[0, 7]) << 32), rows[0, 2]
     P = -(-T // We) if We else 0          # the longest worker interval
     runs = orc.plan_runs(p, lengths)
     cover = [np.zeros(n, dtype=int) for n in nblk]
@@ -507,6 +507,32 @@ def _check_plan_invariants(lengths, W, c):
         assert ns[i + 1] - ns[i] == len(segs)
     assert ns[0] == 0 and ns[-1] == sum(len(v) for v in per_item.values())
     assert ns[-1] <= len(lengths) + W
+
+
+def _t(rows):
+    return (int(rows[0, 6]) & 0xFFFFFFFF) + (int(rows[0, 7]) << 32)
+
+
+def test_plan_axis_past_2_31_closed_form():
+    # n = 2^25 - 1 blocks per item (lengths just under 2^31), 70 items: the
+    # total cost passes 2^31 and is stored as two 32-bit words
+    n = 2**25 - 1
+    # one worker per item: worker w owns exactly item w's units
+    p, ns = orc.plan([64 * n] * 70, 70, 4)
+    rows = p.reshape(-1, 8).astype(np.int64)
+    assert _t(rows) == 70 * (n + 4) and list(rows[0, :6]) == [70, 4, 70, 70, orc.PLAN_VERSION, 64]
+    for w in range(70):
+        assert list(rows[1 + w]) == [w, 0, w, n, 0, 0, 0, 0]
+    assert list(ns) == list(range(71))
+    # overhead 1 and two workers per item: each item's 2^25 units split in halves,
+    # its first unit being the overhead
+    p, ns = orc.plan([64 * n] * 70, 140, 1)
+    rows = p.reshape(-1, 8).astype(np.int64)
+    assert _t(rows) == 70 * 2**25
+    for i in range(70):
+        assert list(rows[1 + 2 * i]) == [i, 0, i, 2**24 - 1, 0, 0, 0, 0]
+        assert list(rows[2 + 2 * i]) == [i, 2**24 - 1, i, n, 1, 0, 0, 0]
+    assert list(ns) == list(range(0, 141, 2))
 
 
 def test_plan_invariants_random():
