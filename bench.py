@@ -29,8 +29,9 @@ k=2048) and reports their bf16 TFLOPS and MFMA fraction under
 counters (FETCH_SIZE and WRITE_SIZE, each calibrated against a plain device
 copy of known size, see --calibrate-copy) and stored in
 profiles/decode_<workload>_traffic.json together with the SHA-256 of the
-kernel source it was taken on; it is reported only while that source is
-unchanged, else null.
+decode kernels' sources it was taken on (mla_common.h, mla_decode_kernel.h,
+mla_decode.hip, mla_decode_rows128.hip); it is reported only while those
+sources are unchanged, else null.
 
 Prints one JSON line (the last line of stdout).
 """
@@ -162,15 +163,20 @@ def run_workload(torch, m, w, steps, warmup, ncopies=NCOPIES):
 
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-DECODE_SRC = os.path.join(HERE, "mla_paged_kv_get_amd", "csrc", "mla_decode.hip")
+DECODE_SRCS = tuple(os.path.join(HERE, "mla_paged_kv_get_amd", "csrc", f)
+                    for f in ("mla_common.h", "mla_decode_kernel.h", "mla_decode.hip", "mla_decode_rows128.hip"))
 PROFILES = os.path.join(HERE, "profiles")
 COMPUTE_BOUND = ("near_ridge", "mtp_causal", "sparse_topk")
 SECONDARY = ("grouped_heads", "sparse_prefill", "memory_bound_fp8", "sparse_topk_fp8", "dual_cache")
 
 
-def source_sha256(path=DECODE_SRC):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def source_sha256(paths=DECODE_SRCS):
+    """Digest of the decode kernels' sources (counter runs are valid for one)."""
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(key, workload):
