@@ -19,8 +19,9 @@
 //    PV over the LDS banks.  Two stages: tile t + 1 is requested before the
 //    wait for tile t.  The copies are issued from inline assembly and waited
 //    for with explicit vmcnt counts (see copy_to_lds_16).
-//  * S^T = K Q^T with v_mfma_f32_16x16x32_bf16: A = 16 key rows read from LDS,
-//    B = 16 query rows held in registers.
+//  * S^T = K Q^T on the matrix cores: A = key rows read from LDS, B = query
+//    rows held in registers (v_mfma_f32_16x16x32_bf16 for items of up to 16
+//    rows, v_mfma_f32_32x32x16_bf16 for larger ones).
 //  * Online softmax in base 2 (scores pre-multiplied by scale*log2(e)).  The
 //    running reference of a row only moves when the row max exceeds it by more
 //    than 8 (a factor 2^8), so the O accumulators are rescaled a few times per
@@ -30,16 +31,19 @@
 //    ds_read_b64_tr_b16.  Items of up to 16 query rows (the memory-bound
 //    decode case) split each tile's keys over the 4 waves for QK^T and the
 //    512 output columns for PV, exchanging P through LDS, so a run ends
-//    without merging partial outputs across waves.  Larger items use 16 rows
-//    per wave and all keys of the tile.
+//    without merging partial outputs across waves.  Larger items: see the
+//    variants below.
 //  * Keys past a sequence's length inside its last page, and sparse padding
 //    entries, are loaded from a valid row of the same sequence and masked to
 //    -inf, so no value outside the key set (e.g. NaN garbage) is ever read.
 //  * Runs covering a whole item write bf16 O and fp32 LSE directly; other runs
-//    write fp32 partials that combine_kernel merges (log-sum-exp).  (Merging
-//    inside this kernel, by the last run of an item to finish, needs a
-//    device-scope release/acquire per run; on MI355X that writes back and
-//    invalidates the XCD's L2 and cost several times the decode itself.)
+//    write fp32 partials that combine_kernel merges (log-sum-exp).  In the
+//    single-launch mode (FUSED) the last run of an item to finish merges them
+//    here instead: partials are stored and loaded at agent scope, which is
+//    coherent across the XCDs' L2s without write-back or invalidation, and
+//    arrivals are counted with agent-scope atomics once a run's stores are
+//    complete (no release/acquire fence, which on this chip writes back and
+//    invalidates the whole L2 of the XCD).
 #pragma once
 
 #include "mla_common.h"
@@ -102,7 +106,7 @@ __device__ __forceinline__ bf16x4 read_tr(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(p));
 }
 
-// Decode variants.  Both use 4 waves, 64-key tiles and two LDS stages.
+// Decode variants.  All use 4 waves, 64-key tiles and two LDS stages.
 //  Rows16 (items of at most 16 query rows): wave tg computes the scores of
 //    keys 16 tg .. 16 tg + 15 (v_mfma_f32_16x16x32_bf16) and, once the
 //    probabilities of the whole tile are exchanged through LDS, output columns
@@ -111,7 +115,11 @@ __device__ __forceinline__ bf16x4 read_tr(const char* p) {
 //    query rows, and the wave computes the scores of keys 32 half .. + 31 and
 //    output columns 256 half .. + 255 (v_mfma_f32_32x32x16_bf16), exchanging
 //    the probabilities with its partner through LDS.
-// In both, the waves sharing a row share its softmax reference, so no partial
+//  Rows128 (items of more than 64 rows over bf16 caches, 128-row tiles): each
+//    wave owns 32 query rows over all 64 keys and all 512 output columns, its
+//    32 x 512 fp32 output block in the 256 accumulation registers, so no
+//    probability or softmax state crosses waves.
+// In all, the waves sharing a row share its softmax reference, so no partial
 // outputs are merged when a run ends.
 // With packed FP8 rows (KV8) the tiles are copied as they are stored (41 KB
 // per 64 rows) into the two stages, and the MFMA operands are read from the
