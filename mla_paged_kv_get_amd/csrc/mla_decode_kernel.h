@@ -942,40 +942,62 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
       Ls = aux ? read_scalar(a.seqlens2 + b) : item_len(item);
       base = aux ? (int64_t)(reinterpret_cast<const char*>(a.kv2) - kv_bytes) : 0;
     };
+    // Each of the two is split in an LDS read (…_read) and the work on its
+    // result (…_use), so that the 128-row variant can issue the read a few
+    // MFMAs before the result is needed.
+    auto translate_read = [&](int item, int blk, int slot) __attribute__((always_inline)) -> int {
+      const SparseList sl = sparse_list(item, blk);
+      const int rr = 16 * wave + (lane & 15);
+      return sl.e0 + rr < sl.n ? idxbuf[slot & 3][rr] : -1;
+    };
+    auto translate_use = [&](int item, int blk, int slot, int idx, unsigned char* vslot) __attribute__((always_inline)) {
+      const int32_t* bt_row;
+      int Ls;
+      int64_t base;
+      sparse_rows(item, blk, bt_row, Ls, base);
+      const bool ok = sparse_key_valid(idx, Ls);
+      copy_to_lds_4(bt_row + ((ok ? idx : 0) >> 6), lds_addr(&pgbuf[slot & 1][wave][0]));
+      if (lane < 16) vslot[16 * wave + (lane & 15)] = ok ? 1 : 0;
+    };
     auto translate_lds = [&](int item, int blk, int slot, unsigned char* vslot) __attribute__((always_inline)) {
-      if constexpr (kWide && sparse) {
-        const SparseList sl = sparse_list(item, blk);
-        const int32_t* bt_row;
-        int Ls;
-        int64_t base;
-        sparse_rows(item, blk, bt_row, Ls, base);
-        const int rr = 16 * wave + (lane & 15);
-        const int idx = sl.e0 + rr < sl.n ? idxbuf[slot & 3][rr] : -1;
-        const bool ok = sparse_key_valid(idx, Ls);
-        copy_to_lds_4(bt_row + ((ok ? idx : 0) >> 6), lds_addr(&pgbuf[slot & 1][wave][0]));
-        if (lane < 16) vslot[rr] = ok ? 1 : 0;
+      if constexpr (kWide && sparse) translate_use(item, blk, slot, translate_read(item, blk, slot), vslot);
+    };
+    // The index entries and pages of this lane's rows of a tile.
+    struct RowsRaw {
+      int idx[C::kOffs];
+      int page[C::kOffs];
+    };
+    auto finish_read = [&](int item, int blk, int slot, RowsRaw& rr) __attribute__((always_inline)) {
+      const SparseList sl = sparse_list(item, blk);
+#pragma unroll
+      for (int r = 0; r < C::kOffs; ++r) {
+        const int row = r < C::kLaneRows ? cp_row[r] : sc_row;
+        rr.idx[r] = sl.e0 + row < sl.n ? idxbuf[slot & 3][row] : -1;
+        rr.page[r] = pgbuf[slot & 1][row >> 4][row & 15];
       }
+    };
+    auto finish_use = [&](int item, int blk, const RowsRaw& rr, Src& src) __attribute__((always_inline)) {
+      const int32_t* bt_row;
+      int Ls;
+      int64_t base;
+      sparse_rows(item, blk, bt_row, Ls, base);
+      const int kvh = item - div_by(item, (unsigned)a.h_kv, a.head_mul) * a.h_kv;
+#pragma unroll
+      for (int r = 0; r < C::kOffs; ++r) {
+        const bool ok = sparse_key_valid(rr.idx[r], Ls);
+        // padding reads the sequence's first row (the pool's first if it has none)
+        const int64_t crow =
+            (ok || Ls > 0) ? (int64_t)rr.page[r] * kPage + ((ok ? rr.idx[r] : 0) & (kPage - 1)) : 0;
+        src.off[r] = base + (crow * a.h_kv + kvh) * (int64_t)C::kRowB;
+      }
+      seal_sparse(src);
+      record(item, blk, src);
     };
     auto finish_lds = [&](int item, int blk, int slot, Src& src) __attribute__((always_inline)) {
       if constexpr (kWide && sparse) {
-        const SparseList sl = sparse_list(item, blk);
-        const int32_t* bt_row;
-        int Ls;
-        int64_t base;
-        sparse_rows(item, blk, bt_row, Ls, base);
-        const int kvh = item - div_by(item, (unsigned)a.h_kv, a.head_mul) * a.h_kv;
-#pragma unroll
-        for (int r = 0; r < C::kOffs; ++r) {
-          const int row = r < C::kLaneRows ? cp_row[r] : sc_row;
-          const int idx = sl.e0 + row < sl.n ? idxbuf[slot & 3][row] : -1;
-          const bool ok = sparse_key_valid(idx, Ls);
-          const int page = pgbuf[slot & 1][row >> 4][row & 15];
-          // padding reads the sequence's first row (the pool's first if it has none)
-          const int64_t crow = (ok || Ls > 0) ? (int64_t)page * kPage + ((ok ? idx : 0) & (kPage - 1)) : 0;
-          src.off[r] = base + (crow * a.h_kv + kvh) * (int64_t)C::kRowB;
-        }
-        seal_sparse(src);
-        record(item, blk, src);
+        RowsRaw rr;
+        finish_read(item, blk, slot, rr);
+        finish_use(item, blk, rr, src);
       }
     };
 
@@ -986,9 +1008,16 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     // has its padding read the pool's first row), and 0 * NaN would reach O
     // through PV.  Such a tile is cleared before it is computed (the test is
     // the same in every wave).
-    auto clear_if_empty = [&](char* tile, const unsigned char* vslot) __attribute__((always_inline)) {
+    // Whether a sparse tile has a valid key, and whether all of its keys are
+    // (wave-uniform; the 64 keys of the tile are the 64 lanes).
+    auto tile_validity = [&](const unsigned char* vslot, bool& any, bool& all) __attribute__((always_inline)) {
+      const bool v = vslot[lane] != 0;
+      any = __builtin_amdgcn_ballot_w64(v) != 0;
+      all = __builtin_amdgcn_ballot_w64(!v) == 0;
+    };
+    auto clear_if_empty = [&](char* tile, bool any_valid) __attribute__((always_inline)) {
       if constexpr (sparse) {
-        if (__builtin_amdgcn_ballot_w64(vslot[lane] != 0) == 0) {
+        if (!any_valid) {
           // the bf16 tile, or (FP8) the copied codes and RoPE values
           constexpr int kClearB = KV8 ? kRaw8ScaleOff : C::kTileB;
           for (int i = threadIdx.x; i < kClearB / 16; i += C::kThreads)
@@ -1469,8 +1498,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     // the first MFMA; the copy of the next tile (dma_stage, `off`) follows, one
     // instruction every third QK^T MFMA; after_qk() runs once the query
     // fragments are no longer needed for this tile.
-    auto compute_full = [&](const char* stage, const unsigned char* vslot, int blk, int lim,
-                            char* dma_stage, auto&& mid, auto&& after_qk, bool first) __attribute__((always_inline)) {
+    auto compute_full = [&](const char* stage, const unsigned char* vslot, bool all_valid, int blk, int lim,
+                            char* dma_stage, auto&& hook, auto&& after_qk, bool first) __attribute__((always_inline)) {
       if constexpr (kFull) {
         floatx16 sacc[2];
         // QK^T MFMAs: k-step n % kQf of block n / kQf.  One block after the
@@ -1480,8 +1509,9 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
         constexpr int kN = 2 * C::kQf;
         constexpr int kPre = 4;             // K fragments read ahead
         // The copies of the next tile go out one every third MFMA from MFMA
-        // kCopy0 on; the index work for later tiles (mid) comes first, so that
-        // a wait it may contain never waits for this tile's copies.
+        // kCopy0 on; the index work for later tiles (hook(n), at the first
+        // MFMAs) comes first, so that a wait it may contain never waits for
+        // this tile's copies.
         constexpr int kCopy0 = 16;
         static_assert(kCopy0 + 3 * (C::kLoads - 1) < kN, "the copies must fit the QK^T MFMAs");
         auto kread = [&](int n) __attribute__((always_inline)) -> bf16x8 {
@@ -1498,7 +1528,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
             if constexpr (n + kPre < kN) kf[n % kPre] = kread(n + kPre);
             if constexpr (n % C::kQf == 0) sacc[n / C::kQf] = mfma_v0(kc, qf[0]);
             else mfma_v(sacc[n / C::kQf], kc, qf[n % C::kQf]);
-            if constexpr (n == 1) mid();
+            hook(nc);
             if constexpr (decltype(with_dma)::value && n >= kCopy0 && (n - kCopy0) % 3 == 0 &&
                           (n - kCopy0) / 3 < C::kLoads)
               issue_one(dma_stage, off, std::integral_constant<int, (n - kCopy0) / 3>{});
@@ -1511,8 +1541,9 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
         after_qk();
         // element r of block kb: key 32 kb + 8 (r / 4) + 4 hl + r % 4.  Tiles
         // whose keys are all valid for every row of the wave skip the mask.
-        const bool full = !sparse && __builtin_amdgcn_ballot_w64(blk * kPage + kPage <= lim) ==
-                                         __builtin_amdgcn_read_exec();
+        const bool full = sparse ? all_valid && __builtin_amdgcn_ballot_w64(row_ok) == __builtin_amdgcn_read_exec()
+                                 : __builtin_amdgcn_ballot_w64(blk * kPage + kPage <= lim) ==
+                                       __builtin_amdgcn_read_exec();
         if (!full) {
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
@@ -1795,7 +1826,11 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
           }
         };
         const bool ends = !has_next || nx_item != cur_item;
-        clear_if_empty(cur, kvalid[t & 3]);
+        if constexpr (sparse) {
+          bool any_v, all_v;
+          tile_validity(kvalid[t & 3], any_v, all_v);
+          clear_if_empty(cur, any_v);
+        }
         if constexpr (!kFull) compute(cur, kvalid[t & 3], cur_blk, cur_lim, has_next ? nxt : nullptr, mid);
         if (ends) {
           finish(cur_item, cur_split);
@@ -1855,7 +1890,11 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
       q8_pending = false;
       if (n2_item >= 0) tile_finish(n2_item, n2_blk, raw, off, kvalid[(t + 2) & 3]);
       const bool ends = !has_next || nx_item != cur_item;
-      clear_if_empty(cur, kvalid[t & 3]);
+      if constexpr (sparse) {
+        bool any_v, all_v;
+        tile_validity(kvalid[t & 3], any_v, all_v);
+        clear_if_empty(cur, any_v);
+      }
       compute(cur, kvalid[t & 3], cur_blk, cur_lim, q_lds && has_next ? nxt : nullptr, [] {});
       q_pending = false;
       if (ends) {
@@ -1893,6 +1932,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     // same as in the other wide steps: tile t + 1's copy goes out during tile
     // t's QK^T, across run boundaries.
     auto run_full = [&]() __attribute__((always_inline)) {
+      bool c_any = true, c_all = true;   // sparse: validity of tile t (any key, every key)
       for (;;) {
         const int run_item = cur_item, run_split = cur_split;
         bool first = true, has_next;
@@ -1911,32 +1951,65 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
           char* cur = (t & 1) ? s1 : s0;
           char* nxt = (t & 1) ? s0 : s1;
           if constexpr (sparse) {
-            if (has_next) finish_lds(nx_item, nx_blk, t + 1, off);
-          } else if (has_next) {
-            idx_from_lds(nx_item, nx_blk, t + 1, raw);
-            tile_finish(nx_item, nx_blk, raw, off, kvalid[(t + 1) & 3]);
+            if (t == 0) tile_validity(kvalid[0], c_any, c_all);
           }
-          auto mid = [&]() __attribute__((always_inline)) {
-            if (n2_item < 0) return;
-            if constexpr (sparse) {
-              translate_lds(n2_item, n2_blk, t + 2, kvalid[(t + 2) & 3]);
-              int n3_item = -1, n3_blk = 0, n3_hi = 0;
-              advance(n2_item, n2_blk, n2_hi, n3_item, n3_blk, n3_hi);
-              if (n3_item >= 0) idx_dma(n3_item, n3_blk, t + 3);
-            } else {
-              idx_dma(n2_item, n2_blk, t + 2);
+          // Index work for later tiles, between the first QK^T MFMAs, each
+          // LDS read a few MFMAs before its result is used: the offsets of
+          // tile t + 1 (whose copies start at MFMA 16); sparse, tile t + 2's
+          // pages and validity, tile t + 3's index entries and tile t + 1's
+          // validity; dense, tile t + 2's page id.
+          RowsRaw nr;
+          int m_idx = -1;
+          bool n_any = true, n_all = true;
+          auto hook = [&](auto nc) __attribute__((always_inline)) {
+            constexpr int n = decltype(nc)::value;
+            if constexpr (n == 0) {
+              if (has_next) {
+                if constexpr (sparse) finish_read(nx_item, nx_blk, t + 1, nr);
+                else nr.idx[0] = idxbuf[(t + 1) & 3][0];
+              }
+            } else if constexpr (n == 3) {
+              if (has_next) {
+                if constexpr (sparse) {
+                  finish_use(nx_item, nx_blk, nr, off);
+                } else {
+                  raw.v[0] = nr.idx[0];
+                  tile_finish(nx_item, nx_blk, raw, off, kvalid[(t + 1) & 3]);
+                }
+              }
+            } else if constexpr (n == 5) {
+              if constexpr (sparse) {
+                if (n2_item >= 0) m_idx = translate_read(n2_item, n2_blk, t + 2);
+              }
+            } else if constexpr (n == 8) {
+              if (n2_item >= 0) {
+                if constexpr (sparse) {
+                  translate_use(n2_item, n2_blk, t + 2, m_idx, kvalid[(t + 2) & 3]);
+                  int n3_item = -1, n3_blk = 0, n3_hi = 0;
+                  advance(n2_item, n2_blk, n2_hi, n3_item, n3_blk, n3_hi);
+                  if (n3_item >= 0) idx_dma(n3_item, n3_blk, t + 3);
+                } else {
+                  idx_dma(n2_item, n2_blk, t + 2);
+                }
+              }
+            } else if constexpr (n == 10) {
+              if constexpr (sparse) {
+                if (has_next) tile_validity(kvalid[(t + 1) & 3], n_any, n_all);
+              }
             }
           };
           const bool ends = !has_next || nx_item != cur_item;
-          clear_if_empty(cur, kvalid[t & 3]);
+          clear_if_empty(cur, c_any);
           // The next item's query rows are loaded as soon as this tile's
           // QK^T is done with their registers; they arrive during PV and the
           // end of the run, and the next tile's wait covers them.
           const bool q_next = ends && has_next;
           const int q_item = nx_item;
-          compute_full(cur, kvalid[t & 3], cur_blk, cur_lim, has_next ? nxt : nullptr, mid,
+          compute_full(cur, kvalid[t & 3], c_all, cur_blk, cur_lim, has_next ? nxt : nullptr, hook,
                        [&]() __attribute__((always_inline)) { if (q_next) load_q(q_item); }, first);
           first = false;
+          c_any = n_any;
+          c_all = n_all;
           cur_item = nx_item;
           cur_blk = nx_blk;
           cur_hi = nx_hi;
