@@ -1494,10 +1494,11 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     // the softmax of the wave's own rows, which needs no other wave (each lane
     // holds 16 keys of each block for its row, its partner lane ^ 32 the other
     // 16); then O^T += V^T P^T over 4 k-steps of 16 keys and the 16 column
-    // blocks of 32.  mid() does the index work for later tiles right after
-    // the first MFMA; the copy of the next tile (dma_stage, `off`) follows, one
-    // instruction every third QK^T MFMA; after_qk() runs once the query
-    // fragments are no longer needed for this tile.
+    // blocks of 32.  hook(n) runs after QK^T MFMA n (the caller does the index
+    // work for later tiles at the first ones); the copy of the next tile
+    // (dma_stage, `off`) follows, one instruction every third QK^T MFMA;
+    // after_qk() runs once the query fragments are no longer needed for this
+    // tile.  all_valid: every key of a sparse tile is valid (no mask).
     auto compute_full = [&](const char* stage, const unsigned char* vslot, bool all_valid, int blk, int lim,
                             char* dma_stage, auto&& hook, auto&& after_qk, bool first) __attribute__((always_inline)) {
       if constexpr (kFull) {
