@@ -242,7 +242,8 @@ def test_sparse_pads_and_empty():
 @pytest.mark.parametrize("h_kv,h_q,s_q,causal", [
     (2, 16, 1, False),      # 8 rows per item: 16-row tiles
     (4, 64, 2, True),       # 32 rows per item: 64-row tiles, causal
-    (2, 256, 1, False),     # 128 rows per item: two 64-row tiles
+    (2, 256, 1, False),     # 128 rows per item: one 128-row tile
+    (2, 256, 2, True),      # 256 rows per item: two 128-row tiles, causal
     (8, 64, 4, True),       # 32 rows per item from four tokens of 8 heads
 ])
 def test_grouped_latent_heads(h_kv, h_q, s_q, causal):
@@ -292,7 +293,7 @@ def test_grouped_heads_workload_full():
     compare(w, o, lse, label="grouped-heads b32 h128 hkv8")
 
 
-@pytest.mark.parametrize("h_kv,h_q", [(2, 32), (4, 256)])
+@pytest.mark.parametrize("h_kv,h_q", [(2, 32), (4, 256), (2, 256)])   # 16, 64 and 128 rows per item
 def test_grouped_latent_heads_sparse(h_kv, h_q):
     w = wl.build("grouped-sparse", 50 + h_kv, np.array([700, 129, 2000]), B=3, s_q=2, h_q=h_q,
                  h_kv=h_kv, num_pages=60, poison=True, topk=128)

@@ -127,7 +127,8 @@ def test_copy_rows_sparse_workloads(name):
 def test_copy_rows_split_runs(W):
     # runs crossing item boundaries and items split over several workers
     L = np.array([1, 63, 64, 65, 200, 0, 4097, 129])
-    for h_q, h_kv, s_q, causal in [(16, 1, 1, False), (128, 1, 2, True), (64, 8, 1, False)]:
+    for h_q, h_kv, s_q, causal in [(16, 1, 1, False), (128, 1, 2, True), (64, 8, 1, False),
+                                   (256, 2, 1, False)]:
         w = wl.build("copy-rows", 70, L, B=len(L), s_q=s_q, h_q=h_q, h_kv=h_kv, num_pages=300,
                      causal=causal, poison=True)
         check(w, num_workers=W)
