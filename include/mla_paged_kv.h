@@ -84,11 +84,11 @@ const char* mla_status_string(int status);
  *                        variant picked for this row count); > 0 forces it
  *   out_num_workers      workers W of the plan (host)
  *   out_plan_words       int32 words of the plan buffer (host): 8 * (W + 1)
- *                        words of plan rows, then items * ceil(num_q_rows' /
- *                        tile rows) int32 arrival counters of the single-launch
- *                        decode (num_q_rows' = rows per item; tile rows = 16,
- *                        64 or 128 depending on the decode variant the row
- *                        count selects)
+ *                        words of plan rows, then items * T int32 arrival
+ *                        counters of the single-launch decode, T = 1 when an
+ *                        item has at most 16 rows, else ceil(rows / 64) (the
+ *                        plan does not know the cache format, so it covers the
+ *                        finest row tiling any decode of this shape uses)
  *   out_num_items        items of the call; num_splits holds items + 1 words (host)
  * Needs the current HIP device only when num_workers_request == 0.  A call
  * with more than MLA_PLAN_MAX_ITEMS items returns MLA_ERR_UNSUPPORTED.
