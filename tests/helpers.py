@@ -73,7 +73,8 @@ def compare(w, o, lse, items=None, softmax_scale=None, label=""):
         do = np.abs(og[b, s] - O_ref[b, s]).max()
         ref_l = L_ref[b, s]
         same_inf = np.isneginf(ref_l) & np.isneginf(lg[b, s])
-        dl = np.where(same_inf, 0.0, np.abs(lg[b, s] - ref_l))
+        with np.errstate(invalid="ignore"):          # -inf - -inf where both are empty
+            dl = np.where(same_inf, 0.0, np.abs(lg[b, s] - ref_l))
         assert not np.isnan(dl).any(), f"{label}: LSE NaN at {(b, s)}"
         worst_o = max(worst_o, float(do))
         worst_l = max(worst_l, float(dl.max()))
