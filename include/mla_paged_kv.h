@@ -153,8 +153,11 @@ int mla_get_metadata(const int32_t* cache_seqlens, int batch, int s_q,
 
 /*
  * mla_workspace_bytes — host only; bytes of the decode scratch buffer: room
- * for (items + W) partial results of (rows per item) x (dv + 1) fp32 values
- * (split runs write one each; at most items + W - 1 are used).
+ * for (items + W) partial results of (rows per item) rows, each dv bf16
+ * output values and one fp32 LSE, i.e. (items + W) x rows x (2 dv + 4) bytes
+ * (split runs write one each; at most items + W - 1 are used).  The partial
+ * outputs are rounded to bf16 once, like the final output; the merge weights
+ * them in fp32.
  */
 size_t mla_workspace_bytes(int batch, int s_q, int num_q_rows, int h_kv, int topk,
                            int dv, int num_workers);
@@ -233,7 +236,7 @@ int mla_decode_with_kvcache_no_alloc(const void* q, const void* kvcache, int64_t
  * mla_decode_with_kvcache_phase — the same decode in two separately launched
  * phases, for callers that time or overlap them: phases = 1 runs the split
  * kernel only (items covered by one worker get their final o / lse, the others
- * get fp32 partials in `workspace`); phases = 2 runs the merge of the partials
+ * get partials in `workspace`); phases = 2 runs the merge of the partials
  * only (it must follow phase 1 on the same stream with the same arguments);
  * phases = 3 runs both and is mla_decode_with_kvcache.  phases = 4 is the
  * single-launch decode (a fixed launch overhead matters: "Blackwell을 위한

@@ -83,7 +83,8 @@ int workers_for(const Shape& s, int request, int* W) {
 
 size_t workspace_for(const Shape& s, int dv, int W) {
   const size_t slots = (size_t)s.items + (size_t)W;
-  return slots * (size_t)s.rows * ((size_t)dv + 1) * sizeof(float);
+  // bf16 partial outputs, then their fp32 LSEs
+  return slots * (size_t)s.rows * ((size_t)dv * sizeof(uint16_t) + sizeof(float));
 }
 
 // Arrival counters of the single-launch mode, after the plan's rows: one per
@@ -259,8 +260,8 @@ int decode_impl(const void* q, const void* kvcache, int64_t num_pages, int page_
   a.o = static_cast<uint16_t*>(o);
   a.lse = lse;
   const size_t slots = (size_t)s.items + (size_t)num_workers;
-  a.part_o = static_cast<float*>(workspace);
-  a.part_lse = a.part_o + slots * (size_t)s.rows * kDv;
+  a.part_o = static_cast<uint16_t*>(workspace);
+  a.part_lse = reinterpret_cast<float*>(a.part_o + slots * (size_t)s.rows * kDv);
   // the plan carries the arrival counters (zeroed by mla_get_metadata)
   a.arrivals = const_cast<int32_t*>(plan) + (int64_t)kPlanWords * (num_workers + 1);
   a.fused = phases == 4;

@@ -47,8 +47,8 @@ struct DecodeArgs {
   const int32_t* num_splits;  // [items + 1]
   uint16_t* o;                // [items * M, 512]
   float* lse;                 // [items * M]
-  float* part_o;              // [slots * M, 512]
-  float* part_lse;            // [slots * M]
+  uint16_t* part_o;           // [slots * M, 512] bf16 partial outputs
+  float* part_lse;            // [slots * M] their LSEs
   int max_blocks;
   int batch;
   int s_q;

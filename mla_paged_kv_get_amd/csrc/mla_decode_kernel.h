@@ -37,7 +37,11 @@
 //    entries, are loaded from a valid row of the same sequence and masked to
 //    -inf, so no value outside the key set (e.g. NaN garbage) is ever read.
 //  * Runs covering a whole item write bf16 O and fp32 LSE directly; other runs
-//    write fp32 partials that combine_kernel merges (log-sum-exp).  In the
+//    write partials (O normalised by the run's own sum and rounded to bf16,
+//    LSE in fp32) that combine_kernel merges (log-sum-exp weights in fp32).
+//    Storing the partial O in the output's precision halves the bytes the
+//    split runs write and the merge reads; it adds at most one bf16 rounding
+//    of the largest partial to the merged value.  In the
 //    single-launch mode (FUSED) the last run of an item to finish merges them
 //    here instead: partials are stored and loaded at agent scope, which is
 //    coherent across the XCDs' L2s without write-back or invalidation, and
@@ -341,24 +345,38 @@ __device__ __forceinline__ void barrier_keep_loads() {
   asm volatile("s_barrier" ::: "memory");
 }
 
-// Partials of split items.  In the single-launch mode the runs of an item,
-// which may sit on different XCDs (each with its own L2, not coherent with the
-// others), exchange them through memory: stores and loads at agent scope
-// (sc1), so no L2 write-back or invalidate is needed.
+// Partials of split items: O in bf16 (the output's precision), LSE in fp32.
+// In the single-launch mode the runs of an item, which may sit on different
+// XCDs (each with its own L2, not coherent with the others), exchange them
+// through memory: stores and loads at agent scope (sc1), so no L2 write-back
+// or invalidate is needed.
+//
+// Eight bf16 partial values (16 bytes) as floats: v0 = the first four.
 template <bool kAgent>
-__device__ __forceinline__ floatx4 load_part4(const float* p) {
+__device__ __forceinline__ void load_part8(const uint16_t* p, floatx4& v0, floatx4& v1) {
+  unsigned w[4];
   if constexpr (!kAgent) {
-    return *reinterpret_cast<const floatx4*>(p);
+    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    w[0] = u.x;
+    w[1] = u.y;
+    w[2] = u.z;
+    w[3] = u.w;
   } else {
-    uint64_t* q = reinterpret_cast<uint64_t*>(const_cast<float*>(p));
+    uint64_t* q = reinterpret_cast<uint64_t*>(const_cast<uint16_t*>(p));
     const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    floatx4 v;
-    v[0] = __uint_as_float((unsigned)lo);
-    v[1] = __uint_as_float((unsigned)(lo >> 32));
-    v[2] = __uint_as_float((unsigned)hi);
-    v[3] = __uint_as_float((unsigned)(hi >> 32));
-    return v;
+    w[0] = (unsigned)lo;
+    w[1] = (unsigned)(lo >> 32);
+    w[2] = (unsigned)hi;
+    w[3] = (unsigned)(hi >> 32);
+  }
+  // a bf16 value is the upper half of the float it denotes
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    v0[2 * i] = __uint_as_float(w[i] << 16);
+    v0[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    v1[2 * i] = __uint_as_float(w[2 + i] << 16);
+    v1[2 * i + 1] = __uint_as_float(w[2 + i] & 0xffff0000u);
   }
 }
 template <bool kAgent>
@@ -370,12 +388,9 @@ __device__ __forceinline__ float load_part1(const float* p) {
     return __uint_as_float(__hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
   }
 }
-__device__ __forceinline__ void store_part4_agent(float* p, floatx4 v) {
-  uint64_t* q = reinterpret_cast<uint64_t*>(p);
-  const uint64_t lo = (uint64_t)__float_as_uint(v[0]) | ((uint64_t)__float_as_uint(v[1]) << 32);
-  const uint64_t hi = (uint64_t)__float_as_uint(v[2]) | ((uint64_t)__float_as_uint(v[3]) << 32);
-  __hip_atomic_store(q, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(q + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void store_part4_agent(uint16_t* p, bf16x4 v) {
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void store_part1_agent(float* p, float v) {
   __hip_atomic_store(reinterpret_cast<unsigned*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
@@ -400,13 +415,12 @@ __device__ __forceinline__ void merge_row(const DecodeArgs& a, int item, int slo
     float lk[8];
     floatx4 v0[8], v1[8];
     const int64_t stride = (int64_t)a.M * kDv;
-    const float* o_col = a.part_o + ((int64_t)slot0 * a.M + r) * kDv + 8 * lane;
+    const uint16_t* o_col = a.part_o + ((int64_t)slot0 * a.M + r) * kDv + 8 * lane;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       if (k < n) {
         lk[k] = load_part1<kAgent>(a.part_lse + (int64_t)(slot0 + k) * a.M + r);
-        v0[k] = load_part4<kAgent>(o_col + k * stride);
-        v1[k] = load_part4<kAgent>(o_col + k * stride + 4);
+        load_part8<kAgent>(o_col + k * stride, v0[k], v1[k]);
       }
     }
     float mx = -INFINITY;
@@ -449,14 +463,15 @@ __device__ __forceinline__ void merge_row(const DecodeArgs& a, int item, int slo
   float tot = 0.f;
   if (mx != -INFINITY) {
     const float* lse_col = a.part_lse + (int64_t)slot0 * a.M + r;
-    const float* o_col = a.part_o + ((int64_t)slot0 * a.M + r) * kDv + 8 * lane;
+    const uint16_t* o_col = a.part_o + ((int64_t)slot0 * a.M + r) * kDv + 8 * lane;
     const int64_t stride = (int64_t)a.M * kDv;
 #pragma unroll 4
     for (int k = 0; k < n; ++k) {
       const float lk = load_part1<kAgent>(lse_col + (int64_t)k * a.M);
       const float wk = lk == -INFINITY ? 0.f : expf(lk - mx);
       tot += wk;
-      const floatx4 v0 = load_part4<kAgent>(o_col + k * stride), v1 = load_part4<kAgent>(o_col + k * stride + 4);
+      floatx4 v0, v1;
+      load_part8<kAgent>(o_col + k * stride, v0, v1);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         acc[i] += wk * v0[i];
@@ -1628,8 +1643,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
       }
     };
 
-    // Finish the run of `item`: write O/LSE, or the fp32 partial when the item
-    // is split over several runs.
+    // Finish the run of `item`: write O/LSE, or the partial (bf16 O, fp32
+    // LSE) when the item is split over several runs.
     int merge_item[2] = {-1, -1};   // single launch: split items whose partials this workgroup merges
     int n_merge = 0;
     auto finish = [&](int item, int split) __attribute__((always_inline)) {
@@ -1682,21 +1697,21 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
               if constexpr (kFull) __builtin_amdgcn_sched_barrier(0);   // one block's registers at a time
             }
         } else {
-          float* orp = a.part_o + orow * kDv + c0;
+          uint16_t* orp = a.part_o + orow * kDv + c0;
 #pragma unroll
           for (int d = 0; d < kOBlocks; ++d)
 #pragma unroll
             for (int q4 = 0; q4 < (kWide ? 4 : 1); ++q4) {
-              floatx4 v;
+              bf16x4 v;
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
                 float e = oacc[d][4 * q4 + i];
                 if constexpr (kFull) e = agpr_read(e);
-                v[i] = e * inv;
+                v[i] = (__bf16)(e * inv);
               }
-              float* dst = orp + (kWide ? 32 * d + 8 * q4 : 16 * d);
+              uint16_t* dst = orp + (kWide ? 32 * d + 8 * q4 : 16 * d);
               if constexpr (FUSED) store_part4_agent(dst, v);
-              else *reinterpret_cast<floatx4*>(dst) = v;
+              else *reinterpret_cast<bf16x4*>(dst) = v;
               if constexpr (kFull) __builtin_amdgcn_sched_barrier(0);
             }
         }

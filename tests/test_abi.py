@@ -65,11 +65,12 @@ def test_plan_dims():
 
 def test_workspace_bytes():
     l = _lib.lib()
-    # (items + W) partial slots of rows x 513 floats
-    assert l.mla_workspace_bytes(64, 1, 16, 1, 0, 512, 256) == (64 + 256) * 16 * 513 * 4
-    assert l.mla_workspace_bytes(16, 8, 1024, 1, 2048, 512, 256) == (128 + 256) * 128 * 513 * 4
+    # (items + W) partial slots of rows x (512 bf16 outputs + one fp32 LSE)
+    row = 512 * 2 + 4
+    assert l.mla_workspace_bytes(64, 1, 16, 1, 0, 512, 256) == (64 + 256) * 16 * row
+    assert l.mla_workspace_bytes(16, 8, 1024, 1, 2048, 512, 256) == (128 + 256) * 128 * row
     assert l.mla_workspace_bytes(64, 1, 16, 1, 0, 512, 0) == 0
-    assert l.mla_workspace_bytes(8, 1, 32, 4, 0, 512, 64) == (32 + 64) * 32 * 513 * 4   # h_kv = 4
+    assert l.mla_workspace_bytes(8, 1, 32, 4, 0, 512, 64) == (32 + 64) * 32 * row   # h_kv = 4
 
 
 DUMMY = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails its host checks
@@ -142,7 +143,7 @@ def test_no_alloc_scratch_size_matches_header():
     (dict(causal=2), _lib.MLA_ERR_INVALID_ARGUMENT),
     (dict(idx=DUMMY, topk=16, causal=1), _lib.MLA_ERR_INVALID_ARGUMENT),
     (dict(W=0), _lib.MLA_ERR_INVALID_ARGUMENT),
-    # partials of (items + W) x 128 rows x 513 floats: 4096 + 8 slots need 1.08 GB
+    # partials of (items + W) x 128 rows x 1028 bytes: 4096 + 8 slots need 0.54 GB
     (dict(batch=4096, h_q=128), _lib.MLA_ERR_SCRATCH_LIMIT),
     (dict(W=1 << 14, h_q=128), _lib.MLA_ERR_SCRATCH_LIMIT),
 ])
