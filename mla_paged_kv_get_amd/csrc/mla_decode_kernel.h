@@ -404,55 +404,63 @@ __device__ __forceinline__ void write_empty_row(const DecodeArgs& a, int item, i
   if (lane == 0) a.lse[orow] = -INFINITY;
 }
 
-// Log-sum-exp merge of the n partials of row r of an item, one wave per row,
-// 8 columns per lane.  The partial LSEs are read lane-parallel for the max;
-// the weighted sum of the partial rows keeps 4 reads in flight.
-template <bool kAgent>
-__device__ __forceinline__ void merge_row(const DecodeArgs& a, int item, int slot0, int n, int r, int lane) {
-  const int64_t orow = q_row(a, item, r);
-  if (n <= 8) {
-    // all reads in one go (one memory latency), then the arithmetic
-    float lk[8];
-    floatx4 v0[8], v1[8];
-    const int64_t stride = (int64_t)a.M * kDv;
-    const uint16_t* o_col = a.part_o + ((int64_t)slot0 * a.M + r) * kDv + 8 * lane;
+// Log-sum-exp merge of n <= N partials of row r of an item (one wave, 8
+// columns per lane): all N reads go out together, unconditionally (reads past
+// the n-th repeat the last partial and are not used), so the merge waits for
+// one memory latency; then the arithmetic.
+template <int N, bool kAgent>
+__device__ __forceinline__ void merge_row_small(const DecodeArgs& a, int64_t orow, int slot0, int n, int r,
+                                                int lane) {
+  float lk[N];
+  floatx4 v0[N], v1[N];
+  const int64_t stride = (int64_t)a.M * kDv;
+  const uint16_t* o_col = a.part_o + ((int64_t)slot0 * a.M + r) * kDv + 8 * lane;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+  for (int k = 0; k < N; ++k) {
+    const int kk = k < n ? k : n - 1;
+    lk[k] = load_part1<kAgent>(a.part_lse + (int64_t)(slot0 + kk) * a.M + r);
+    load_part8<kAgent>(o_col + kk * stride, v0[k], v1[k]);
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < N; ++k)
+    if (k < n) mx = fmaxf(mx, lk[k]);
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  float tot = 0.f;
+  if (mx != -INFINITY) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
       if (k < n) {
-        lk[k] = load_part1<kAgent>(a.part_lse + (int64_t)(slot0 + k) * a.M + r);
-        load_part8<kAgent>(o_col + k * stride, v0[k], v1[k]);
-      }
-    }
-    float mx = -INFINITY;
+        const float wk = lk[k] == -INFINITY ? 0.f : expf(lk[k] - mx);
+        tot += wk;
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
-      if (k < n) mx = fmaxf(mx, lk[k]);
-    float acc[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    float tot = 0.f;
-    if (mx != -INFINITY) {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        if (k < n) {
-          const float wk = lk[k] == -INFINITY ? 0.f : expf(lk[k] - mx);
-          tot += wk;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            acc[i] += wk * v0[k][i];
-            acc[4 + i] += wk * v1[k][i];
-          }
+        for (int i = 0; i < 4; ++i) {
+          acc[i] += wk * v0[k][i];
+          acc[4 + i] += wk * v1[k][i];
         }
       }
     }
-    const float inv = tot > 0.f ? 1.f / tot : 0.f;
-    bf16x8 v;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = (__bf16)(acc[i] * inv);
-    *reinterpret_cast<bf16x8*>(a.o + orow * kDv + 8 * lane) = v;
-    if (lane == 0) a.lse[orow] = tot > 0.f ? mx + logf(tot) : -INFINITY;
-    return;
   }
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  bf16x8 v;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (__bf16)(acc[i] * inv);
+  *reinterpret_cast<bf16x8*>(a.o + orow * kDv + 8 * lane) = v;
+  if (lane == 0) a.lse[orow] = tot > 0.f ? mx + logf(tot) : -INFINITY;
+}
+
+// Log-sum-exp merge of the n >= 1 partials of row r of an item, one wave per
+// row, 8 columns per lane.  Up to 8 partials: one batch of reads (sized 2, 4
+// or 8).  More: the partial LSEs are read lane-parallel for the max, and the
+// weighted sum of the partial rows keeps 4 reads in flight.
+template <bool kAgent>
+__device__ __forceinline__ void merge_row(const DecodeArgs& a, int item, int slot0, int n, int r, int lane) {
+  const int64_t orow = q_row(a, item, r);
+  if (n <= 2) return merge_row_small<2, kAgent>(a, orow, slot0, n, r, lane);
+  if (n <= 4) return merge_row_small<4, kAgent>(a, orow, slot0, n, r, lane);
+  if (n <= 8) return merge_row_small<8, kAgent>(a, orow, slot0, n, r, lane);
   float mx = -INFINITY;
   for (int k = lane; k < n; k += 64) mx = fmaxf(mx, load_part1<kAgent>(a.part_lse + (int64_t)(slot0 + k) * a.M + r));
 #pragma unroll
