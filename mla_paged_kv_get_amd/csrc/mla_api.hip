@@ -81,10 +81,16 @@ int workers_for(const Shape& s, int request, int* W) {
   return MLA_OK;
 }
 
+// Rows per partial slot: the 128-row variant writes its partials in blocks of
+// 32 rows, so its slots are rounded up to a whole number of blocks.
+int part_rows_of(const Shape& s) {
+  return s.variant == kVariantRows128 ? (s.rows + 31) / 32 * 32 : s.rows;
+}
+
 size_t workspace_for(const Shape& s, int dv, int W) {
   const size_t slots = (size_t)s.items + (size_t)W;
   // bf16 partial outputs, then their fp32 LSEs
-  return slots * (size_t)s.rows * ((size_t)dv * sizeof(uint16_t) + sizeof(float));
+  return slots * (size_t)part_rows_of(s) * ((size_t)dv * sizeof(uint16_t) + sizeof(float));
 }
 
 // Arrival counters of the single-launch mode, after the plan's rows: one per
@@ -260,11 +266,13 @@ int decode_impl(const void* q, const void* kvcache, int64_t num_pages, int page_
   a.o = static_cast<uint16_t*>(o);
   a.lse = lse;
   const size_t slots = (size_t)s.items + (size_t)num_workers;
+  a.part_rows = part_rows_of(s);
   a.part_o = static_cast<uint16_t*>(workspace);
-  a.part_lse = reinterpret_cast<float*>(a.part_o + slots * (size_t)s.rows * kDv);
+  a.part_lse = reinterpret_cast<float*>(a.part_o + slots * (size_t)a.part_rows * kDv);
   // the plan carries the arrival counters (zeroed by mla_get_metadata)
   a.arrivals = const_cast<int32_t*>(plan) + (int64_t)kPlanWords * (num_workers + 1);
   a.fused = phases == 4;
+  a.part_blocks = s.variant == kVariantRows128 && !a.fused;
   a.max_blocks = max_blocks;
   a.batch = batch;
   a.s_q = s_q;

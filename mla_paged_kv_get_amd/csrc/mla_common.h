@@ -47,8 +47,10 @@ struct DecodeArgs {
   const int32_t* num_splits;  // [items + 1]
   uint16_t* o;                // [items * M, 512]
   float* lse;                 // [items * M]
-  uint16_t* part_o;           // [slots * M, 512] bf16 partial outputs
-  float* part_lse;            // [slots * M] their LSEs
+  uint16_t* part_o;           // [slots * part_rows, 512] bf16 partial outputs
+  float* part_lse;            // [slots * part_rows] their LSEs
+  int part_rows;              // rows per partial slot: M, or M rounded up to 32 (128-row variant)
+  int part_blocks;            // partial O in 32-row blocks in accumulator order (128-row, two launches)
   int max_blocks;
   int batch;
   int s_q;

@@ -413,12 +413,12 @@ __device__ __forceinline__ void merge_row_small(const DecodeArgs& a, int64_t oro
                                                 int lane) {
   float lk[N];
   floatx4 v0[N], v1[N];
-  const int64_t stride = (int64_t)a.M * kDv;
-  const uint16_t* o_col = a.part_o + ((int64_t)slot0 * a.M + r) * kDv + 8 * lane;
+  const int64_t stride = (int64_t)a.part_rows * kDv;
+  const uint16_t* o_col = a.part_o + ((int64_t)slot0 * a.part_rows + r) * kDv + 8 * lane;
 #pragma unroll
   for (int k = 0; k < N; ++k) {
     const int kk = k < n ? k : n - 1;
-    lk[k] = load_part1<kAgent>(a.part_lse + (int64_t)(slot0 + kk) * a.M + r);
+    lk[k] = load_part1<kAgent>(a.part_lse + (int64_t)(slot0 + kk) * a.part_rows + r);
     load_part8<kAgent>(o_col + kk * stride, v0[k], v1[k]);
   }
   float mx = -INFINITY;
@@ -462,7 +462,8 @@ __device__ __forceinline__ void merge_row(const DecodeArgs& a, int item, int slo
   if (n <= 4) return merge_row_small<4, kAgent>(a, orow, slot0, n, r, lane);
   if (n <= 8) return merge_row_small<8, kAgent>(a, orow, slot0, n, r, lane);
   float mx = -INFINITY;
-  for (int k = lane; k < n; k += 64) mx = fmaxf(mx, load_part1<kAgent>(a.part_lse + (int64_t)(slot0 + k) * a.M + r));
+  for (int k = lane; k < n; k += 64)
+    mx = fmaxf(mx, load_part1<kAgent>(a.part_lse + (int64_t)(slot0 + k) * a.part_rows + r));
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d, 64));
   float acc[8];
@@ -470,12 +471,12 @@ __device__ __forceinline__ void merge_row(const DecodeArgs& a, int item, int slo
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
   float tot = 0.f;
   if (mx != -INFINITY) {
-    const float* lse_col = a.part_lse + (int64_t)slot0 * a.M + r;
-    const uint16_t* o_col = a.part_o + ((int64_t)slot0 * a.M + r) * kDv + 8 * lane;
-    const int64_t stride = (int64_t)a.M * kDv;
+    const float* lse_col = a.part_lse + (int64_t)slot0 * a.part_rows + r;
+    const uint16_t* o_col = a.part_o + ((int64_t)slot0 * a.part_rows + r) * kDv + 8 * lane;
+    const int64_t stride = (int64_t)a.part_rows * kDv;
 #pragma unroll 4
     for (int k = 0; k < n; ++k) {
-      const float lk = load_part1<kAgent>(lse_col + (int64_t)k * a.M);
+      const float lk = load_part1<kAgent>(lse_col + (int64_t)k * a.part_rows);
       const float wk = lk == -INFINITY ? 0.f : expf(lk - mx);
       tot += wk;
       floatx4 v0, v1;
@@ -1665,7 +1666,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
       }
       const int nsplit = slot1 - slot0;
       const bool final_out = nsplit == 1;
-      const int64_t part_base = (int64_t)(slot0 + split) * a.M;
+      const int64_t part_base = (int64_t)(slot0 + split) * a.part_rows;
       // row sums over the lanes and waves holding the row (same order everywhere)
       float l_tot = l_lane;
       if constexpr (!kWide) l_tot = xor16_sum(l_tot);
@@ -1706,6 +1707,12 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
             }
         } else {
           uint16_t* orp = a.part_o + orow * kDv + c0;
+          // 128-row variant, two launches: the wave's 32 rows as one block of
+          // 16384 values in accumulator order (value i of piece (d, q4) of
+          // lane l at ((4 d + q4) * 64 + l) * 4 + i), so that every store
+          // instruction writes 512 contiguous bytes; combine_kernel reads the
+          // blocks back.
+          uint16_t* blk = a.part_o + (part_base + row0 + 32 * pair) * kDv + 4 * lane;
 #pragma unroll
           for (int d = 0; d < kOBlocks; ++d)
 #pragma unroll
@@ -1717,7 +1724,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
                 if constexpr (kFull) e = agpr_read(e);
                 v[i] = (__bf16)(e * inv);
               }
-              uint16_t* dst = orp + (kWide ? 32 * d + 8 * q4 : 16 * d);
+              uint16_t* dst = (kFull && !FUSED) ? blk + (4 * d + q4) * 256 : orp + (kWide ? 32 * d + 8 * q4 : 16 * d);
               if constexpr (FUSED) store_part4_agent(dst, v);
               else *reinterpret_cast<bf16x4*>(dst) = v;
               if constexpr (kFull) __builtin_amdgcn_sched_barrier(0);
