@@ -153,11 +153,12 @@ int mla_get_metadata(const int32_t* cache_seqlens, int batch, int s_q,
 
 /*
  * mla_workspace_bytes — host only; bytes of the decode scratch buffer: room
- * for (items + W) partial results of (rows per item) rows, each dv bf16
- * output values and one fp32 LSE, i.e. (items + W) x rows x (2 dv + 4) bytes
- * (split runs write one each; at most items + W - 1 are used).  The partial
- * outputs are rounded to bf16 once, like the final output; the merge weights
- * them in fp32.
+ * for (items + W) partial results of R rows, each dv bf16 output values and
+ * one fp32 LSE, i.e. (items + W) x R x (2 dv + 4) bytes (split runs write one
+ * each; at most items + W - 1 are used).  R = rows per item, rounded up to a
+ * multiple of 32 for items of more than 64 rows (their partials are written
+ * in 32-row blocks).  The partial outputs are rounded to bf16 once, like the
+ * final output; the merge weights them in fp32.
  */
 size_t mla_workspace_bytes(int batch, int s_q, int num_q_rows, int h_kv, int topk,
                            int dv, int num_workers);

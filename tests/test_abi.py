@@ -71,6 +71,9 @@ def test_workspace_bytes():
     assert l.mla_workspace_bytes(16, 8, 1024, 1, 2048, 512, 256) == (128 + 256) * 128 * row
     assert l.mla_workspace_bytes(64, 1, 16, 1, 0, 512, 0) == 0
     assert l.mla_workspace_bytes(8, 1, 32, 4, 0, 512, 64) == (32 + 64) * 32 * row   # h_kv = 4
+    # items of more than 64 rows: slots of whole 32-row blocks
+    assert l.mla_workspace_bytes(2, 1, 100, 1, 0, 512, 8) == (2 + 8) * 128 * row
+    assert l.mla_workspace_bytes(2, 1, 64, 1, 0, 512, 8) == (2 + 8) * 64 * row
 
 
 DUMMY = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails its host checks

@@ -212,6 +212,18 @@ def test_causal_edges(h_q, s_q):
     compare(w, o, lse, label=f"causal h_q={h_q} s_q={s_q}")
 
 
+@pytest.mark.parametrize("h_q,s_q,causal", [(100, 1, False), (40, 3, True)])
+def test_wide_rows_not_multiple_of_32(h_q, s_q, causal):
+    # 100 and 120 rows per item: the 128-row variant's partials are 32-row blocks,
+    # the last one part padding; whole items and several split counts
+    L = [1, 65, 300, 2049, 0]
+    w = wl.build("rows-odd", 50 + s_q, np.array(L), B=len(L), s_q=s_q, h_q=h_q, num_pages=60,
+                 causal=causal, poison=True)
+    for W in (None, 3, 7):
+        o, lse, _ = run_gpu(Dev(w), num_workers=W)
+        compare(w, o, lse, label=f"h_q={h_q} s_q={s_q} W={W}")
+
+
 def test_noncausal_multi_token():
     w = wl.build("mtp-noncausal", 33, np.array([100, 7, 300]), B=3, s_q=2, h_q=64, num_pages=20)
     o, lse, _ = run_gpu(Dev(w))

@@ -57,10 +57,14 @@ def _cases():
                                           h_kv=2, num_pages=60, poison=True, d_qk=512), 19),
         ("wide-splits", lambda: wl.build("wsplits", 97, np.array([4096, 1, 2000, 777, 64, 65, 0]), B=7,
                                          s_q=1, h_q=128, num_pages=200, poison=True), 37),
+        # 120 rows per item: the two-launch merge reads 32-row blocks of which the
+        # last is part padding, the single launch row-major partials
+        ("wide-odd-rows", lambda: wl.build("wodd", 98, np.array([3000, 1, 777, 65, 0]), B=5, s_q=3,
+                                           h_q=40, num_pages=100, causal=True, poison=True), 23),
     ]
 
 
-@pytest.mark.parametrize("case", range(7))
+@pytest.mark.parametrize("case", range(8))
 def test_single_launch_equals_two_launches(case):
     name, make, W = _cases()[case]
     w = make()
