@@ -227,7 +227,7 @@ def merge_splits(o_parts: np.ndarray, lse_parts: np.ndarray):
 # Split-KV scheduler ("tile_scheduler_metadata" / "num_splits")
 # --------------------------------------------------------------------------
 PLAN_WORDS = 8        # int32 words per plan row
-PLAN_VERSION = 2
+PLAN_VERSION = 3
 
 
 def plan(lengths, num_workers: int, overhead: int):
@@ -235,15 +235,19 @@ def plan(lengths, num_workers: int, overhead: int):
 
     Each item (a sequence; in sparse mode a query token) of length ``len``
     has n = ceil(len / 64) blocks and costs ``overhead + n`` units, the
-    overhead standing for loading its queries and writing its result.  Items
-    are laid end to end on a cost axis of total T.  The first W' = min(W, T)
-    workers share the axis evenly: worker w owns the units
-    [floor(w T / W'), floor((w + 1) T / W')), at least one unit each; the
-    others get nothing.  Block b of item i occupies the unit
-    C_i + overhead + b, C_i being the item's start.  A worker processes, for
-    every item, the blocks whose units fall inside its interval (a contiguous
-    run, possibly empty); the non-empty runs of one item, in worker order, are
-    the item's splits, numbered 0, 1, ...
+    overhead standing for loading its queries (a lead of ceil(overhead / 2)
+    units before its blocks) and writing its result (a tail of
+    floor(overhead / 2) units after them).  Items are laid end to end on a
+    cost axis of total T.  The first W' = min(W, T) workers share the axis
+    evenly: worker w owns the units [floor(w T / W'), floor((w + 1) T / W')),
+    at least one unit each; the others get nothing.  Block b of item i
+    occupies the unit C_i + lead + b, C_i being the item's start.  A worker
+    processes, for every item, the blocks whose units fall inside its
+    interval (a contiguous run, possibly empty); the non-empty runs of one
+    item, in worker order, are the item's splits, numbered 0, 1, ...  (Every
+    run loads its queries and writes its result, a split one included; with
+    the overhead at both ends of an item, the workers that start or end
+    inside an item are charged alike.)
 
     Returns (plan int32 [(W + 1) * 8], num_splits int32 [num_items + 1]):
       plan row 0  = [W, overhead, W', num_items, version, 64, T mod 2^32,
@@ -258,6 +262,7 @@ def plan(lengths, num_workers: int, overhead: int):
     c = int(overhead)
     if W < 1 or c < 1:
         raise ValueError("need num_workers >= 1 and overhead >= 1")
+    lead = (c + 1) // 2          # the tail, c - lead units, follows the blocks
     nblk = [-(-L // PAGE) if L > 0 else 0 for L in lengths]
     start = []
     acc = 0
@@ -279,7 +284,7 @@ def plan(lengths, num_workers: int, overhead: int):
         for i, n in enumerate(nblk):
             if n == 0:
                 continue
-            first = start[i] + c                  # unit of block 0
+            first = start[i] + lead               # unit of block 0
             b_lo = min(max(lo - first, 0), n)
             b_hi = min(max(hi - first, 0), n)
             if b_lo < b_hi:

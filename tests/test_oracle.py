@@ -471,7 +471,7 @@ def _read_plan_examples():
 
 def test_plan_hand_worked_examples():
     exs = _read_plan_examples()
-    assert len(exs) == 4
+    assert len(exs) == 5
     for e in exs:
         p, ns = orc.plan(e["lengths"], e["workers"][0], e["overhead"][0])
         rows = p.reshape(-1, 8)
@@ -543,7 +543,7 @@ def test_plan_invariants_random():
         if rng.random() < 0.3:
             lengths[int(rng.integers(0, B))] = 0
         W = int(rng.integers(1, 70))
-        c = int(rng.integers(1, 4))
+        c = int(rng.integers(1, 7))
         _check_plan_invariants(lengths, W, c)
 
 
@@ -551,7 +551,8 @@ def test_plan_invariants_exhaustive_pairs():
     for L0 in range(0, 200, 7):
         for L1 in range(0, 200, 11):
             for W in (1, 2, 3, 5, 8):
-                _check_plan_invariants([L0, L1], W, 2)
+                for c in (2, 3):
+                    _check_plan_invariants([L0, L1], W, c)
 
 
 def test_decode_by_plan_equals_decode():
