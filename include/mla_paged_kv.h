@@ -119,16 +119,19 @@ int mla_plan_num_workers(int plan_words, int batch, int s_q, int num_q_rows, int
  * Rule: item i has n_i blocks (dense: ceil(cache_seqlens[i / h_kv] / 64);
  * sparse: ceil(topk / 64) + ceil(topk2 / 64), topk2 being the length of the
  * auxiliary index lists of the dual-cache decode, 0 otherwise) and costs
- * overhead + n_i units (overhead = 1 block
- * for items of at most 16 query rows, 4 for wider items); items are laid end to end on a cost axis (total T); the first
- * W' = min(W, T) workers share it evenly, worker w owning the units
- * [floor(w T / W'), floor((w + 1) T / W')); block b of item i sits on unit
- * (start of item i) + overhead + b, and a worker gets the blocks on its units.
+ * overhead + n_i units (overhead = 1 block for items of at most 16 query
+ * rows, 3 for bf16 items over 64 rows, 4 for the others), the overhead split
+ * into a lead of ceil(overhead / 2) units before the item's blocks and a tail
+ * of floor(overhead / 2) units after them; items are laid end to end on a cost
+ * axis (total T); the first W' = min(W, T) workers share it evenly, worker w
+ * owning the units [floor(w T / W'), floor((w + 1) T / W')); block b of item i
+ * sits on unit (start of item i) + lead + b, and a worker gets the blocks on
+ * its units.
  *
  *   topk, topk2    index-list lengths of the sparse modes (0 for dense; topk2
  *                  only with topk > 0)
  *   plan           [out_plan_words] int32, device (output).  Row 0 = {W, per-run
- *                  overhead in blocks, W', items, version 2, 64, total cost T
+ *                  overhead in blocks, W', items, version 3, 64, total cost T
  *                  mod 2^32, T div 2^32} (the cost axis is 64-bit); row
  *                  1 + w = {first item, its first block, last item, end block
  *                  (exclusive) in the last item, split number of the run in

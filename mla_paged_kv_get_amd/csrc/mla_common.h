@@ -20,7 +20,7 @@ constexpr int kRowBytes8 = 656;
 constexpr int kRaw8Bytes = kPage * kRowBytes8;     // 41984 B per 64-row tile as copied
 constexpr int kRaw8ScaleOff = kPage * 640;         // scales of a copied tile: [4 blocks][64 rows] float32
 constexpr int kPlanWords = 8;
-constexpr int kPlanVersion = 2;
+constexpr int kPlanVersion = 3;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -140,11 +140,12 @@ enum Variant : int {
                          // rows over every key and output column
 };
 constexpr int variant_rows(int v) { return v == kVariantRows16 ? 16 : v == kVariantRows64 ? 64 : 128; }
-// Plan cost of starting an item, in blocks (measured: an item boundary costs
-// about 1.6 tiles of a 16-row worker; for 64-row and 128-row items 4 balanced
-// the MTP decode best among the values tried, 1 to 8, while the wide
-// one-token decodes lost under 3% against 2).
-constexpr int variant_overhead(int v) { return v == kVariantRows16 ? 1 : 4; }
+// Plan cost of a run of an item, in blocks, laid out half before and half
+// after its blocks (measured: an item boundary costs about 1.6 tiles of a
+// 16-row worker, where 1 unit ahead of the blocks balanced best; 128-row
+// items balanced best at 3, split 2 + 1, among 2 to 6, and the FP8 64-row
+// items at 4, split 2 + 2).
+constexpr int variant_overhead(int v) { return v == kVariantRows16 ? 1 : v == kVariantRows128 ? 3 : 4; }
 // kv_format 0: bf16 rows; 1: packed FP8 rows (no 128-row variant).
 inline int pick_variant(int rows_per_item, int kv_format) {
   if (rows_per_item <= 16) return kVariantRows16;

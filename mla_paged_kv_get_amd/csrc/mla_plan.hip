@@ -2,14 +2,15 @@
 // topnet.top, installation-and-use section, step 2: it returns the tile
 // scheduler metadata and num_splits).  The pages do not say how work is split;
 // this kernel implements the rule stated in the C header:
-//   n_i = ceil(len_i / 64) blocks, item cost = overhead + n_i, items laid end
-//   to end on a cost axis (start C_i, total T); the first W' = min(W, T)
-//   workers share the axis evenly, worker w owning units
-//   [floor(w T / W'), floor((w + 1) T / W')); block b of item i sits on unit
-//   C_i + overhead + b.
+//   n_i = ceil(len_i / 64) blocks, item cost = overhead + n_i (a lead of
+//   ceil(overhead / 2) units before the blocks, a tail of floor(overhead / 2)
+//   after them), items laid end to end on a cost axis (start C_i, total T);
+//   the first W' = min(W, T) workers share the axis evenly, worker w owning
+//   units [floor(w T / W'), floor((w + 1) T / W')); block b of item i sits on
+//   unit C_i + lead + b.
 // One workgroup computes it from closed forms: unit x belongs to worker
 // floor(((x + 1) W' - 1) / T), so the workers touching item i's blocks are
-// owner(C_i + overhead) .. owner(C_{i+1} - 1), every one of them with at
+// owner(C_i + lead) .. owner(C_{i+1} - tail - 1), every one of them with at
 // least one block, and the split count and split numbers follow without a walk.
 // A worker's first and last items are the least and greatest items that reach
 // it.  With up to kScatterW workers and no item reaching more than
@@ -134,6 +135,8 @@ __device__ void plan_body(const int32_t* __restrict__ seqlens, int topk, int num
   const int tid = threadIdx.x;
   const int per = (num_items + kPlanThreads - 1) / kPlanThreads;
   const int i0 = min(tid * per, num_items), i1 = min(i0 + per, num_items);
+  // an item's overhead: cl units before its blocks, ct after them
+  const int cl = (c + 1) / 2, ct = c / 2;
   const bool can_mark = first_s != nullptr && W <= kScatterW;
   if (can_mark) {
     for (int w = tid; w < W; w += kPlanThreads) {
@@ -179,7 +182,7 @@ __device__ void plan_body(const int32_t* __restrict__ seqlens, int topk, int num
   int nsplit = 0;
   int span = 0;
   for (int i = i0; i < i1; ++i) {
-    const Ax first = start[i] + c, end = start[i + 1];
+    const Ax first = start[i] + cl, end = start[i + 1] - ct;
     if (end > first) {
       const int n = owner(end - 1) - owner(first) + 1;
       nsplit += n;
@@ -196,7 +199,7 @@ __device__ void plan_body(const int32_t* __restrict__ seqlens, int topk, int num
   int srun = sincl - nsplit;
   for (int i = i0; i < i1; ++i) {
     num_splits[i] = srun;
-    const Ax first = start[i] + c, end = start[i + 1];
+    const Ax first = start[i] + cl, end = start[i + 1] - ct;
     if (end > first) {
       const int wl = owner(first), wh = owner(end - 1);
       srun += wh - wl + 1;
@@ -224,10 +227,10 @@ __device__ void plan_body(const int32_t* __restrict__ seqlens, int topk, int num
       if (first_s[w] < num_items) {
         first_item = first_s[w];
         last_item = last_s[w];
-        const Ax ff = start[first_item] + c;
+        const Ax ff = start[first_item] + cl;
         first_blk = (int)(max(lo, ff) - ff);
         split = w - owner(ff);
-        last_end = (int)(min(hi, start[last_item + 1]) - start[last_item] - c);
+        last_end = (int)(min(hi, start[last_item + 1] - ct) - start[last_item] - cl);
       }
     } else if (lo < hi) {
       // Last item starting at or before lo.
@@ -237,11 +240,11 @@ __device__ void plan_body(const int32_t* __restrict__ seqlens, int topk, int num
         if (start[m] <= lo) a = m; else b = m - 1;
       }
       for (int i = a; i < num_items && start[i] < hi; ++i) {
-        const Ax bl = max(lo, start[i] + c), bh = min(hi, start[i + 1]);
+        const Ax bl = max(lo, start[i] + cl), bh = min(hi, start[i + 1] - ct);
         if (bl < bh) {
           first_item = i;
-          first_blk = (int)(bl - start[i] - c);
-          split = w - owner(start[i] + c);
+          first_blk = (int)(bl - start[i] - cl);
+          split = w - owner(start[i] + cl);
           break;
         }
       }
@@ -254,10 +257,10 @@ __device__ void plan_body(const int32_t* __restrict__ seqlens, int topk, int num
           if (start[m] < hi) a = m; else b = m - 1;
         }
         for (int i = a; i >= first_item; --i) {
-          const Ax bl = max(lo, start[i] + c), bh = min(hi, start[i + 1]);
+          const Ax bl = max(lo, start[i] + cl), bh = min(hi, start[i + 1] - ct);
           if (bl < bh) {
             last_item = i;
-            last_end = (int)(bh - start[i] - c);
+            last_end = (int)(bh - start[i] - cl);
             break;
           }
         }
