@@ -30,6 +30,59 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
 // merge_row's (the same weights, summed in the same order), so both merges
 // give the same bits.
 constexpr int kBlockQuarters = 4;
+
+// Weighted sum of the block partials k of one thread's two chunks (values
+// 8 c .. 8 c + 7 of chunk c = v[i]; the first four belong to block row ja, the
+// last four to jb), partial weights from s_w[k].
+__device__ __forceinline__ void add_block_partial(const uint4 (&v)[2], float wa, float wb, float (&acc)[2][8]) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const unsigned w4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+    // a bf16 value is the upper half of the float it denotes
+    acc[i][0] += wa * __uint_as_float(w4[0] << 16);
+    acc[i][1] += wa * __uint_as_float(w4[0] & 0xffff0000u);
+    acc[i][2] += wa * __uint_as_float(w4[1] << 16);
+    acc[i][3] += wa * __uint_as_float(w4[1] & 0xffff0000u);
+    acc[i][4] += wb * __uint_as_float(w4[2] << 16);
+    acc[i][5] += wb * __uint_as_float(w4[2] & 0xffff0000u);
+    acc[i][6] += wb * __uint_as_float(w4[3] << 16);
+    acc[i][7] += wb * __uint_as_float(w4[3] & 0xffff0000u);
+  }
+}
+
+// Items of at most N <= 8 splits: every read of the block goes out at once
+// (the N partials' chunks, the last partial standing in for those past n, and
+// thread (j, p)'s LSE of partial p of row j), so the merge waits for memory
+// once instead of three times (LSEs for the maxima, LSEs for the weights,
+// then the partials).  Same weights and order of sums as the general loop.
+template <int N>
+__device__ __forceinline__ void merge_block_batch(const DecodeArgs& a, const float* lse0,
+                                                  const uint16_t* blk0, int64_t stride, int n,
+                                                  int tid, int ja, int jb, float* s_mx,
+                                                  float (*s_w)[32], float (&acc)[2][8],
+                                                  float& tot) {
+  uint4 v[N][2];
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    const int kk = k < n ? k : n - 1;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) v[k][i] = *reinterpret_cast<const uint4*>(blk0 + kk * stride + 2048 * i);
+  }
+  const int j = tid >> 3, p = tid & 7;
+  const float lk = lse0[(int64_t)(p < n ? p : n - 1) * a.part_rows + j];
+  float mx = p < n ? lk : -INFINITY;
+#pragma unroll
+  for (int d = 1; d < 8; d <<= 1) mx = fmaxf(mx, __shfl_xor(mx, d, 64));
+  if (p == 0) s_mx[j] = mx;
+  if (p < n) s_w[p][j] = (mx == -INFINITY || lk == -INFINITY) ? 0.f : expf(lk - mx);
+  __syncthreads();
+  if (tid < 32)
+    for (int k = 0; k < n; ++k) tot += s_w[k][tid];
+#pragma unroll
+  for (int k = 0; k < N; ++k)
+    if (k < n) add_block_partial(v[k], s_w[k][ja], s_w[k][jb], acc);
+}
+
 __global__ __launch_bounds__(256) void combine_blocks_kernel(DecodeArgs a) {
   const int item = blockIdx.x;
   const int r0 = 32 * (blockIdx.y / kBlockQuarters);   // first row of the block inside the item
@@ -50,15 +103,6 @@ __global__ __launch_bounds__(256) void combine_blocks_kernel(DecodeArgs a) {
   __shared__ float s_w[32][32];   // weights of partials k0 .. k0 + 31 of the block's rows
   __shared__ __attribute__((aligned(16))) uint16_t s_out[32 * kRowPad];
   const float* lse0 = a.part_lse + (int64_t)slot0 * a.part_rows + r0;
-  // row maxima: 8 threads per row, each over every 8th partial
-  {
-    const int j = tid >> 3, p = tid & 7;
-    float mx = -INFINITY;
-    for (int k = p; k < n; k += 8) mx = fmaxf(mx, lse0[(int64_t)k * a.part_rows + j]);
-#pragma unroll
-    for (int d = 1; d < 8; d <<= 1) mx = fmaxf(mx, __shfl_xor(mx, d, 64));
-    if (p == 0) s_mx[j] = mx;
-  }
   // This thread's two chunks of 8 values: chunk c = 512 cq + tid + 256 i of
   // the block covers values 8 c .. 8 c + 7, the pieces of writing lanes
   // 2 c mod 64 and 2 c mod 64 + 1 (rows (2 c) mod 32 and (2 c + 1) mod 32 of
@@ -72,36 +116,40 @@ __global__ __launch_bounds__(256) void combine_blocks_kernel(DecodeArgs a) {
   const int ja = (2 * tid) & 31, jb = (2 * tid + 1) & 31;   // the same for both chunks
   const uint16_t* blk0 = a.part_o + ((int64_t)slot0 * a.part_rows + r0) * kDv + 8 * (512 * cq + tid);
   const int64_t stride = (int64_t)a.part_rows * kDv;
-  for (int k0 = 0; k0 < n; k0 += 32) {
-    const int kn = min(32, n - k0);
-    __syncthreads();   // s_mx is written; the previous weights are used
-    for (int e = tid; e < 32 * kn; e += 256) {
-      const int k = e >> 5, j = e & 31;
-      const float lk = lse0[(int64_t)(k0 + k) * a.part_rows + j];
-      s_w[k][j] = (s_mx[j] == -INFINITY || lk == -INFINITY) ? 0.f : expf(lk - s_mx[j]);
+  if (n <= 2) {
+    merge_block_batch<2>(a, lse0, blk0, stride, n, tid, ja, jb, s_mx, s_w, acc, tot);
+  } else if (n <= 4) {
+    merge_block_batch<4>(a, lse0, blk0, stride, n, tid, ja, jb, s_mx, s_w, acc, tot);
+  } else if (n <= 8) {
+    merge_block_batch<8>(a, lse0, blk0, stride, n, tid, ja, jb, s_mx, s_w, acc, tot);
+  } else {
+    // row maxima: 8 threads per row, each over every 8th partial
+    {
+      const int j = tid >> 3, p = tid & 7;
+      float mx = -INFINITY;
+      for (int k = p; k < n; k += 8) mx = fmaxf(mx, lse0[(int64_t)k * a.part_rows + j]);
+#pragma unroll
+      for (int d = 1; d < 8; d <<= 1) mx = fmaxf(mx, __shfl_xor(mx, d, 64));
+      if (p == 0) s_mx[j] = mx;
     }
-    __syncthreads();
-    if (tid < 32)
-      for (int k = 0; k < kn; ++k) tot += s_w[k][tid];
+    for (int k0 = 0; k0 < n; k0 += 32) {
+      const int kn = min(32, n - k0);
+      __syncthreads();   // s_mx is written; the previous weights are used
+      for (int e = tid; e < 32 * kn; e += 256) {
+        const int k = e >> 5, j = e & 31;
+        const float lk = lse0[(int64_t)(k0 + k) * a.part_rows + j];
+        s_w[k][j] = (s_mx[j] == -INFINITY || lk == -INFINITY) ? 0.f : expf(lk - s_mx[j]);
+      }
+      __syncthreads();
+      if (tid < 32)
+        for (int k = 0; k < kn; ++k) tot += s_w[k][tid];
 #pragma unroll 4
-    for (int k = 0; k < kn; ++k) {
-      const uint16_t* src = blk0 + (int64_t)(k0 + k) * stride;
-      uint4 v[2];
+      for (int k = 0; k < kn; ++k) {
+        const uint16_t* src = blk0 + (int64_t)(k0 + k) * stride;
+        uint4 v[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) v[i] = *reinterpret_cast<const uint4*>(src + 2048 * i);
-      const float wa = s_w[k][ja], wb = s_w[k][jb];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const unsigned w4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-        // a bf16 value is the upper half of the float it denotes
-        acc[i][0] += wa * __uint_as_float(w4[0] << 16);
-        acc[i][1] += wa * __uint_as_float(w4[0] & 0xffff0000u);
-        acc[i][2] += wa * __uint_as_float(w4[1] << 16);
-        acc[i][3] += wa * __uint_as_float(w4[1] & 0xffff0000u);
-        acc[i][4] += wb * __uint_as_float(w4[2] << 16);
-        acc[i][5] += wb * __uint_as_float(w4[2] & 0xffff0000u);
-        acc[i][6] += wb * __uint_as_float(w4[3] << 16);
-        acc[i][7] += wb * __uint_as_float(w4[3] & 0xffff0000u);
+        for (int i = 0; i < 2; ++i) v[i] = *reinterpret_cast<const uint4*>(src + 2048 * i);
+        add_block_partial(v, s_w[k][ja], s_w[k][jb], acc);
       }
     }
   }
