@@ -298,6 +298,76 @@ __device__ __attribute__((noinline)) void plan_body_wide(const int32_t* seqlens,
                      nullptr, run, T, sums_b, span_w);
 }
 
+// The same schedule for at most kPlanThreads items and workers on a 32-bit
+// axis with W' T < 2^32 (every decode batch of up to 256 sequences or query
+// tokens): thread t holds item t (n blocks, start `run`) and worker t, so no
+// thread loops over items or workers and every division goes by
+// multiplication.  Item t marks the workers its blocks reach in LDS
+// (s_first / s_last), and worker t reads its first and last item from there.
+// s_start has kPlanThreads + 1 entries; s_first and s_last kPlanThreads.
+__device__ __forceinline__ void plan_small(int num_items, int W, int c, int32_t* __restrict__ plan,
+                                           int32_t* __restrict__ num_splits, int n, int run, int T,
+                                           int* s_start, int* s_first, int* s_last, int* sums_b) {
+  const int tid = threadIdx.x;
+  const int cl = (c + 1) / 2, ct = c / 2;   // an item's overhead: cl units before its blocks, ct after them
+  const int We = min(W, T);
+  const uint32_t mT = T > 0 ? 0xffffffffu / (uint32_t)T : 0u;
+  const uint32_t mW = We > 0 ? 0xffffffffu / (uint32_t)We : 0u;
+  auto owner = [&](int x) -> int {   // worker owning unit x (T >= 1 when any item has a block)
+    return (int)udiv((uint32_t)(x + 1) * (uint32_t)We - 1u, (uint32_t)T, mT);
+  };
+  const bool has_item = tid < num_items;
+  if (has_item) s_start[tid] = run;
+  if (tid == 0) s_start[num_items] = T;
+  if (tid < W) {
+    s_first[tid] = num_items;   // none
+    s_last[tid] = -1;
+  }
+  const int wl = has_item && n > 0 ? owner(run + cl) : 0;
+  const int ns = has_item && n > 0 ? owner(run + cl + n - 1) - wl + 1 : 0;
+  int S;
+  const int sincl = block_inclusive_scan(ns, sums_b, S);   // its barrier publishes the stores above
+  if (has_item) num_splits[tid] = sincl - ns;
+  if (tid == 0) num_splits[num_items] = S;
+  for (int w = wl; w < wl + ns; ++w) {
+    atomicMin(&s_first[w], tid);
+    atomicMax(&s_last[w], tid);
+  }
+  __syncthreads();
+  if (tid < W) {
+    int4 r0 = make_int4(-1, 0, -1, 0);
+    int4 r1 = make_int4(0, 0, 0, 0);
+    const int fi = s_first[tid];
+    if (fi < num_items) {
+      const int li = s_last[tid];
+      const int lo = (int)udiv((uint32_t)tid * (uint32_t)T, (uint32_t)We, mW);
+      const int hi = (int)udiv((uint32_t)(tid + 1) * (uint32_t)T, (uint32_t)We, mW);
+      const int ff = s_start[fi] + cl;
+      r0 = make_int4(fi, max(lo, ff) - ff, li, min(hi, s_start[li + 1] - ct) - s_start[li] - cl);
+      r1.x = tid - owner(ff);
+    }
+    int32_t* row = plan + kPlanWords * (1 + tid);
+    row[0] = r0.x;
+    row[1] = r0.y;
+    row[2] = r0.z;
+    row[3] = r0.w;
+    row[4] = r1.x;
+    row[5] = 0;
+    row[6] = 0;
+    row[7] = 0;
+  }
+  if (tid == 0) {
+    plan[0] = W;
+    plan[1] = c;
+    plan[2] = We;
+    plan[3] = num_items;
+    plan[4] = kPlanVersion;
+    plan[5] = kPage;
+    plan[6] = T;
+    plan[7] = 0;
+  }
+}
+
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ seqlens,
                                                             int topk, int num_items, int item_div,
                                                             int W, int c,
@@ -330,7 +400,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
   }
   int64_t total;
   const int64_t run = block_exclusive_scan64(local, sums_lo, sums_hi, total);
-  if (total <= 0x7fffffff) {
+  if (num_items <= kPlanThreads && W <= kPlanThreads && total <= 0x7fffffff &&
+      (uint64_t)min((int64_t)W, total) * (uint64_t)total < (1ull << 32)) {
+    // one item per thread: its block count is the one parked by this thread
+    plan_small(num_items, W, c, plan, num_splits, i1 > i0 ? start32[i0] : 0, (int)run, (int)total,
+               start32, start32 + kStartInts, start32 + kStartInts + kScatterW, sums_b);
+  } else if (total <= 0x7fffffff) {
     plan_body<int>(seqlens, topk, num_items, item_div, W, c, plan, num_splits, start32,
                    start32 + kStartInts, start32 + kStartInts + kScatterW, (int)run, (int)total,
                    sums_b, span_w);
