@@ -63,7 +63,8 @@ extern "C" {
 #define MLA_D_QK 576
 #define MLA_D_V 512
 #define MLA_PLAN_WORDS 8             /* int32 words per plan row */
-#define MLA_PLAN_MAX_ITEMS 16384     /* items one metadata call can plan */
+#define MLA_PLAN_MAX_ITEMS 1048576   /* items one metadata call can plan */
+#define MLA_PLAN_LDS_ITEMS 16384     /* beyond this many items, at most 4096 workers */
 #define MLA_NO_ALLOC_SCRATCH_BYTES ((size_t)128 << 20)   /* per GPU, see below */
 
 /* Human-readable text of a status code (static storage, never NULL). */
@@ -90,8 +91,10 @@ const char* mla_status_string(int status);
  *                        plan does not know the cache format, so it covers the
  *                        finest row tiling any decode of this shape uses)
  *   out_num_items        items of the call; num_splits holds items + 1 words (host)
- * Needs the current HIP device only when num_workers_request == 0.  A call
- * with more than MLA_PLAN_MAX_ITEMS items returns MLA_ERR_UNSUPPORTED.
+ * Needs the current HIP device only when num_workers_request == 0.  The
+ * metadata call plans at most MLA_PLAN_MAX_ITEMS items, and with more than
+ * MLA_PLAN_LDS_ITEMS items at most 4096 workers; beyond, it returns
+ * MLA_ERR_UNSUPPORTED.
  */
 int mla_plan_dims(int batch, int s_q, int num_q_rows, int h_kv, int topk,
                   int num_workers_request, int* out_num_workers,
@@ -147,8 +150,11 @@ int mla_plan_num_workers(int plan_words, int batch, int s_q, int num_q_rows, int
  * only read it, except the single-launch decode (phases = 4), which counts
  * finished runs in the plan's arrival counters and leaves them zero when it
  * completes: single-launch calls that share one plan must not overlap (two
- * streams), while two-launch calls may.  More than MLA_PLAN_MAX_ITEMS items:
- * MLA_ERR_UNSUPPORTED.  Any lengths up to 2^31 - 1 are planned exactly (the
+ * streams), while two-launch calls may.  More than MLA_PLAN_MAX_ITEMS items,
+ * or more than MLA_PLAN_LDS_ITEMS items with W > 4096: MLA_ERR_UNSUPPORTED
+ * (batches past MLA_PLAN_LDS_ITEMS items, such as a sparse prefill of that
+ * many query tokens, are planned by a kernel that keeps no per-item state
+ * in LDS).  Any lengths up to 2^31 - 1 are planned exactly (the
  * total cost may pass 2^31; block numbers inside an item stay below 2^25).
  */
 int mla_get_metadata(const int32_t* cache_seqlens, int batch, int s_q,

@@ -12,6 +12,7 @@
 
 namespace mla {
 int plan_max_items();
+int plan_large_max_workers(int num_items);
 }
 
 namespace {
@@ -152,6 +153,7 @@ int mla_get_metadata(const int32_t* cache_seqlens, int batch, int s_q, int num_q
   const int st = shape_of(batch, s_q, num_q_rows, h_kv, topk, &s);
   if (st != MLA_OK) return st;
   if (s.items > mla::plan_max_items()) return MLA_ERR_UNSUPPORTED;
+  if (num_workers > mla::plan_large_max_workers(s.items)) return MLA_ERR_UNSUPPORTED;
   // Sparse items: the tiles of the main list, then those of the auxiliary list
   // (dual cache), each list in 64-key tiles.
   int64_t tile_keys = 0;

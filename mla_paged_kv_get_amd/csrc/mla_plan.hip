@@ -27,7 +27,8 @@ namespace {
 
 constexpr int kPlanThreads = 256;
 constexpr int kPlanWaves = kPlanThreads / 64;
-constexpr int kPlanMaxItems = 16384;
+constexpr int kPlanMaxItems = 16384;       // item starts in LDS up to this many items
+constexpr int kPlanLargeItems = 1 << 20;   // beyond: plan_kernel_large, up to this many
 constexpr int kScatterW = 4096;
 constexpr int kScatterSpan = 32;
 
@@ -415,15 +416,138 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
   }
 }
 
+// Batches of more than kPlanMaxItems items (a sparse prefill of that many
+// query tokens): the same schedule with no per-item state in LDS.  Each
+// thread walks a contiguous range of items three times (block counts come
+// from the lengths each time): the cost of its range; the split counts of
+// its items, with each item marking the workers its blocks reach (LDS min /
+// max of the item index, so W <= kScatterW); then each item writes the row
+// words of the workers it is the first or the last item of, and num_splits.
+// Worker threads write the rows of workers with no item and the zero words.
+// The 64-bit axis throughout; the range costs are scanned by one thread.
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel_large(const int32_t* __restrict__ seqlens,
+                                                                  int topk, int num_items, int item_div,
+                                                                  int W, int c,
+                                                                  int32_t* __restrict__ plan,
+                                                                  int32_t* __restrict__ num_splits,
+                                                                  int32_t* __restrict__ counters,
+                                                                  int num_counters) {
+  __shared__ int first_s[kScatterW], last_s[kScatterW];
+  __shared__ int64_t s_run[kPlanThreads + 1];
+  __shared__ int sums_b[kPlanWaves];
+  const int tid = threadIdx.x;
+  const int per = (num_items + kPlanThreads - 1) / kPlanThreads;
+  const int i0 = min(tid * per, num_items), i1 = min(i0 + per, num_items);
+  const int cl = (c + 1) / 2, ct = c / 2;   // an item's overhead: cl units before its blocks, ct after them
+
+  for (int i = tid; i < num_counters; i += kPlanThreads) counters[i] = 0;
+  for (int w = tid; w < W; w += kPlanThreads) {
+    first_s[w] = num_items;   // none
+    last_s[w] = -1;
+  }
+  int64_t local = 0;
+  for (int i = i0; i < i1; ++i) local += c + item_blocks(seqlens, topk, item_div, i);
+  s_run[tid] = local;
+  __syncthreads();
+  if (tid == 0) {
+    int64_t r = 0;
+    for (int t = 0; t < kPlanThreads; ++t) {
+      const int64_t v = s_run[t];
+      s_run[t] = r;
+      r += v;
+    }
+    s_run[kPlanThreads] = r;
+  }
+  __syncthreads();
+  const int64_t run = s_run[tid], T = s_run[kPlanThreads];
+  const int64_t We = min((int64_t)W, T);
+  auto owner = [&](int64_t x) -> int { return (int)floor_div<true>((x + 1) * We - 1, T); };
+  auto unit0 = [&](int w) -> int64_t { return floor_div<true>((int64_t)w * T, We); };
+
+  // split counts, and the marks
+  int nsplit = 0;
+  int64_t C = run;
+  for (int i = i0; i < i1; ++i) {
+    const int n = item_blocks(seqlens, topk, item_div, i);
+    if (n > 0) {
+      const int wl = owner(C + cl), wh = owner(C + cl + n - 1);
+      nsplit += wh - wl + 1;
+      for (int w = wl; w <= wh; ++w) {
+        atomicMin(&first_s[w], i);
+        atomicMax(&last_s[w], i);
+      }
+    }
+    C += c + n;
+  }
+  int S;
+  const int sincl = block_inclusive_scan(nsplit, sums_b, S);   // its barrier publishes the marks
+
+  // num_splits, and the row words of the workers whose first or last item it is
+  int srun = sincl - nsplit;
+  C = run;
+  for (int i = i0; i < i1; ++i) {
+    num_splits[i] = srun;
+    const int n = item_blocks(seqlens, topk, item_div, i);
+    if (n > 0) {
+      const int64_t first = C + cl, end = C + cl + n;
+      const int wl = owner(first), wh = owner(end - 1);
+      for (int w = wl; w <= wh; ++w) {
+        int32_t* row = plan + kPlanWords * (1 + w);
+        if (first_s[w] == i) {
+          row[0] = i;
+          row[1] = (int)(max(unit0(w), first) - first);
+          row[4] = w - wl;
+        }
+        if (last_s[w] == i) {
+          row[2] = i;
+          row[3] = (int)(min(unit0(w + 1), end) - first);
+        }
+      }
+      srun += wh - wl + 1;
+    }
+    C += c + n;
+  }
+  if (tid == 0) num_splits[num_items] = S;
+  for (int w = tid; w < W; w += kPlanThreads) {
+    int32_t* row = plan + kPlanWords * (1 + w);
+    if (first_s[w] == num_items) {
+      row[0] = -1;
+      row[1] = 0;
+      row[2] = -1;
+      row[3] = 0;
+      row[4] = 0;
+    }
+    row[5] = 0;
+    row[6] = 0;
+    row[7] = 0;
+  }
+  if (tid == 0) {
+    plan[0] = W;
+    plan[1] = c;
+    plan[2] = (int32_t)We;
+    plan[3] = num_items;
+    plan[4] = kPlanVersion;
+    plan[5] = kPage;
+    plan[6] = (int32_t)(uint32_t)((uint64_t)T & 0xffffffffu);   // T, low and high words
+    plan[7] = (int32_t)((uint64_t)T >> 32);
+  }
+}
+
 }  // namespace
 
-int plan_max_items() { return kPlanMaxItems; }
+int plan_max_items() { return kPlanLargeItems; }
+int plan_large_max_workers(int num_items) { return num_items > kPlanMaxItems ? kScatterW : (1 << 20); }
 
 hipError_t launch_plan(const int32_t* seqlens, int topk, int num_items, int item_div, int num_workers,
                        int overhead, int32_t* plan, int32_t* num_splits, int32_t* counters,
                        int num_counters, hipStream_t stream) {
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, seqlens, topk, num_items,
-                     item_div, num_workers, overhead, plan, num_splits, counters, num_counters);
+  if (num_items > kPlanMaxItems)
+    hipLaunchKernelGGL(plan_kernel_large, dim3(1), dim3(kPlanThreads), 0, stream, seqlens, topk,
+                       num_items, item_div, num_workers, overhead, plan, num_splits, counters,
+                       num_counters);
+  else
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, seqlens, topk, num_items,
+                       item_div, num_workers, overhead, plan, num_splits, counters, num_counters);
   return hipGetLastError();
 }
 

@@ -233,18 +233,23 @@ def test_metadata_rejects():
 
 
 def test_metadata_item_cap():
-    # one call plans at most MLA_PLAN_MAX_ITEMS = 16384 items (dense: batch * h_kv;
-    # sparse: batch * s_q * h_kv); one more is rejected before anything is enqueued
+    # one call plans at most MLA_PLAN_MAX_ITEMS = 2^20 items (dense: batch * h_kv;
+    # sparse: batch * s_q * h_kv), and past MLA_PLAN_LDS_ITEMS = 16384 items with
+    # at most 4096 workers; the rest is rejected before anything is enqueued
     l = _lib.lib()
-    cap = 16384
+    cap, lds = 1 << 20, 16384
     assert l.mla_get_metadata(DUMMY, cap + 1, 1, 16, 1, 0, 0, 8, DUMMY, DUMMY, None) == _lib.MLA_ERR_UNSUPPORTED
     assert l.mla_get_metadata(DUMMY, cap // 2 + 1, 1, 32, 2, 0, 0, 8, DUMMY, DUMMY, None) == _lib.MLA_ERR_UNSUPPORTED
     assert l.mla_get_metadata(DUMMY, 1, cap + 1, (cap + 1) * 16, 1, 64, 0, 8, DUMMY, DUMMY,
                               None) == _lib.MLA_ERR_UNSUPPORTED
     assert l.mla_get_metadata(DUMMY, 2, cap // 2 + 1, (cap // 2 + 1) * 16, 1, 64, 32, 8, DUMMY, DUMMY,
                               None) == _lib.MLA_ERR_UNSUPPORTED
+    assert l.mla_get_metadata(DUMMY, lds + 1, 1, 16, 1, 0, 0, 4097, DUMMY, DUMMY, None) == _lib.MLA_ERR_UNSUPPORTED
+    assert l.mla_get_metadata(DUMMY, 1, lds + 1, (lds + 1) * 16, 1, 64, 0, 4097, DUMMY, DUMMY,
+                              None) == _lib.MLA_ERR_UNSUPPORTED
     hdr = open(os.path.join(ROOT, "include", "mla_paged_kv.h")).read()
-    assert re.search(r"#define MLA_PLAN_MAX_ITEMS\s+16384\b", hdr)
+    assert re.search(r"#define MLA_PLAN_MAX_ITEMS\s+1048576\b", hdr)
+    assert re.search(r"#define MLA_PLAN_LDS_ITEMS\s+16384\b", hdr)
 
 
 def test_debug_and_validate_reject():

@@ -71,6 +71,39 @@ def test_plan_bit_exact_division_paths(lengths, W):
     assert (ns.cpu().numpy() == ref_ns).all()
 
 
+@pytest.mark.parametrize("case", ["dense", "dense-grouped", "sparse", "sparse-dual", "axis-past-2-31"])
+def test_plan_bit_exact_past_lds_items(case):
+    # more than 16384 items: the scheduler that keeps no per-item state in LDS
+    m = _m()
+    rng = np.random.default_rng(91)
+    topk, topk2, s_q, h_q, h_kv, W = None, 0, 1, 16, 1, 256
+    if case == "dense":
+        lengths = [int(x) for x in rng.integers(0, 700, 17000)]
+    elif case == "dense-grouped":                       # 9000 sequences x 2 latent heads
+        lengths, h_q, h_kv, W = [int(x) for x in rng.integers(1, 3000, 9000)], 32, 2, 64
+    elif case == "sparse":                              # one sequence, 16500 query tokens
+        lengths, topk, s_q, W = [20000], 100, 16500, 37
+    elif case == "sparse-dual":
+        lengths, topk, topk2, s_q, W = [5000, 9000], 64, 32, 8300, 200
+    else:
+        lengths, W = [int(x) for x in rng.integers(2**30, 2**31 - 1, 16400)], 64
+    sl = i32_dev(np.array(lengths))
+    plan, ns = m.get_mla_metadata(sl, s_q * h_q // h_kv, h_kv, s_q=s_q, topk=topk, num_workers=W,
+                                  topk2=topk2)
+    torch.cuda.synchronize()
+    p = plan.cpu().numpy()
+    if topk:
+        tiles = -(-topk // 64) + -(-topk2 // 64)
+        items = [64 * tiles] * (len(lengths) * s_q * h_kv)
+    else:
+        items = [L for L in lengths for _ in range(h_kv)]
+    assert len(items) > 16384
+    ref_p, ref_ns = orc.plan(items, W, int(p[1]))
+    assert (p[:ref_p.size] == ref_p).all(), f"{case}: {(p[:ref_p.size] != ref_p).sum()} plan words differ"
+    assert (p[ref_p.size:] == 0).all()          # the single-launch arrival counters
+    assert (ns.cpu().numpy() == ref_ns).all()
+
+
 @pytest.mark.parametrize("case", ["dense-random", "dense-halves", "sparse", "search"])
 def test_plan_bit_exact_axis_past_2_31(case):
     # total cost past 2^31 (lengths near 2^31): the scheduler's 64-bit axis
@@ -280,6 +313,36 @@ def test_sparse_prefill_sampled():
     ends = sorted({int(x) for x in rows[:, 0] if x >= 0} | {int(x) for x in rows[:, 2] if x >= 0})
     toks = sorted(set(np.linspace(0, 4095, 40).astype(int)) | set(ends[:: max(1, len(ends) // 24)]))
     compare(w, o, lse, items=[(0, int(t)) for t in toks], label="sparse-prefill")
+
+
+def test_sparse_prefill_past_lds_items():
+    # 16500 query tokens of 16 rows (16500 items: the plan without per-item LDS
+    # state; over 64 items per worker): every output finite, tokens on both
+    # sides of item 16384 and spread over the rest against the oracle, and the
+    # single-launch decode bit for bit equal to the two launches
+    T, ctx, k = 16500, 100, 64
+    w = wl.build("prefill-16k", 62, np.array([ctx + T]), B=1, s_q=T, h_q=16,
+                 num_pages=(ctx + T) // 64 + 4, topk=None)
+    rng = np.random.default_rng(63)
+    idx = np.full((1, T, k), -1, dtype=np.int32)
+    for t in range(T):
+        n = min(k, ctx + t + 1)
+        idx[0, t, :n] = rng.choice(ctx + t + 1, n, replace=False)
+    w.indices = idx
+    d = Dev(w)
+    o, lse, plan = run_gpu(d)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    toks = sorted({0, 1, 16383, 16384, 16385, T - 1} | set(int(x) for x in np.linspace(0, T - 1, 14)))
+    compare(w, o, lse, items=[(0, t) for t in toks], label="prefill T=16500")
+    m = _m()
+    ws = torch.empty(m.workspace_bytes(1, T, T * 16, 1, k, 512, int(plan[0][0].item())), dtype=torch.uint8,
+                     device="cuda")
+    o1 = torch.empty_like(o)
+    lse1 = torch.empty_like(lse)
+    m.mla_decode_with_kvcache(d.q, d.kv, d.bt, d.sl, 512, plan[0], plan[1], causal=w.causal, indices=d.idx,
+                              out=(o1, lse1), workspace=ws, phases=4)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o.view(torch.int16)) and torch.equal(lse1, lse)
 
 
 @pytest.mark.parametrize("h_q", [16, 128])
