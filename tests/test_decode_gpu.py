@@ -71,6 +71,23 @@ def test_plan_bit_exact_division_paths(lengths, W):
     assert (ns.cpu().numpy() == ref_ns).all()
 
 
+@pytest.mark.parametrize("items,W", [(256, 256), (257, 256), (256, 257), (1, 256), (255, 1),
+                                     (16384, 64), (16385, 64), (16385, 2048)])
+def test_plan_bit_exact_path_boundaries(items, W):
+    # the edges between the scheduler's paths: one item and one worker per
+    # thread (up to 256 of each), items in LDS (up to 16384), no per-item LDS state
+    m = _m()
+    rng = np.random.default_rng(items + W)
+    lengths = [int(x) for x in rng.integers(0, 900, items)]
+    sl = i32_dev(np.array(lengths))
+    plan, ns = m.get_mla_metadata(sl, 16, 1, num_workers=W)
+    torch.cuda.synchronize()
+    p = plan.cpu().numpy()
+    ref_p, ref_ns = orc.plan(lengths, W, int(p[1]))
+    assert (p[:ref_p.size] == ref_p).all(), f"{(p[:ref_p.size] != ref_p).sum()} plan words differ"
+    assert (ns.cpu().numpy() == ref_ns).all()
+
+
 @pytest.mark.parametrize("case", ["dense", "dense-grouped", "sparse", "sparse-dual", "axis-past-2-31"])
 def test_plan_bit_exact_past_lds_items(case):
     # more than 16384 items: the scheduler that keeps no per-item state in LDS
