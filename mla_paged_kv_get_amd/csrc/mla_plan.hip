@@ -336,23 +336,26 @@ __device__ __forceinline__ void plan_small(int num_items, int W, int c, int32_t*
   }
   __syncthreads();
   if (tid < W) {
-    int4 r0 = make_int4(-1, 0, -1, 0);
-    int4 r1 = make_int4(0, 0, 0, 0);
-    const int fi = s_first[tid];
+    // {first item, its first block, last item, end block in it, split number
+    // of the first run}, or no blocks
+    int fi = s_first[tid], first_blk = 0, li = -1, last_end = 0, split = 0;
     if (fi < num_items) {
-      const int li = s_last[tid];
+      li = s_last[tid];
       const int lo = (int)udiv((uint32_t)tid * (uint32_t)T, (uint32_t)We, mW);
       const int hi = (int)udiv((uint32_t)(tid + 1) * (uint32_t)T, (uint32_t)We, mW);
       const int ff = s_start[fi] + cl;
-      r0 = make_int4(fi, max(lo, ff) - ff, li, min(hi, s_start[li + 1] - ct) - s_start[li] - cl);
-      r1.x = tid - owner(ff);
+      first_blk = max(lo, ff) - ff;
+      last_end = min(hi, s_start[li + 1] - ct) - s_start[li] - cl;
+      split = tid - owner(ff);
+    } else {
+      fi = -1;
     }
     int32_t* row = plan + kPlanWords * (1 + tid);
-    row[0] = r0.x;
-    row[1] = r0.y;
-    row[2] = r0.z;
-    row[3] = r0.w;
-    row[4] = r1.x;
+    row[0] = fi;
+    row[1] = first_blk;
+    row[2] = li;
+    row[3] = last_end;
+    row[4] = split;
     row[5] = 0;
     row[6] = 0;
     row[7] = 0;
