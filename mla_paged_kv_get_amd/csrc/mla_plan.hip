@@ -20,6 +20,10 @@
 // when the total fits 31 bits (every realistic batch) the axis is kept in
 // 32-bit integers, otherwise in 64-bit ones (item starts in LDS as int64, no
 // marking).  Block numbers inside an item always fit 32 bits.
+// Three paths give the same words: up to 256 items and workers on a narrow
+// 32-bit axis, one item and one worker per thread (plan_small); up to
+// kPlanMaxItems items, the item starts in LDS (plan_body); beyond, a second
+// kernel with no per-item state in LDS (plan_kernel_large).
 #include "mla_common.h"
 
 namespace mla {
