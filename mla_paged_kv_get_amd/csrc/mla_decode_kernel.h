@@ -2050,6 +2050,12 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
           ++t;
           if (ends) break;
         }
+        // The output blocks stay in their AGPRs into the run's end: without
+        // this the register allocator moves some of them to VGPRs after the
+        // last PV MFMAs, then needs an AGPR back for each read below, parks a
+        // whole block in scratch and reloads it behind the partial stores.
+#pragma unroll
+        for (int d = 0; d < kOBlocks; ++d) asm volatile("" : "+a"(oacc[d]));
         finish(run_item, run_split);
         if (!has_next) break;
         cur_lim = key_limit(cur_item);
