@@ -291,6 +291,14 @@ __device__ __forceinline__ floatx16 mfma_v0(bf16x8 a, bf16x8 b) {
   return d;
 }
 __device__ __forceinline__ void mfma_result_wait() { asm volatile("s_nop 15\n\ts_nop 3" ::: "memory"); }
+// This lane's index, produced where it is used by an instruction the
+// compiler cannot hoist, so that per-lane LDS addresses built from it are
+// remade at each use instead of staying live (and spilled) across a tile loop.
+__device__ __forceinline__ int lane_here() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
 __device__ __forceinline__ float agpr_zero() {
   float r;
   asm volatile("v_accvgpr_write_b32 %0, 0" : "=a"(r));
@@ -971,7 +979,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     // MFMAs before the result is needed.
     auto translate_read = [&](int item, int blk, int slot) __attribute__((always_inline)) -> int {
       const SparseList sl = sparse_list(item, blk);
-      const int rr = 16 * wave + (lane & 15);
+      const int rr = 16 * wave + (lane_here() & 15);
       return sl.e0 + rr < sl.n ? idxbuf[slot & 3][rr] : -1;
     };
     auto translate_use = [&](int item, int blk, int slot, int idx, unsigned char* vslot) __attribute__((always_inline)) {
@@ -981,7 +989,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
       sparse_rows(item, blk, bt_row, Ls, base);
       const bool ok = sparse_key_valid(idx, Ls);
       copy_to_lds_4(bt_row + ((ok ? idx : 0) >> 6), lds_addr(&pgbuf[slot & 1][wave][0]));
-      if (lane < 16) vslot[16 * wave + (lane & 15)] = ok ? 1 : 0;
+      if (lane < 16) vslot[16 * wave + (lane_here() & 15)] = ok ? 1 : 0;
     };
     auto translate_lds = [&](int item, int blk, int slot, unsigned char* vslot) __attribute__((always_inline)) {
       if constexpr (kWide && sparse) translate_use(item, blk, slot, translate_read(item, blk, slot), vslot);
@@ -995,7 +1003,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
       const SparseList sl = sparse_list(item, blk);
 #pragma unroll
       for (int r = 0; r < C::kOffs; ++r) {
-        const int row = r < C::kLaneRows ? cp_row[r] : sc_row;
+        const int row = r < C::kLaneRows ? 8 * (2 * wave + r) + (lane_here() >> 3) : sc_row;
         rr.idx[r] = sl.e0 + row < sl.n ? idxbuf[slot & 3][row] : -1;
         rr.page[r] = pgbuf[slot & 1][row >> 4][row & 15];
       }
