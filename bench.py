@@ -107,7 +107,8 @@ def run_workload(torch, m, w, steps, warmup, ncopies=NCOPIES):
         aux = (_to_dev(torch, kv2.view(np.int16), torch.bfloat16), _to_dev(torch, bt2.astype(np.int32)),
                _to_dev(torch, sl2.astype(np.int32)), _to_dev(torch, idx2.astype(np.int32)))
         topk2 = idx2.shape[2]
-    plan, ns = m.get_mla_metadata(sl, rows, h_kv, s_q=w.s_q, topk=w.topk, topk2=topk2)
+    fp8 = w.kv.dtype == np.uint8
+    plan, ns = m.get_mla_metadata(sl, rows, h_kv, s_q=w.s_q, topk=w.topk, topk2=topk2, fp8=fp8)
     W = int(plan[0].item())                   # header word 0
     B = w.B
     o = torch.empty((B, w.s_q, w.h_q, 512), dtype=torch.bfloat16, device="cuda")
@@ -116,7 +117,7 @@ def run_workload(torch, m, w, steps, warmup, ncopies=NCOPIES):
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
 
     def plan_call(k):
-        return m.get_mla_metadata(sl, rows, h_kv, s_q=w.s_q, topk=w.topk, topk2=topk2)
+        return m.get_mla_metadata(sl, rows, h_kv, s_q=w.s_q, topk=w.topk, topk2=topk2, fp8=fp8)
 
     def decode_call(k, p, n, phases):
         c = k % ncopies

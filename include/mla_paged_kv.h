@@ -101,6 +101,19 @@ int mla_plan_dims(int batch, int s_q, int num_q_rows, int h_kv, int topk,
                   int* out_plan_words, int* out_num_items);
 
 /*
+ * mla_plan_dims_fp8 — mla_plan_dims for decodes over a packed FP8 cache
+ * (mla_decode_with_kvcache_fp8).  The pages' metadata call takes no cache
+ * format; this library's decode picks its row tiling by the format (packed
+ * FP8 items of more than 16 rows run in 64-row tiles, bf16 items of more than
+ * 64 rows in 128-row tiles), and the default worker count follows the tiling:
+ * one workgroup per CU for every worker's row tiles.  Same arguments, outputs
+ * and status codes.
+ */
+int mla_plan_dims_fp8(int batch, int s_q, int num_q_rows, int h_kv, int topk,
+                      int num_workers_request, int* out_num_workers,
+                      int* out_plan_words, int* out_num_items);
+
+/*
  * mla_plan_num_workers — host only; the W of a plan of `plan_words` words made
  * for this call shape (inverse of mla_plan_dims), or -1 if the size does not
  * fit the shape.
@@ -160,6 +173,18 @@ int mla_plan_num_workers(int plan_words, int batch, int s_q, int num_q_rows, int
 int mla_get_metadata(const int32_t* cache_seqlens, int batch, int s_q,
                      int num_q_rows, int h_kv, int topk, int topk2, int num_workers,
                      int32_t* plan, int32_t* num_splits, void* stream);
+
+/*
+ * mla_get_metadata_fp8 — mla_get_metadata for decodes over a packed FP8 cache
+ * (no auxiliary lists: topk2 = 0).  The same rule with the overhead of the
+ * FP8 decode's row tiling (1 block for items of at most 16 rows, else 4);
+ * with W from mla_plan_dims_fp8 every row tile of every worker has a CU at
+ * once.  Any plan, of either call, is valid for either decode; this one
+ * balances the FP8 decode.
+ */
+int mla_get_metadata_fp8(const int32_t* cache_seqlens, int batch, int s_q,
+                         int num_q_rows, int h_kv, int topk, int num_workers,
+                         int32_t* plan, int32_t* num_splits, void* stream);
 
 /*
  * mla_workspace_bytes — host only; bytes of the decode scratch buffer: room

@@ -23,7 +23,8 @@ MLA_ERR_SCRATCH_LIMIT = 5
 NO_ALLOC_SCRATCH_BYTES = 128 << 20     # MLA_NO_ALLOC_SCRATCH_BYTES
 
 EXPORTS = (
-    "mla_status_string", "mla_plan_dims", "mla_plan_num_workers", "mla_get_metadata",
+    "mla_status_string", "mla_plan_dims", "mla_plan_dims_fp8", "mla_plan_num_workers", "mla_get_metadata",
+    "mla_get_metadata_fp8",
     "mla_workspace_bytes",
     "mla_decode_with_kvcache", "mla_decode_with_kvcache_no_alloc", "mla_decode_with_kvcache_phase",
     "mla_decode_with_kvcache_fp8",
@@ -39,8 +40,10 @@ _ip = ctypes.POINTER(ctypes.c_int)
 _SIGS = {
     "mla_status_string": (ctypes.c_char_p, [_c_int]),
     "mla_plan_dims": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _ip, _ip, _ip]),
+    "mla_plan_dims_fp8": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _ip, _ip, _ip]),
     "mla_plan_num_workers": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
     "mla_get_metadata": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp]),
+    "mla_get_metadata_fp8": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp]),
     "mla_workspace_bytes": (ctypes.c_size_t, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
     "mla_decode_with_kvcache": (_c_int, [
         _vp, _vp, _c_i64, _c_int, _vp, _c_int, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,

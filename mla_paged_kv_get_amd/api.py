@@ -45,11 +45,11 @@ def _i32(t: torch.Tensor, name: str) -> torch.Tensor:
 
 
 def plan_dims(batch: int, s_q: int, num_q_rows: int, h_kv: int, topk: int = 0,
-              num_workers: int = 0):
+              num_workers: int = 0, fp8: bool = False):
     W, words, items = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
-    _lib.check(_lib.lib().mla_plan_dims(batch, s_q, num_q_rows, h_kv, topk, num_workers,
-                                        ctypes.byref(W), ctypes.byref(words), ctypes.byref(items)),
-               "mla_plan_dims")
+    fn = "mla_plan_dims_fp8" if fp8 else "mla_plan_dims"
+    _lib.check(getattr(_lib.lib(), fn)(batch, s_q, num_q_rows, h_kv, topk, num_workers,
+                                       ctypes.byref(W), ctypes.byref(words), ctypes.byref(items)), fn)
     return W.value, words.value, items.value
 
 
@@ -58,25 +58,34 @@ def workspace_bytes(batch, s_q, num_q_rows, h_kv, topk, dv, num_workers) -> int:
 
 
 def get_mla_metadata(cache_seqlens: torch.Tensor, num_q_rows: int, h_kv: int, *, s_q: int = 1,
-                     topk: int | None = None, num_workers: int | None = None, topk2: int = 0):
+                     topk: int | None = None, num_workers: int | None = None, topk2: int = 0,
+                     fp8: bool = False):
     """Split-KV plan: returns ``(tile_scheduler_metadata, num_splits)`` (int32, device).
 
     ``num_q_rows`` is s_q * h_q / h_kv as in the pages' call.  In sparse mode
     (``topk`` given) every query token is an item of ``topk`` keys and ``s_q``
     must be passed; with an auxiliary cache (dual-cache decode) ``topk2`` is
-    the length of its index lists.
+    the length of its index lists.  ``fp8`` plans for the decode over a packed
+    FP8 cache (its row tiling sets the default worker count and the per-run
+    overhead); any plan is valid for either decode.
     """
     _i32(cache_seqlens, "cache_seqlens")
     _need(cache_seqlens.is_cuda, "cache_seqlens must be on the GPU")
     batch = cache_seqlens.numel()
     tk = int(topk or 0)
-    W, words, items = plan_dims(batch, s_q, num_q_rows, h_kv, tk, int(num_workers or 0))
+    _need(not (fp8 and topk2), "the FP8 decode has no auxiliary cache (topk2)")
+    W, words, items = plan_dims(batch, s_q, num_q_rows, h_kv, tk, int(num_workers or 0), fp8=fp8)
     dev = cache_seqlens.device
     plan = torch.empty(words, dtype=torch.int32, device=dev)
     num_splits = torch.empty(items + 1, dtype=torch.int32, device=dev)
-    _lib.check(_lib.lib().mla_get_metadata(_ptr(cache_seqlens), batch, s_q, num_q_rows, h_kv, tk,
-                                           int(topk2), W, _ptr(plan), _ptr(num_splits), _stream(dev)),
-               "mla_get_metadata")
+    if fp8:
+        _lib.check(_lib.lib().mla_get_metadata_fp8(_ptr(cache_seqlens), batch, s_q, num_q_rows, h_kv, tk,
+                                                   W, _ptr(plan), _ptr(num_splits), _stream(dev)),
+                   "mla_get_metadata_fp8")
+    else:
+        _lib.check(_lib.lib().mla_get_metadata(_ptr(cache_seqlens), batch, s_q, num_q_rows, h_kv, tk,
+                                               int(topk2), W, _ptr(plan), _ptr(num_splits), _stream(dev)),
+                   "mla_get_metadata")
     return plan, num_splits
 
 

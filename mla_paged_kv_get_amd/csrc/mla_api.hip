@@ -115,12 +115,20 @@ const char* mla_status_string(int status) {
   }
 }
 
-int mla_plan_dims(int batch, int s_q, int num_q_rows, int h_kv, int topk, int num_workers_request,
-                  int* out_num_workers, int* out_plan_words, int* out_num_items) {
+}  // extern "C"
+
+namespace {
+
+// The plan's sizes and the plan for decodes of one cache format (kv_format 0:
+// bf16 rows; 1: packed FP8 rows): the format picks the decode variant, whose
+// row tiles set the default worker count and whose overhead is the plan's.
+int plan_dims_for(int batch, int s_q, int num_q_rows, int h_kv, int topk, int kv_format,
+                  int num_workers_request, int* out_num_workers, int* out_plan_words,
+                  int* out_num_items) {
   if (!out_num_workers || !out_plan_words || !out_num_items) return MLA_ERR_INVALID_ARGUMENT;
   if (num_workers_request < 0) return MLA_ERR_INVALID_ARGUMENT;
   Shape s;
-  int st = shape_of(batch, s_q, num_q_rows, h_kv, topk, &s);
+  int st = shape_of(batch, s_q, num_q_rows, h_kv, topk, &s, kv_format);
   if (st != MLA_OK) return st;
   if (num_workers_request > (1 << 20)) return MLA_ERR_INVALID_ARGUMENT;
   int W = 0;
@@ -134,23 +142,15 @@ int mla_plan_dims(int batch, int s_q, int num_q_rows, int h_kv, int topk, int nu
   return MLA_OK;
 }
 
-int mla_plan_num_workers(int plan_words, int batch, int s_q, int num_q_rows, int h_kv, int topk) {
-  Shape s;
-  if (shape_of(batch, s_q, num_q_rows, h_kv, topk, &s) != MLA_OK) return -1;
-  const int64_t rows_words = (int64_t)plan_words - plan_counters(s);
-  if (rows_words < 2 * kPlanWords || rows_words % kPlanWords) return -1;
-  return (int)(rows_words / kPlanWords - 1);
-}
-
-int mla_get_metadata(const int32_t* cache_seqlens, int batch, int s_q, int num_q_rows, int h_kv,
-                     int topk, int topk2, int num_workers, int32_t* plan, int32_t* num_splits,
-                     void* stream) {
+int get_metadata_for(const int32_t* cache_seqlens, int batch, int s_q, int num_q_rows, int h_kv,
+                     int topk, int topk2, int kv_format, int num_workers, int32_t* plan,
+                     int32_t* num_splits, void* stream) {
   if (!plan || !num_splits) return MLA_ERR_INVALID_ARGUMENT;
   if (topk <= 0 && !cache_seqlens && batch > 0) return MLA_ERR_INVALID_ARGUMENT;
   if (num_workers < 1 || num_workers > (1 << 20)) return MLA_ERR_INVALID_ARGUMENT;
   if (topk2 < 0 || (topk2 > 0 && topk <= 0)) return MLA_ERR_INVALID_ARGUMENT;
   Shape s;
-  const int st = shape_of(batch, s_q, num_q_rows, h_kv, topk, &s);
+  const int st = shape_of(batch, s_q, num_q_rows, h_kv, topk, &s, kv_format);
   if (st != MLA_OK) return st;
   if (s.items > mla::plan_max_items()) return MLA_ERR_UNSUPPORTED;
   if (num_workers > mla::plan_large_max_workers(s.items)) return MLA_ERR_UNSUPPORTED;
@@ -167,6 +167,43 @@ int mla_get_metadata(const int32_t* cache_seqlens, int batch, int s_q, int num_q
                                    plan + (int64_t)kPlanWords * (num_workers + 1),
                                    (int)plan_counters(s), reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_plan_dims(int batch, int s_q, int num_q_rows, int h_kv, int topk, int num_workers_request,
+                  int* out_num_workers, int* out_plan_words, int* out_num_items) {
+  return plan_dims_for(batch, s_q, num_q_rows, h_kv, topk, 0, num_workers_request, out_num_workers,
+                       out_plan_words, out_num_items);
+}
+
+int mla_plan_dims_fp8(int batch, int s_q, int num_q_rows, int h_kv, int topk, int num_workers_request,
+                      int* out_num_workers, int* out_plan_words, int* out_num_items) {
+  return plan_dims_for(batch, s_q, num_q_rows, h_kv, topk, 1, num_workers_request, out_num_workers,
+                       out_plan_words, out_num_items);
+}
+
+int mla_plan_num_workers(int plan_words, int batch, int s_q, int num_q_rows, int h_kv, int topk) {
+  Shape s;
+  if (shape_of(batch, s_q, num_q_rows, h_kv, topk, &s) != MLA_OK) return -1;
+  const int64_t rows_words = (int64_t)plan_words - plan_counters(s);
+  if (rows_words < 2 * kPlanWords || rows_words % kPlanWords) return -1;
+  return (int)(rows_words / kPlanWords - 1);
+}
+
+int mla_get_metadata(const int32_t* cache_seqlens, int batch, int s_q, int num_q_rows, int h_kv,
+                     int topk, int topk2, int num_workers, int32_t* plan, int32_t* num_splits,
+                     void* stream) {
+  return get_metadata_for(cache_seqlens, batch, s_q, num_q_rows, h_kv, topk, topk2, 0, num_workers,
+                          plan, num_splits, stream);
+}
+
+int mla_get_metadata_fp8(const int32_t* cache_seqlens, int batch, int s_q, int num_q_rows, int h_kv,
+                         int topk, int num_workers, int32_t* plan, int32_t* num_splits, void* stream) {
+  return get_metadata_for(cache_seqlens, batch, s_q, num_q_rows, h_kv, topk, 0, 1, num_workers, plan,
+                          num_splits, stream);
 }
 
 size_t mla_workspace_bytes(int batch, int s_q, int num_q_rows, int h_kv, int topk, int dv,

@@ -48,7 +48,7 @@ def run_gpu(d: Dev, num_workers=None, plan=None, softmax_scale=None):
         h_kv = w.kv.shape[2]
         topk2 = w.aux[3].shape[2] if d.aux is not None else 0
         plan = m.get_mla_metadata(d.sl, w.s_q * w.h_q // h_kv, h_kv, s_q=w.s_q, topk=w.topk,
-                                  num_workers=num_workers, topk2=topk2)
+                                  num_workers=num_workers, topk2=topk2, fp8=w.kv.dtype == np.uint8)
     o, lse = m.mla_decode_with_kvcache(d.q, d.kv, d.bt, d.sl, 512, plan[0], plan[1], causal=w.causal,
                                        softmax_scale=softmax_scale, indices=d.idx, aux=d.aux)
     torch.cuda.synchronize()

@@ -63,6 +63,24 @@ def test_plan_dims():
     assert _dims(4, 1, 16, 1, 0, -3)[0] == _lib.MLA_ERR_INVALID_ARGUMENT
 
 
+def test_plan_dims_fp8_and_metadata_fp8_checks():
+    # the FP8 plan has the same words (the arrival counters cover the finest
+    # row tiling of either format) and rejects the same arguments
+    l = _lib.lib()
+    for args in [(64, 1, 16, 1, 0, 256), (16, 8, 8 * 128, 1, 2048, 128), (32, 2, 256, 1, 0, 64)]:
+        W, w, it = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+        st = l.mla_plan_dims_fp8(*args, ctypes.byref(W), ctypes.byref(w), ctypes.byref(it))
+        assert (st, W.value, w.value, it.value) == _dims(*args)
+    W, w, it = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    assert l.mla_plan_dims_fp8(4, 3, 16, 1, 64, 8, ctypes.byref(W), ctypes.byref(w),
+                               ctypes.byref(it)) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert l.mla_get_metadata_fp8(DUMMY, 4, 1, 16, 1, 0, 8, None, DUMMY, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert l.mla_get_metadata_fp8(DUMMY, 4, 1, 16, 1, 0, 0, DUMMY, DUMMY, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert l.mla_get_metadata_fp8(None, 4, 1, 16, 1, 0, 8, DUMMY, DUMMY, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert l.mla_get_metadata_fp8(DUMMY, (1 << 20) + 1, 1, 16, 1, 0, 8, DUMMY, DUMMY,
+                                  None) == _lib.MLA_ERR_UNSUPPORTED
+
+
 def test_workspace_bytes():
     l = _lib.lib()
     # (items + W) partial slots of rows x (512 bf16 outputs + one fp32 LSE)

@@ -107,3 +107,28 @@ def test_fp8_many_short_items(topk):
     for W in (1, 2, 37):
         o, lse, _ = run_gpu(Dev(w), num_workers=W)
         compare(w, o, lse, label=f"fp8 many items topk={topk} W={W}")
+
+
+def test_fp8_plan_bit_exact_and_bf16_plan_also_valid():
+    # the FP8 plan: the oracle's schedule with the 64-row variant's overhead (4)
+    # and, by default, one workgroup per CU for both row tiles of every worker;
+    # the FP8 decode of the full sparse top-k workload on it, and on the bf16
+    # call's plan (any plan is valid for either decode), against the oracle
+    import mla_paged_kv_get_amd as m
+    w = wl.sparse_topk_fp8()
+    d = Dev(w)
+    rows = w.s_q * w.h_q
+    plan8, ns8 = m.get_mla_metadata(d.sl, rows, 1, s_q=w.s_q, topk=w.topk, fp8=True)
+    plan16, _ = m.get_mla_metadata(d.sl, rows, 1, s_q=w.s_q, topk=w.topk)
+    torch.cuda.synchronize()
+    p = plan8.cpu().numpy()
+    W8, W16 = int(p[0]), int(plan16[0].item())
+    assert int(p[1]) == 4 and W8 * 2 == W16                 # 64-row tiles: two per worker
+    ref_p, ref_ns = orc.plan([64 * (-(-w.topk // 64))] * (w.B * w.s_q), W8, 4)
+    assert (p[:ref_p.size] == ref_p).all()
+    assert (ns8.cpu().numpy() == ref_ns).all()
+    o8, lse8, _ = run_gpu(d, plan=(plan8, ns8))
+    compare(w, o8, lse8, label="fp8 sparse top-k, FP8 plan")
+    plan16, ns16 = m.get_mla_metadata(d.sl, rows, 1, s_q=w.s_q, topk=w.topk)
+    o16, lse16, _ = run_gpu(d, plan=(plan16, ns16))
+    compare(w, o16, lse16, label="fp8 sparse top-k, bf16 plan")
