@@ -136,8 +136,8 @@ int mla_plan_num_workers(int plan_words, int batch, int s_q, int num_q_rows, int
  * sparse: ceil(topk / 64) + ceil(topk2 / 64), topk2 being the length of the
  * auxiliary index lists of the dual-cache decode, 0 otherwise) and costs
  * overhead + n_i units (overhead = 1 block for items of at most 16 query
- * rows, 4 for 17 to 64 rows, 3 for more; the call does not know the cache
- * format, so an FP8 decode runs the same plan), the overhead split
+ * rows, 4 for 17 to 64 rows, 3 for more: the bf16 decode's row tiling;
+ * mla_get_metadata_fp8 plans for the FP8 decode's), the overhead split
  * into a lead of ceil(overhead / 2) units before the item's blocks and a tail
  * of floor(overhead / 2) units after them; items are laid end to end on a cost
  * axis (total T); the first W' = min(W, T) workers share it evenly, worker w

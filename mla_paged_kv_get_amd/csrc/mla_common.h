@@ -143,9 +143,9 @@ constexpr int variant_rows(int v) { return v == kVariantRows16 ? 16 : v == kVari
 // Plan cost of a run of an item, in blocks, laid out half before and half
 // after its blocks (measured: an item boundary costs about 1.6 tiles of a
 // 16-row worker, where 1 unit ahead of the blocks balanced best; items over
-// 64 rows balanced best at 3, split 2 + 1, among 2 to 6).  The metadata call
-// knows the row count but not the cache format: the variant here is the bf16
-// one, and an FP8 decode of the same rows runs the same plan.
+// 64 rows balanced best at 3, split 2 + 1, among 2 to 6).  The variant is
+// the one the decode of the plan's cache format runs (the metadata calls for
+// bf16 and for packed FP8 caches).
 constexpr int variant_overhead(int v) { return v == kVariantRows16 ? 1 : v == kVariantRows128 ? 3 : 4; }
 // kv_format 0: bf16 rows; 1: packed FP8 rows (no 128-row variant).
 inline int pick_variant(int rows_per_item, int kv_format) {
